@@ -1,0 +1,389 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself -- literal hand-built blocks, a bit-level field reader, exact rational
+arithmetic, library routines, brute-force loops, closed-form probes and exact
+invariants.  CPU only."""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle as O
+import q4k_synth as S
+from tests import q4k_blocks as B
+
+
+
+def _w(blk):
+    """Decoded float64 weights of one block."""
+    return O.q4k_dequant(blk.reshape(1, 1, 144), 1, 256)[0]
+
+
+def _per_subblock(values):
+    """256 weights from 8 per-sub-block constants."""
+    return np.repeat(np.asarray(values, dtype=np.float64), 32)
+
+
+# ---------------------------------------------------------------------------
+# Q4_K decode: literal hand-built blocks
+# ---------------------------------------------------------------------------
+def test_zero_block_is_all_positive_zero():
+    w = _w(B.block())
+    assert np.all(w == 0.0)
+    assert not np.any(np.signbit(w.astype(np.float32)))
+
+
+def test_unit_scales_with_quants_i_mod_16():
+    # Q[32c + l] carries l % 16 in both nibbles, so weight i holds i % 16.
+    Q = [(l % 16) | ((l % 16) << 4) for c in range(4) for l in range(32)]
+    w = _w(B.block(B.F16_ONE, 0, B.S_UNIT_SCALES, Q))
+    assert np.array_equal(w, np.arange(256) % 16)
+
+
+# With d = 1, dmin = 0 and every quant 1, setting scale byte S[k] = 0xFF alone
+# gives these per-sub-block weights (worked out by hand from the field table:
+# S[0..3] carry sc_0..3 in bits 0-5 and the top two bits of sc_4..7 in bits 6-7;
+# S[4..7] carry only mins; S[8..11] carry the low nibble of sc_4..7).
+SCALE_WALK = {
+    0: [63, 0, 0, 0, 48, 0, 0, 0],
+    1: [0, 63, 0, 0, 0, 48, 0, 0],
+    2: [0, 0, 63, 0, 0, 0, 48, 0],
+    3: [0, 0, 0, 63, 0, 0, 0, 48],
+    4: [0] * 8, 5: [0] * 8, 6: [0] * 8, 7: [0] * 8,
+    8: [0, 0, 0, 0, 15, 0, 0, 0],
+    9: [0, 0, 0, 0, 0, 15, 0, 0],
+    10: [0, 0, 0, 0, 0, 0, 15, 0],
+    11: [0, 0, 0, 0, 0, 0, 0, 15],
+}
+
+# With d = 0, dmin = 1: S[4..7] carry m_0..3 in bits 0-5 and the top two bits
+# of m_4..7 in bits 6-7; S[8..11] carry the low nibble of m_4..7 in bits 4-7.
+MIN_WALK = {
+    0: [0] * 8, 1: [0] * 8, 2: [0] * 8, 3: [0] * 8,
+    4: [-63, 0, 0, 0, -48, 0, 0, 0],
+    5: [0, -63, 0, 0, 0, -48, 0, 0],
+    6: [0, 0, -63, 0, 0, 0, -48, 0],
+    7: [0, 0, 0, -63, 0, 0, 0, -48],
+    8: [0, 0, 0, 0, -15, 0, 0, 0],
+    9: [0, 0, 0, 0, 0, -15, 0, 0],
+    10: [0, 0, 0, 0, 0, 0, -15, 0],
+    11: [0, 0, 0, 0, 0, 0, 0, -15],
+}
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_scale_byte_walk(k):
+    Sb = [0] * 12
+    Sb[k] = 0xFF
+    w = _w(B.block(B.F16_ONE, 0, Sb, [0x11] * 128))
+    assert np.array_equal(w, _per_subblock(SCALE_WALK[k]))
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_min_byte_walk(k):
+    Sb = [0] * 12
+    Sb[k] = 0xFF
+    w = _w(B.block(0, B.F16_ONE, Sb, [0x11] * 128))
+    assert np.array_equal(w, _per_subblock(MIN_WALK[k]))
+
+
+def test_min_j_gives_minus_j():
+    # m_j = j: S[4..7] = 0,1,2,3 and the high nibbles of S[8..11] = 4..7.
+    Sb = [0, 0, 0, 0, 0, 1, 2, 3, 0x40, 0x50, 0x60, 0x70]
+    w = _w(B.block(0, B.F16_ONE, Sb, [0x55] * 128))
+    assert np.array_equal(w, _per_subblock([0, -1, -2, -3, -4, -5, -6, -7]))
+
+
+# Positions of the low and high nibbles of the 128 quant bytes, in byte order:
+# bytes 0-31 -> weights 0-31 (low) and 32-63 (high); bytes 32-63 -> 64-95 and
+# 96-127; bytes 64-95 -> 128-159 and 160-191; bytes 96-127 -> 192-223, 224-255.
+LOW_POS = list(range(0, 32)) + list(range(64, 96)) + list(range(128, 160)) + list(range(192, 224))
+HIGH_POS = list(range(32, 64)) + list(range(96, 128)) + list(range(160, 192)) + list(range(224, 256))
+
+
+def test_single_nibble_walk_is_a_permutation():
+    seen = []
+    for byte in range(128):
+        for nib, table in ((0x01, LOW_POS), (0x10, HIGH_POS)):
+            Q = [0] * 128
+            Q[byte] = nib
+            w = _w(B.block(B.F16_ONE, 0, B.S_UNIT_SCALES, Q))
+            nz = np.flatnonzero(w)
+            assert nz.tolist() == [table[byte]] and w[nz[0]] == 1.0
+            seen.append(int(nz[0]))
+    assert sorted(seen) == list(range(256))
+
+
+def test_fp16_header_fields_literal():
+    # d = 0.5, dmin = 2: w = 0.5*1*q - 2*0 on unit scales
+    w = _w(B.block(B.F16_HALF, B.F16_TWO, B.S_UNIT_SCALES, [0x33] * 128))
+    assert np.all(w == 1.5)
+    # negative d is decoded literally
+    w = _w(B.block(B.F16_NEG_ONE, 0, B.S_UNIT_SCALES, [0x22] * 128))
+    assert np.all(w == -2.0)
+    # d and dmin are not swapped: d = 2, dmin = 0.5 with unit mins (m_j = 1)
+    Sb = [1, 1, 1, 1, 1, 1, 1, 1, 0x11, 0x11, 0x11, 0x11]
+    w = _w(B.block(B.F16_TWO, B.F16_HALF, Sb, [0x44] * 128))
+    assert np.all(w == 2.0 * 4 - 0.5)
+
+
+# ---------------------------------------------------------------------------
+# Q4_K decode: brute-force bit reader and exact arithmetic on random blocks
+# ---------------------------------------------------------------------------
+def _bit(blk, pos):
+    return (int(blk[pos // 8]) >> (pos % 8)) & 1
+
+
+def _field(blk, positions):
+    return sum(_bit(blk, p) << t for t, p in enumerate(positions))
+
+
+def _field_positions():
+    """Absolute LSB-first bit positions of every field inside a block."""
+    pos = {}
+    for j in range(4):
+        pos[("sc", j)] = [8 * (4 + j) + t for t in range(6)]
+        pos[("m", j)] = [8 * (8 + j) + t for t in range(6)]
+    for j in range(4, 8):
+        pos[("sc", j)] = [8 * (4 + j + 4) + t for t in range(4)] + [8 * (4 + j - 4) + 6, 8 * (4 + j - 4) + 7]
+        pos[("m", j)] = [8 * (4 + j + 4) + 4 + t for t in range(4)] + [8 * (4 + j) + 6, 8 * (4 + j) + 7]
+    for c in range(4):
+        for l in range(32):
+            byte = 16 + 32 * c + l
+            pos[("q", 64 * c + l)] = [8 * byte + t for t in range(4)]
+            pos[("q", 64 * c + 32 + l)] = [8 * byte + 4 + t for t in range(4)]
+    return pos
+
+
+def test_bit_reader_partitions_the_block():
+    # sixteen 6-bit fields + 256 nibbles cover bits 32..1151 exactly once
+    all_bits = [p for v in _field_positions().values() for p in v]
+    assert sorted(all_bits) == list(range(32, 144 * 8))
+
+
+def test_fields_match_bit_level_reader():
+    rng = np.random.default_rng(12345)
+    blob = S.gen_q4k_blob(rng, 40, 256 * 5)
+    d, dmin, sc, m, q = O.q4k_fields(blob)
+    pos = _field_positions()
+    for r in range(40):
+        for b in range(5):
+            blk = blob[r, b]
+            for j in range(8):
+                assert sc[r, b, j] == _field(blk, pos[("sc", j)])
+                assert m[r, b, j] == _field(blk, pos[("m", j)])
+            for i in range(256):
+                assert q[r, b, i] == _field(blk, pos[("q", i)])
+            assert d[r, b] == float(np.frombuffer(bytes(blk[0:2]), dtype="<f2")[0])
+            assert dmin[r, b] == float(np.frombuffer(bytes(blk[2:4]), dtype="<f2")[0])
+
+
+def test_dequant_is_exact_rational_value():
+    rng = np.random.default_rng(7)
+    blob = S.gen_q4k_blob(rng, 3, 512)
+    W = O.q4k_dequant(blob, 3, 512)
+    pos = _field_positions()
+    for r in range(3):
+        for b in range(2):
+            blk = blob[r, b]
+            dF = Fraction(float(np.frombuffer(bytes(blk[0:2]), dtype="<f2")[0]))
+            mF = Fraction(float(np.frombuffer(bytes(blk[2:4]), dtype="<f2")[0]))
+            for i in range(256):
+                j = i // 32
+                exact = dF * _field(blk, pos[("sc", j)]) * _field(blk, pos[("q", i)]) \
+                    - mF * _field(blk, pos[("m", j)])
+                assert Fraction(W[r, 256 * b + i]) == exact
+
+
+def test_fp32_dequant_is_round_to_nearest_even_of_exact():
+    rng = np.random.default_rng(8)
+    blob = S.gen_q4k_blob(rng, 16, 512)
+    W64 = O.q4k_dequant(blob, 16, 512)
+    W32 = O.q4k_dequant_f32(blob, 16, 512)
+    # RNE: |w32 - w| <= half an ulp of w32, and ties go to the even mantissa
+    ulp = np.spacing(np.abs(W32).astype(np.float32)).astype(np.float64)
+    diff = np.abs(W32.astype(np.float64) - W64)
+    assert np.all(diff <= ulp / 2)
+
+
+# ---------------------------------------------------------------------------
+# silu
+# ---------------------------------------------------------------------------
+def test_silu_identities_and_library():
+    z = np.linspace(-30, 30, 6001)
+    s = O.silu(z)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert np.allclose(s - O.silu(-z), z, rtol=0, atol=1e-12)       # silu(z) - silu(-z) = z
+    assert np.allclose(s, z * expit(z), rtol=1e-14, atol=1e-300)
+    assert O.silu(np.array([60.0]))[0] == pytest.approx(60.0, rel=1e-20)
+    big_neg = O.silu(np.array([-800.0]))[0]
+    assert big_neg == 0.0 and not math.isnan(big_neg)
+
+
+# ---------------------------------------------------------------------------
+# MLP
+# ---------------------------------------------------------------------------
+def _tiny_mlp_inputs(seed=3, H=256, I=256, M=2):
+    rng = np.random.default_rng(seed)
+    wg = S.gen_q4k_blob(rng, I, H)
+    wu = S.gen_q4k_blob(rng, I, H)
+    wd = S.gen_q4k_blob(rng, H, I)
+    x = S.gen_x(rng, M, H)
+    return x, wg, wu, wd
+
+
+def test_mlp_matches_brute_force_loops():
+    H, I, M = 256, 256, 2
+    x, wg, wu, wd = _tiny_mlp_inputs(H=H, I=I, M=M)
+    Wg, Wu, Wd = (O.q4k_dequant(wg, I, H), O.q4k_dequant(wu, I, H), O.q4k_dequant(wd, H, I))
+    y, h = O.mlp(x, wg, wu, wd, H, I)
+    xs = x.astype(np.float64).tolist()
+    for t in range(M):
+        hh = []
+        for j in range(I):
+            g = sum(Wg[j][k] * xs[t][k] for k in range(H))
+            u = sum(Wu[j][k] * xs[t][k] for k in range(H))
+            hh.append(g / (1.0 + math.exp(-g)) * u if g > -700 else -0.0)
+        for n in range(H):
+            yy = sum(Wd[n][j] * hh[j] for j in range(I))
+            assert y[t, n] == pytest.approx(yy, rel=1e-11, abs=1e-9 * abs(yy) + 1e-300)
+        assert np.allclose(h[t], hh, rtol=1e-11)
+
+
+def test_one_hot_x_selects_weight_columns():
+    H, I = 512, 256
+    x, wg, wu, wd = _tiny_mlp_inputs(H=H, I=I, M=1)
+    k = 300
+    x = np.zeros((1, H), dtype=np.float16)
+    x[0, k] = 1.0
+    _, h = O.mlp(x, wg, wu, wd, H, I)
+    g_col = O.q4k_dequant(wg, I, H)[:, k]         # column k of W_gate (not row k)
+    u_col = O.q4k_dequant(wu, I, H)[:, k]
+    assert np.array_equal(h[0], g_col / (1.0 + np.exp(-g_col)) * u_col)
+
+
+def test_gate_branch_is_the_one_through_silu():
+    H, I = 256, 256
+    x, wg, wu, wd = _tiny_mlp_inputs(H=H, I=I, M=1)
+    x = np.zeros((1, H), dtype=np.float16)
+    x[0, 17] = 1.0
+    ones = B.unit_matrix(I, H)
+    # W_up = 1 everywhere: u = 1, so h = silu(g) with g = column 17 of W_gate
+    _, h = O.mlp(x, wg, ones, wd, H, I)
+    g = O.q4k_dequant(wg, I, H)[:, 17]
+    assert np.allclose(h[0], g * expit(g), rtol=1e-14)
+    # W_gate = 1 everywhere: g = 1, so h = silu(1) * u
+    _, h = O.mlp(x, ones, wu, wd, H, I)
+    u = O.q4k_dequant(wu, I, H)[:, 17]
+    assert np.allclose(h[0], expit(1.0) * u, rtol=1e-14)
+
+
+def test_zero_input_gives_exact_zero():
+    x, wg, wu, wd = _tiny_mlp_inputs()
+    y, h = O.mlp(np.zeros_like(x), wg, wu, wd, 256, 256)
+    assert np.all(y == 0.0) and np.all(h == 0.0)
+
+
+def test_doubling_down_scales_doubles_output_exactly():
+    x, wg, wu, wd = _tiny_mlp_inputs()
+    y1, _ = O.mlp(x, wg, wu, wd, 256, 256)
+    wd2 = B.scaled_blob(wd, B.double_fp16_bits)
+    y2, _ = O.mlp(x, wg, wu, wd2, 256, 256)
+    assert np.array_equal(y2, 2.0 * y1)
+
+
+def test_hidden_block_permutation_invariance():
+    H, I = 1024, 256
+    x, wg, wu, wd = _tiny_mlp_inputs(H=H, I=I, M=3)
+    y1, _ = O.mlp(x, wg, wu, wd, H, I)
+    perm = np.array([2, 0, 3, 1])          # permute the four 256-column blocks of the hidden axis
+    xp = x.reshape(3, 4, 256)[:, perm].reshape(3, H)
+    y2, _ = O.mlp(xp, wg[:, perm], wu[:, perm], wd, H, I)
+    # the down projection's outputs are hidden columns too; they are not permuted
+    assert np.allclose(y1, y2, rtol=1e-11, atol=1e-9 * np.abs(y1).max())
+
+
+# ---------------------------------------------------------------------------
+# MoE
+# ---------------------------------------------------------------------------
+def _tiny_moe(E=4, H=256, I=256, M=5, k=2, seed=11):
+    rng = np.random.default_rng(seed)
+    wg = np.stack([S.gen_q4k_blob(rng, I, H) for _ in range(E)])
+    wu = np.stack([S.gen_q4k_blob(rng, I, H) for _ in range(E)])
+    wd = np.stack([S.gen_q4k_blob(rng, H, I) for _ in range(E)])
+    x = S.gen_x(rng, M, H)
+    ids, p = S.gen_routing(rng, M, E, k)
+    return x, wg, wu, wd, ids, p
+
+
+def test_moe_top1_weight1_is_dense():
+    x, wg, wu, wd, ids, p = _tiny_moe()
+    ids1 = np.full((x.shape[0], 1), 2, dtype=np.int32)
+    y, bad = O.moe(x, wg, wu, wd, ids1, np.ones((x.shape[0], 1), np.float32), 256, 256)
+    yd, _ = O.mlp(x, wg[2], wu[2], wd[2], 256, 256)
+    assert bad == 0 and np.array_equal(y, yd)
+
+
+def test_moe_slot_permutation_invariance():
+    x, wg, wu, wd, ids, p = _tiny_moe()
+    y1, _ = O.moe(x, wg, wu, wd, ids, p, 256, 256)
+    y2, _ = O.moe(x, wg, wu, wd, ids[:, ::-1].copy(), p[:, ::-1].copy(), 256, 256)
+    assert np.allclose(y1, y2, rtol=1e-13, atol=1e-12 * np.abs(y1).max())
+
+
+def test_moe_identical_experts_reduce_to_dense():
+    x, wg, wu, wd, ids, p = _tiny_moe()
+    E = wg.shape[0]
+    same = lambda a: np.stack([a[0]] * E)
+    y, _ = O.moe(x, same(wg), same(wu), same(wd), ids, p, 256, 256)
+    yd, _ = O.mlp(x, wg[0], wu[0], wd[0], 256, 256)
+    scale = p.astype(np.float64).sum(axis=1, keepdims=True)     # = 1 up to fp32 rounding
+    assert np.allclose(y, scale * yd, rtol=1e-12, atol=1e-12 * np.abs(yd).max())
+
+
+def test_moe_out_of_range_ids_contribute_nothing():
+    x, wg, wu, wd, ids, p = _tiny_moe()
+    bad_ids = ids.copy()
+    bad_ids[1, 0] = -1
+    bad_ids[3, 1] = 99
+    y, bad = O.moe(x, wg, wu, wd, bad_ids, p, 256, 256)
+    keep = p.copy()
+    keep[1, 0] = 0
+    keep[3, 1] = 0
+    y2, _ = O.moe(x, wg, wu, wd, np.where(bad_ids < 0, 0, np.where(bad_ids > 3, 0, bad_ids)), keep, 256, 256)
+    assert bad == 2 and np.allclose(y, y2, rtol=1e-13, atol=1e-12 * np.abs(y).max())
+
+
+# ---------------------------------------------------------------------------
+# Workload shift exponents keep the fp16 intermediate and output in range
+# ---------------------------------------------------------------------------
+def test_tiny_workload_shifts_have_headroom():
+    w = S.WORKLOADS["tiny"]
+    wg, wu, wd = S.layer_weights(w.seed, 0, w.hidden, w.inter)
+    y, h = O.mlp(S.workload_x(w), wg, wu, wd, w.hidden, w.inter)
+    assert np.abs(h).max() * 2.0 ** -w.inter_shift <= 2 ** 13
+    assert np.abs(y).max() * 2.0 ** -w.out_shift <= 2 ** 13
+
+
+def test_oracle_matches_committed_regression_fixture(root_dir):
+    import os
+    path = os.path.join(root_dir, "tests", "golden", "tiny_oracle.txt")
+    sections, cur = {}, None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("["):
+            cur = line[1:-1]
+            sections[cur] = []
+        else:
+            sections[cur].append(float.fromhex(line))
+    w = S.WORKLOADS["tiny"]
+    wg, wu, wd = S.layer_weights(w.seed, 0, w.hidden, w.inter)
+    y, _ = O.mlp(S.workload_x(w), wg, wu, wd, w.hidden, w.inter)
+    assert np.array_equal(O.q4k_dequant_f32(wg[0:1, 0:1], 1, 256)[0], np.array(sections["w32"], np.float32))
+    assert np.allclose(y[0], sections["y0"], rtol=1e-12, atol=0)
+    assert np.allclose(y[7], sections["y7"], rtol=1e-12, atol=0)
