@@ -1,0 +1,147 @@
+/*
+ * zinc_mlp.h -- C ABI of the MI355X (gfx950) Q4_K SwiGLU MLP library.
+ *
+ * The operation is the SwiGLU feed-forward block described on the page
+ * "Fused SwiGLU MLP: ZINC RDNA4 Down-Projection Bandwidth" (section "The MLP is
+ * two trips up to a wider width"): the hidden state is projected up twice, by
+ * a gate weight and an up weight, combined by SwiGLU, and projected back down:
+ *
+ *     y = W_down . ( silu(W_gate . x)  (*)  (W_up . x) ),   silu(z) = z / (1 + e^-z)
+ *
+ * with every weight matrix stored as Q4_K super-blocks and unpacked in
+ * registers on the way into the multiply (same page, opening Q&A; "VGPR
+ * pressure caps the fused RDNA4 prefill GEMM at nine waves", section "What the
+ * fused GEMM actually spends registers on").
+ *
+ * Q4_K (the GGUF block; the pages name it but print no layout): 144 bytes hold
+ * 256 consecutive weights of one row along the contraction dimension --
+ * bytes 0-1 fp16 d, bytes 2-3 fp16 dmin, bytes 4-15 eight 6-bit scales sc_j
+ * and eight 6-bit mins m_j packed as
+ *     j < 4 : sc_j = S[j] & 63,  m_j = S[j+4] & 63
+ *     j >= 4: sc_j = (S[j+4] & 15) | (S[j-4] >> 6) << 4,  m_j = (S[j+4] >> 4) | (S[j] >> 6) << 4
+ * and bytes 16-143 the 4-bit quants: weight i sits in byte 16 + 32*(i/64) + i%32,
+ * low nibble if i%64 < 32, else high nibble.  Weight i = d*sc_{i/32}*q_i - dmin*m_{i/32}.
+ * A matrix [rows x cols] (cols % 256 == 0) is rows x (cols/256) blocks, row-major,
+ * blocks running along cols.  W_gate and W_up are [inter x hidden]; W_down is
+ * [hidden x inter].
+ *
+ * Activations: x and y are fp16, row-major [M x hidden].  Accumulation is fp32.
+ *
+ * fp16 range: the intermediate is stored in fp16 on chip and y in fp16 in
+ * memory.  Both are divided by an exact power of two first:
+ *     intermediate held as fp16(h * 2^-inter_shift),  y written as fp16(y * 2^-out_shift).
+ * With real-model weights both shifts are 0; synthetic weights with a large
+ * non-zero mean need positive shifts to stay below 65504.  Shifts are in [0, 30].
+ *
+ * Conventions for every entry point:
+ *   - All pointers are device pointers owned by the caller, 16-byte aligned.
+ *     Nothing is allocated or freed inside; the workspace is caller-provided.
+ *   - Every argument check runs on the host before any HIP call; a failed check
+ *     returns a negative zinc_status and enqueues nothing.
+ *   - On success the call only enqueues work on `stream` (a hipStream_t; NULL
+ *     means the null stream) and returns ZINC_OK without synchronising the
+ *     host.  Buffers must stay valid until the stream has passed the call.
+ *   - A failed kernel launch returns ZINC_ERR_HIP.
+ *   - M == 0 is a no-op returning ZINC_OK.
+ *   - Calls are stateless; concurrent calls need distinct workspaces and outputs.
+ *   - y must not alias x, the weights or the workspace.
+ */
+#ifndef ZINC_MLP_H
+#define ZINC_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZINC_OK = 0,
+  ZINC_ERR_NULL = -1,        /* a required pointer is NULL */
+  ZINC_ERR_SHAPE = -2,       /* hidden or inter not a positive multiple of 256, or too large */
+  ZINC_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+  ZINC_ERR_WORKSPACE = -4,   /* workspace smaller than the matching *_workspace_size() */
+  ZINC_ERR_ARG = -5,         /* M < 0, M above the entry point's limit, shift or top_k out of range */
+  ZINC_ERR_HIP = -6,         /* a HIP launch or runtime call failed */
+  ZINC_ERR_UNSUPPORTED = -7  /* a size this build does not handle */
+} zinc_status;
+
+/* Text of a status code (static storage; never NULL). */
+const char* zinc_strerror(int status);
+
+/*
+ * Q4_K block decoder: out[r*cols + c] = the fp32 weight (row r, column c) of the
+ * Q4_K matrix `blocks` [rows x cols], cols % 256 == 0.  Every weight is the exact
+ * value d*sc*q - dmin*m rounded once to nearest-even fp32 (all the products are
+ * exact in fp32), so the result is bit-for-bit unique.
+ * Definition: the Q4_K block named on "Fused SwiGLU MLP: ZINC RDNA4 Down-Projection
+ * Bandwidth" (opening Q&A), layout above.
+ * rows >= 0; rows * cols must fit in int32.
+ */
+int zinc_q4k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* out, void* stream);
+
+/*
+ * Batched prefill: y[M x hidden] = MLP(x[M x hidden]) for any M >= 0.
+ * One fused kernel decodes the gate/up Q4_K blocks in registers into fp16 MFMA
+ * operands (fp32 accumulation), applies SwiGLU in registers, stages the
+ * tokens x intermediate strip in LDS and runs the down projection on it, so
+ * the intermediate never reaches device memory ("Fused SwiGLU MLP: ZINC RDNA4
+ * Down-Projection Bandwidth", sections "Why this fusion is harder than the
+ * last one" and "What it is worth").  Partial down-projection sums of the
+ * intermediate chunks are reduced in fp32 in `workspace`.
+ * Limits: hidden, inter multiples of 256, hidden <= 16384, inter <= 65536.
+ */
+size_t zinc_mlp_q4k_prefill_workspace_size(int32_t M, int32_t hidden, int32_t inter);
+int zinc_mlp_q4k_prefill(const void* w_gate, const void* w_up, const void* w_down,
+                         int32_t hidden, int32_t inter,
+                         const void* x_f16, void* y_f16, int32_t M,
+                         int32_t inter_shift, int32_t out_shift,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode, 1 <= M <= 8 tokens: the same block as a pair of HBM-bound matvecs.
+ * The first streams W_gate and W_up once, computing both projections from one
+ * read of x and applying SwiGLU (the same-input gate/up pair fusion of "Four
+ * bottlenecks, one CUDA backend", "Bottleneck 3"); the second streams W_down.
+ * The per-token intermediate (fp32, M x inter) lives in `workspace` between
+ * the two kernels -- for decode it is small and consumed at once ("Fused SwiGLU
+ * MLP: ZINC RDNA4 Down-Projection Bandwidth", opening Q&A "Does this affect
+ * decode?").  inter_shift has no numerical effect here (the intermediate is
+ * fp32); out_shift applies as above.  M > 8 returns ZINC_ERR_ARG.
+ */
+size_t zinc_mlp_q4k_decode_workspace_size(int32_t M, int32_t hidden, int32_t inter);
+int zinc_mlp_q4k_decode(const void* w_gate, const void* w_up, const void* w_down,
+                        int32_t hidden, int32_t inter,
+                        const void* x_f16, void* y_f16, int32_t M,
+                        int32_t inter_shift, int32_t out_shift,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Batched-expert MoE MLP: y[t] = sum_{s < top_k} p[t,s] * MLP_{ids[t,s]}(x[t]).
+ * Expert ids (int32 [M x top_k]) and mixing weights (fp32 [M x top_k]) are read
+ * on the GPU; the host never reads them back and launches a fixed number of
+ * kernels whatever the routing ("Four bottlenecks, one CUDA backend",
+ * "Bottleneck 2": batched experts whose kernels index the chosen experts'
+ * weights themselves).  w_gate / w_up hold n_experts [inter x hidden] Q4_K
+ * matrices back to back, w_down n_experts [hidden x inter] matrices.
+ * A slot whose id is outside [0, n_experts) contributes nothing; the kernel
+ * then ORs 1 into *dev_error (a device int32, may be NULL) -- the flag is
+ * sticky and the caller clears it.  Duplicate ids within a token each count.
+ * 1 <= top_k <= n_experts <= 1024; M * top_k <= 2^24.
+ */
+size_t zinc_moe_q4k_experts_workspace_size(int32_t M, int32_t top_k, int32_t n_experts,
+                                           int32_t hidden, int32_t inter);
+int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_down,
+                         int32_t n_experts, int32_t hidden, int32_t inter,
+                         const void* x_f16, int32_t M,
+                         const int32_t* expert_ids, const float* expert_weights, int32_t top_k,
+                         void* y_f16, int32_t inter_shift, int32_t out_shift,
+                         void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZINC_MLP_H */

@@ -1,0 +1,185 @@
+"""Python binding of the gfx950 Q4_K SwiGLU MLP library (``include/zinc_mlp.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``_lib/libzinc_mlp.so``.  PyTorch supplies device memory and the
+current HIP stream.  If the library has not been built this module raises on
+import -- there is no CPU fallback.
+
+Functions carry the C entry points' names and take torch tensors:
+
+* ``zinc_q4k_dequant_f32(blocks, rows, cols)`` -> fp32 ``[rows, cols]``
+* ``zinc_mlp_q4k_prefill(w_gate, w_up, w_down, hidden, inter, x, ...)`` -> fp16 y
+* ``zinc_mlp_q4k_decode(...)`` (1 <= M <= 8) -> fp16 y
+* ``zinc_moe_q4k_experts(w_gate, w_up, w_down, n_experts, hidden, inter, x, ids, p, ...)`` -> fp16 y
+
+Q4_K weights are uint8 tensors holding the raw 144-byte blocks ([rows,
+cols/256, 144] or flat); x is fp16 ``[M, hidden]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libzinc_mlp.so")
+
+ZINC_OK = 0
+STATUS_NAMES = {
+    0: "ZINC_OK", -1: "ZINC_ERR_NULL", -2: "ZINC_ERR_SHAPE", -3: "ZINC_ERR_ALIGN",
+    -4: "ZINC_ERR_WORKSPACE", -5: "ZINC_ERR_ARG", -6: "ZINC_ERR_HIP", -7: "ZINC_ERR_UNSUPPORTED",
+}
+
+EXPORTS = (
+    "zinc_strerror",
+    "zinc_q4k_dequant_f32",
+    "zinc_mlp_q4k_prefill_workspace_size",
+    "zinc_mlp_q4k_prefill",
+    "zinc_mlp_q4k_decode_workspace_size",
+    "zinc_mlp_q4k_decode",
+    "zinc_moe_q4k_experts_workspace_size",
+    "zinc_moe_q4k_experts",
+)
+
+
+class ZincError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({strerror(status)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()' or python q4_swiglu_mlp_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.zinc_strerror.restype = ctypes.c_char_p
+    lib.zinc_strerror.argtypes = [ctypes.c_int]
+    lib.zinc_q4k_dequant_f32.restype = ctypes.c_int
+    lib.zinc_q4k_dequant_f32.argtypes = [P, I32, I32, P, P]
+    for name in ("zinc_mlp_q4k_prefill_workspace_size", "zinc_mlp_q4k_decode_workspace_size"):
+        fn = getattr(lib, name)
+        fn.restype = SZ
+        fn.argtypes = [I32, I32, I32]
+    for name in ("zinc_mlp_q4k_prefill", "zinc_mlp_q4k_decode"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P, P, P, I32, I32, P, P, I32, I32, I32, P, SZ, P]
+    lib.zinc_moe_q4k_experts_workspace_size.restype = SZ
+    lib.zinc_moe_q4k_experts_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+    lib.zinc_moe_q4k_experts.restype = ctypes.c_int
+    lib.zinc_moe_q4k_experts.argtypes = [P, P, P, I32, I32, I32, P, I32, P, P, I32, P, I32, I32, P, SZ, P, P]
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.zinc_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != ZINC_OK:
+        raise ZincError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int | None:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else (int(stream) if stream else None)
+
+
+def _require_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def zinc_q4k_dequant_f32(blocks, rows: int, cols: int, out=None, stream=None):
+    torch = _torch()
+    _require_cuda(blocks, out)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=blocks.device)
+    _check(lib.zinc_q4k_dequant_f32(_ptr(blocks), rows, cols, _ptr(out), _stream(stream)), "zinc_q4k_dequant_f32")
+    return out
+
+
+def prefill_workspace_size(M: int, hidden: int, inter: int) -> int:
+    return int(lib.zinc_mlp_q4k_prefill_workspace_size(M, hidden, inter))
+
+
+def decode_workspace_size(M: int, hidden: int, inter: int) -> int:
+    return int(lib.zinc_mlp_q4k_decode_workspace_size(M, hidden, inter))
+
+
+def moe_workspace_size(M: int, top_k: int, n_experts: int, hidden: int, inter: int) -> int:
+    return int(lib.zinc_moe_q4k_experts_workspace_size(M, top_k, n_experts, hidden, inter))
+
+
+def _dense(fn_name: str, ws_fn, w_gate, w_up, w_down, hidden, inter, x, inter_shift, out_shift, y, workspace,
+           stream):
+    torch = _torch()
+    _require_cuda(w_gate, w_up, w_down, x, y, workspace)
+    M = int(x.shape[0])
+    if y is None:
+        y = torch.empty((M, hidden), dtype=torch.float16, device=x.device)
+    need = ws_fn(M, hidden, inter)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    st = getattr(lib, fn_name)(_ptr(w_gate), _ptr(w_up), _ptr(w_down), hidden, inter, _ptr(x), _ptr(y), M,
+                               inter_shift, out_shift, _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                               _stream(stream))
+    _check(st, fn_name)
+    return y
+
+
+def zinc_mlp_q4k_prefill(w_gate, w_up, w_down, hidden: int, inter: int, x, inter_shift: int = 0, out_shift: int = 0,
+                         y=None, workspace=None, stream=None):
+    """y = fp16(MLP(x) * 2^-out_shift) for fp16 x [M, hidden]; fused prefill kernel."""
+    return _dense("zinc_mlp_q4k_prefill", prefill_workspace_size, w_gate, w_up, w_down, hidden, inter, x,
+                  inter_shift, out_shift, y, workspace, stream)
+
+
+def zinc_mlp_q4k_decode(w_gate, w_up, w_down, hidden: int, inter: int, x, inter_shift: int = 0, out_shift: int = 0,
+                        y=None, workspace=None, stream=None):
+    """Same result as the prefill entry point for 1 <= M <= 8, via HBM-bound matvecs."""
+    return _dense("zinc_mlp_q4k_decode", decode_workspace_size, w_gate, w_up, w_down, hidden, inter, x, inter_shift,
+                  out_shift, y, workspace, stream)
+
+
+def zinc_moe_q4k_experts(w_gate, w_up, w_down, n_experts: int, hidden: int, inter: int, x, expert_ids,
+                         expert_weights, inter_shift: int = 0, out_shift: int = 0, y=None, workspace=None,
+                         dev_error=None, stream=None):
+    """y[t] = sum_s p[t,s] * MLP_{ids[t,s]}(x[t]) with ids/p read on the GPU."""
+    torch = _torch()
+    _require_cuda(w_gate, w_up, w_down, x, expert_ids, expert_weights, y, workspace, dev_error)
+    M = int(x.shape[0])
+    top_k = int(expert_ids.shape[1]) if expert_ids.dim() == 2 else 1
+    if y is None:
+        y = torch.empty((M, hidden), dtype=torch.float16, device=x.device)
+    need = moe_workspace_size(M, top_k, n_experts, hidden, inter)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    st = lib.zinc_moe_q4k_experts(_ptr(w_gate), _ptr(w_up), _ptr(w_down), n_experts, hidden, inter, _ptr(x), M,
+                                  _ptr(expert_ids), _ptr(expert_weights), top_k, _ptr(y), inter_shift, out_shift,
+                                  _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                  _ptr(dev_error), _stream(stream))
+    _check(st, "zinc_moe_q4k_experts")
+    return y

@@ -1,0 +1,137 @@
+// C ABI of the library (include/zinc_mlp.h): host-side argument checks, then
+// the launchers.  Every check runs before the first HIP call, so a rejected
+// call enqueues nothing and needs no GPU.
+#include "../../include/zinc_mlp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxHidden = 16384;
+constexpr int kMaxInter = 65536;
+constexpr int kMaxShift = 30;
+constexpr int kMaxDecodeM = 8;
+constexpr int kMaxExperts = 1024;
+constexpr long long kMaxPrefillM = 1 << 20;
+constexpr long long kMaxMoeSlots = 1 << 24;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool dim_ok(int32_t v, int32_t max) { return v > 0 && v % 256 == 0 && v <= max; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? ZINC_OK : ZINC_ERR_HIP; }
+
+// Checks shared by the dense entry points.
+int check_dense(const void* wg, const void* wu, const void* wd, int32_t hidden, int32_t inter, const void* x,
+                const void* y, int32_t M, int32_t inter_shift, int32_t out_shift, long long max_m) {
+  if (!wg || !wu || !wd || !x || !y) return ZINC_ERR_NULL;
+  if (!dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return ZINC_ERR_SHAPE;
+  if (!aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(x) || !aligned16(y)) return ZINC_ERR_ALIGN;
+  if (M < 0 || M > max_m) return ZINC_ERR_ARG;
+  if (inter_shift < 0 || inter_shift > kMaxShift || out_shift < 0 || out_shift > kMaxShift) return ZINC_ERR_ARG;
+  return ZINC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zinc_strerror(int status) {
+  switch (status) {
+    case ZINC_OK: return "ok";
+    case ZINC_ERR_NULL: return "a required pointer is NULL";
+    case ZINC_ERR_SHAPE: return "hidden/inter/cols must be positive multiples of 256 within the supported range";
+    case ZINC_ERR_ALIGN: return "a pointer is not aligned as required (16 bytes; 4 for ids/weights/error flag)";
+    case ZINC_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_size()";
+    case ZINC_ERR_ARG: return "argument out of range (M, shift or top_k)";
+    case ZINC_ERR_HIP: return "a HIP launch or runtime call failed";
+    case ZINC_ERR_UNSUPPORTED: return "size not supported by this build";
+    default: return "unknown zinc status";
+  }
+}
+
+int zinc_q4k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* out, void* stream) {
+  if (!blocks || !out) return ZINC_ERR_NULL;
+  if (cols <= 0 || cols % 256 != 0) return ZINC_ERR_SHAPE;
+  if (rows < 0) return ZINC_ERR_ARG;
+  if ((long long)rows * cols > INT32_MAX) return ZINC_ERR_SHAPE;
+  if (!aligned16(blocks) || !aligned16(out)) return ZINC_ERR_ALIGN;
+  if (rows == 0) return ZINC_OK;
+  (void)hipGetLastError();
+  return from_hip(zinc::launch_q4k_dequant_f32(blocks, rows, cols, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t zinc_mlp_q4k_prefill_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
+  if (M < 0 || !dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
+  return zinc::prefill_workspace_bytes(M, hidden, inter);
+}
+
+int zinc_mlp_q4k_prefill(const void* w_gate, const void* w_up, const void* w_down, int32_t hidden, int32_t inter,
+                         const void* x_f16, void* y_f16, int32_t M, int32_t inter_shift, int32_t out_shift,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift, kMaxPrefillM);
+  if (st != ZINC_OK) return st;
+  if (M == 0) return ZINC_OK;
+  if (!workspace) return ZINC_ERR_NULL;
+  if (!aligned16(workspace)) return ZINC_ERR_ALIGN;
+  if (workspace_bytes < zinc::prefill_workspace_bytes(M, hidden, inter)) return ZINC_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return from_hip(zinc::launch_prefill(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift,
+                                       workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t zinc_mlp_q4k_decode_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
+  if (M < 0 || M > kMaxDecodeM || !dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
+  return zinc::decode_workspace_bytes(M, hidden, inter);
+}
+
+int zinc_mlp_q4k_decode(const void* w_gate, const void* w_up, const void* w_down, int32_t hidden, int32_t inter,
+                        const void* x_f16, void* y_f16, int32_t M, int32_t inter_shift, int32_t out_shift,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift, kMaxDecodeM);
+  if (st != ZINC_OK) return st;
+  if (M == 0) return ZINC_OK;
+  if (!workspace) return ZINC_ERR_NULL;
+  if (!aligned16(workspace)) return ZINC_ERR_ALIGN;
+  if (workspace_bytes < zinc::decode_workspace_bytes(M, hidden, inter)) return ZINC_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return from_hip(zinc::launch_decode(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift,
+                                      workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t zinc_moe_q4k_experts_workspace_size(int32_t M, int32_t top_k, int32_t n_experts, int32_t hidden,
+                                           int32_t inter) {
+  if (M < 0 || n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > n_experts) return 0;
+  if ((long long)M * top_k > kMaxMoeSlots) return 0;
+  if (!dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
+  return zinc::moe_workspace_bytes(M, top_k, n_experts, hidden, inter);
+}
+
+int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_down, int32_t n_experts, int32_t hidden,
+                         int32_t inter, const void* x_f16, int32_t M, const int32_t* expert_ids,
+                         const float* expert_weights, int32_t top_k, void* y_f16, int32_t inter_shift,
+                         int32_t out_shift, void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                         void* stream) {
+  if (!w_gate || !w_up || !w_down || !x_f16 || !y_f16 || !expert_ids || !expert_weights) return ZINC_ERR_NULL;
+  if (!dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return ZINC_ERR_SHAPE;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(x_f16) || !aligned16(y_f16) ||
+      !aligned4(expert_ids) || !aligned4(expert_weights) || (dev_error && !aligned4(dev_error)))
+    return ZINC_ERR_ALIGN;
+  if (n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > n_experts) return ZINC_ERR_ARG;
+  if (M < 0 || (long long)M * top_k > kMaxMoeSlots) return ZINC_ERR_ARG;
+  if (inter_shift < 0 || inter_shift > kMaxShift || out_shift < 0 || out_shift > kMaxShift) return ZINC_ERR_ARG;
+  if (M == 0) return ZINC_OK;
+  if (!workspace) return ZINC_ERR_NULL;
+  if (!aligned16(workspace)) return ZINC_ERR_ALIGN;
+  if (workspace_bytes < zinc::moe_workspace_bytes(M, top_k, n_experts, hidden, inter)) return ZINC_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return from_hip(zinc::launch_moe(w_gate, w_up, w_down, n_experts, hidden, inter, x_f16, M, expert_ids,
+                                   expert_weights, top_k, y_f16, inter_shift, out_shift, workspace, dev_error,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Host-side launchers of the library's kernels.  Every launcher assumes its
+// arguments were validated by the C ABI layer (capi.cpp): shapes are
+// multiples of 256, pointers are 16-byte aligned, sizes fit the workspace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace zinc {
+
+hipError_t launch_q4k_dequant_f32(const void* blocks, int rows, int cols, float* out, hipStream_t stream);
+
+// Fused prefill.
+size_t prefill_workspace_bytes(int M, int hidden, int inter);
+hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter,
+                          const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
+                          hipStream_t stream);
+
+// Decode matvec pair, 1 <= M <= 8.
+size_t decode_workspace_bytes(int M, int hidden, int inter);
+hipError_t launch_decode(const void* wg, const void* wu, const void* wd, int hidden, int inter,
+                         const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
+                         hipStream_t stream);
+
+// Batched-expert MoE.
+size_t moe_workspace_bytes(int M, int top_k, int n_experts, int hidden, int inter);
+hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_experts, int hidden, int inter,
+                      const void* x, int M, const int32_t* ids, const float* p, int top_k, void* y,
+                      int inter_shift, int out_shift, void* ws, int32_t* dev_error, hipStream_t stream);
+
+}  // namespace zinc

@@ -1,0 +1,16 @@
+// Small helper kernels shared by the prefill and MoE paths.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace zinc {
+
+// Zero n floats (n % 4 == 0, 16-byte aligned).  A kernel, not hipMemsetAsync,
+// so the call stays valid inside a captured HIP graph.
+void launch_fill_zero(float* p, size_t n, hipStream_t stream);
+
+// y[t][n] = fp16(Y32t[n][t] * scale) for t < M, n < H (H % 64 == 0, Mpad % 64 == 0).
+void launch_y32t_to_f16(const float* y32t, int Mpad, _Float16* y, int H, int M, float scale, hipStream_t stream);
+
+}  // namespace zinc

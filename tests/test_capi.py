@@ -1,0 +1,111 @@
+"""The C-ABI library: it loads without a GPU, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call.
+CPU only -- no compute call is made."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import q4_swiglu_mlp_amd as Z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10004        # misaligned by 4
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "zinc_mlp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zinc_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(Z.EXPORTS)
+    for n in names:
+        assert hasattr(Z.lib, n), n
+    # and they are real dynamic symbols of the shared object
+    so = ctypes.CDLL(Z.LIB_PATH)
+    for n in names:
+        assert ctypes.cast(getattr(so, n), ctypes.c_void_p).value
+
+
+def test_strerror_covers_every_status():
+    for st in range(-7, 1):
+        assert Z.strerror(st) and "unknown" not in Z.strerror(st)
+    assert "unknown" in Z.strerror(-99)
+
+
+def prefill(**kw):
+    args = dict(wg=A, wu=A, wd=A, hidden=4096, inter=11008, x=A, y=A, M=256, a=0, b=0, ws=A, wsb=1 << 30)
+    args.update(kw)
+    return Z.lib.zinc_mlp_q4k_prefill(args["wg"], args["wu"], args["wd"], args["hidden"], args["inter"], args["x"],
+                                      args["y"], args["M"], args["a"], args["b"], args["ws"], args["wsb"], None)
+
+
+def decode(**kw):
+    args = dict(wg=A, wu=A, wd=A, hidden=4096, inter=11008, x=A, y=A, M=4, a=0, b=0, ws=A, wsb=1 << 30)
+    args.update(kw)
+    return Z.lib.zinc_mlp_q4k_decode(args["wg"], args["wu"], args["wd"], args["hidden"], args["inter"], args["x"],
+                                     args["y"], args["M"], args["a"], args["b"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("fn", [prefill, decode])
+def test_dense_argument_errors(fn):
+    assert fn(wg=None) == -1 and fn(wd=None) == -1 and fn(x=None) == -1 and fn(y=None) == -1
+    assert fn(hidden=0) == -2 and fn(hidden=300) == -2 and fn(inter=-256) == -2 and fn(inter=1000) == -2
+    assert fn(hidden=16384 + 256) == -2
+    assert fn(wg=MIS) == -3 and fn(x=MIS) == -3 and fn(y=MIS) == -3
+    assert fn(M=-1) == -5
+    assert fn(a=-1) == -5 and fn(a=31) == -5 and fn(b=31) == -5
+    assert fn(ws=None) == -1
+    assert fn(ws=MIS) == -3
+    assert fn(wsb=16) == -4
+    # M == 0: a no-op that succeeds without touching the GPU or the workspace
+    assert fn(M=0, ws=None, wsb=0) == 0
+
+
+def test_decode_token_limit():
+    assert decode(M=9) == -5
+    assert Z.decode_workspace_size(9, 4096, 11008) == 0
+
+
+def test_workspace_sizes():
+    assert Z.prefill_workspace_size(256, 4096, 11008) >= 256 * 4096 * 4
+    assert Z.prefill_workspace_size(257, 4096, 11008) > Z.prefill_workspace_size(256, 4096, 11008)
+    assert Z.prefill_workspace_size(256, 4000, 11008) == 0
+    assert Z.decode_workspace_size(4, 4096, 11008) >= 4 * 11008 * 2
+    assert Z.moe_workspace_size(512, 8, 64, 2048, 768) >= 512 * 2048 * 4 + 512 * 8 * 4
+    assert Z.moe_workspace_size(512, 65, 64, 2048, 768) == 0
+
+
+def moe(**kw):
+    args = dict(wg=A, wu=A, wd=A, E=64, hidden=2048, inter=768, x=A, M=512, ids=A, p=A, k=8, y=A, a=0, b=0, ws=A,
+                wsb=1 << 30, err=None)
+    args.update(kw)
+    return Z.lib.zinc_moe_q4k_experts(args["wg"], args["wu"], args["wd"], args["E"], args["hidden"], args["inter"],
+                                      args["x"], args["M"], args["ids"], args["p"], args["k"], args["y"], args["a"],
+                                      args["b"], args["ws"], args["wsb"], args["err"], None)
+
+
+def test_moe_argument_errors():
+    assert moe(ids=None) == -1 and moe(p=None) == -1 and moe(wu=None) == -1
+    assert moe(hidden=100) == -2
+    assert moe(ids=A + 2) == -3 and moe(err=A + 1) == -3 and moe(x=MIS) == -3
+    assert moe(k=0) == -5 and moe(k=65) == -5 and moe(E=0) == -5 and moe(E=1025, k=8) == -5
+    assert moe(M=-3) == -5 and moe(M=(1 << 24) // 8 + 1) == -5
+    assert moe(ws=None) == -1 and moe(wsb=100) == -4
+    assert moe(M=0, ws=None, wsb=0) == 0
+
+
+def test_dequant_argument_errors():
+    f = Z.lib.zinc_q4k_dequant_f32
+    assert f(None, 4, 256, A, None) == -1
+    assert f(A, 4, 255, A, None) == -2
+    assert f(A, -1, 256, A, None) == -5
+    assert f(MIS, 4, 256, A, None) == -3
+    assert f(A, 1 << 20, 1 << 12, A, None) == -2     # rows*cols beyond int32
+    assert f(A, 0, 256, A, None) == 0
