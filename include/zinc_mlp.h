@@ -70,6 +70,10 @@ typedef enum {
 /* Text of a status code (static storage; never NULL). */
 const char* zinc_strerror(int status);
 
+/* HIP's description of the error behind the most recent ZINC_ERR_HIP returned
+ * on the calling thread, or "no HIP error" (static storage; never NULL). */
+const char* zinc_hip_error_string(void);
+
 /*
  * Q4_K block decoder: out[r*cols + c] = the fp32 weight (row r, column c) of the
  * Q4_K matrix `blocks` [rows x cols], cols % 256 == 0.  Every weight is the exact
@@ -104,11 +108,11 @@ int zinc_mlp_q4k_prefill(const void* w_gate, const void* w_up, const void* w_dow
  * The first streams W_gate and W_up once, computing both projections from one
  * read of x and applying SwiGLU (the same-input gate/up pair fusion of "Four
  * bottlenecks, one CUDA backend", "Bottleneck 3"); the second streams W_down.
- * The per-token intermediate (fp32, M x inter) lives in `workspace` between
- * the two kernels -- for decode it is small and consumed at once ("Fused SwiGLU
- * MLP: ZINC RDNA4 Down-Projection Bandwidth", opening Q&A "Does this affect
- * decode?").  inter_shift has no numerical effect here (the intermediate is
- * fp32); out_shift applies as above.  M > 8 returns ZINC_ERR_ARG.
+ * The per-token intermediate, fp16(h * 2^-inter_shift) [M x inter], lives in
+ * `workspace` between the two kernels -- for decode it is small and consumed at
+ * once ("Fused SwiGLU MLP: ZINC RDNA4 Down-Projection Bandwidth", opening Q&A
+ * "Does this affect decode?").  Both shifts apply as above.  M > 8 returns
+ * ZINC_ERR_ARG.
  */
 size_t zinc_mlp_q4k_decode_workspace_size(int32_t M, int32_t hidden, int32_t inter);
 int zinc_mlp_q4k_decode(const void* w_gate, const void* w_up, const void* w_down,

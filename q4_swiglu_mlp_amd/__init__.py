@@ -31,6 +31,7 @@ STATUS_NAMES = {
 
 EXPORTS = (
     "zinc_strerror",
+    "zinc_hip_error_string",
     "zinc_q4k_dequant_f32",
     "zinc_mlp_q4k_prefill_workspace_size",
     "zinc_mlp_q4k_prefill",
@@ -44,10 +45,18 @@ EXPORTS = (
 class ZincError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({strerror(status)})")
+        msg = f"{where}: {STATUS_NAMES.get(status, status)} ({strerror(status)})"
+        if status == -6:
+            msg += f": {lib.zinc_hip_error_string().decode()}"
+        super().__init__(msg)
 
 
 def _load() -> ctypes.CDLL:
+    # torch bundles its own HIP runtime with the same soname as /opt/rocm's.
+    # Importing torch first makes the library bind to that already-loaded
+    # runtime; otherwise the process would hold two HIP runtimes and torch's
+    # streams and allocations would be foreign to the library's launches.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
@@ -56,6 +65,8 @@ def _load() -> ctypes.CDLL:
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.zinc_strerror.restype = ctypes.c_char_p
     lib.zinc_strerror.argtypes = [ctypes.c_int]
+    lib.zinc_hip_error_string.restype = ctypes.c_char_p
+    lib.zinc_hip_error_string.argtypes = []
     lib.zinc_q4k_dequant_f32.restype = ctypes.c_int
     lib.zinc_q4k_dequant_f32.argtypes = [P, I32, I32, P, P]
     for name in ("zinc_mlp_q4k_prefill_workspace_size", "zinc_mlp_q4k_decode_workspace_size"):

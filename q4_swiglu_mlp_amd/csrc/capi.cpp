@@ -23,7 +23,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool dim_ok(int32_t v, int32_t max) { return v > 0 && v % 256 == 0 && v <= max; }
 
-int from_hip(hipError_t e) { return e == hipSuccess ? ZINC_OK : ZINC_ERR_HIP; }
+thread_local const char* t_last_hip_error = "no HIP error";
+
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return ZINC_OK;
+  t_last_hip_error = hipGetErrorString(e);
+  return ZINC_ERR_HIP;
+}
 
 // Checks shared by the dense entry points.
 int check_dense(const void* wg, const void* wu, const void* wd, int32_t hidden, int32_t inter, const void* x,
@@ -53,6 +59,8 @@ const char* zinc_strerror(int status) {
     default: return "unknown zinc status";
   }
 }
+
+const char* zinc_hip_error_string(void) { return t_last_hip_error; }
 
 int zinc_q4k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* out, void* stream) {
   if (!blocks || !out) return ZINC_ERR_NULL;
