@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused Q4_K SwiGLU MLP on one MI355X.
+
+Headline: one 4096 -> 11008 -> 4096 Q4_K SwiGLU MLP layer on a 256-token
+prefill tile (seed 1), timed over K repeats after W warmup calls, inputs
+already resident in HBM.  A step is one call of zinc_mlp_q4k_prefill (zero
+the fp32 reduction buffer, the fused kernel, the fp16 epilogue).
+
+Printed as ONE JSON line: tokens/s, the fused kernel's MFMA roofline fraction
+(its duration measured with HIP events recorded on its own stream by the
+library's timing hook), the HBM traffic from the committed rocprofv3 counter
+summary when it matches the current kernel source, and the CPU oracle timed
+on the host.  Secondary lines (decode M=1/M=4 over 32 independent layers,
+the 64-expert MoE over two rotated expert sets) ride in "secondary".
+
+usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-secondary] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_K SwiGLU-MLP tokens/s at 4096/11008 M=256; % of MFMA/HBM roofline"
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_fused_m256_traffic.json")
+KERNEL_SOURCES = ("q4_swiglu_mlp_amd/csrc/fused_core.hpp", "q4_swiglu_mlp_amd/csrc/q4k_device.hpp",
+                  "q4_swiglu_mlp_amd/csrc/k_prefill.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def q4k_bytes(rows: int, cols: int) -> int:
+    return rows * (cols // 256) * 144
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_calls(fn, steps: int, warmup: int, torch):
+    """Warmup, then time exactly `steps` calls bracketed by synchronize; returns
+    (wall seconds, per-call main-kernel durations in ms from the timing hook)."""
+    import q4_swiglu_mlp_amd as Z
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    Z.timing_enable(4 * steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = Z.timing_collect(4 * steps)
+    Z.timing_disable()
+    return t1 - t0, ms
+
+
+def headline(args, torch):
+    import numpy as np
+
+    import q4_swiglu_mlp_amd as Z
+    import q4k_synth as S
+    w = S.WORKLOADS["prefill_m256"]
+    dev = torch.device("cuda:0")
+    wg, wu, wd = S.layer_weights(w.seed, 0, w.hidden, w.inter)
+    x = S.workload_x(w)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    gwg, gwu, gwd, gx = t(wg), t(wu), t(wd), t(x)
+    y = torch.empty((w.M, w.hidden), dtype=torch.float16, device=dev)
+    ws = torch.empty(Z.prefill_workspace_size(w.M, w.hidden, w.inter), dtype=torch.uint8, device=dev)
+
+    def call(_i):
+        Z.zinc_mlp_q4k_prefill(gwg, gwu, gwd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
+
+    wall, ms = time_calls(call, args.steps, args.warmup, torch)
+    kern_ms = sum(ms) / len(ms)
+    flops = 6.0 * w.M * w.hidden * w.inter
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("source_sha256") == kernel_source_hash():
+            traffic = rec.get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "k_prefill_fused", "kernel_ms": round(kern_ms, 5),
+                "flops_per_launch": flops}
+    res = {
+        "value": w.M * args.steps / wall,
+        "ms_per_step": wall / args.steps * 1e3,
+        "roofline": roofline,
+        "whole_call_tflops": round(flops / (wall / args.steps) / 1e12, 2),
+    }
+    inputs = (wg, wu, wd, x)
+    return res, inputs
+
+
+def cpu_baseline(inputs):
+    """The oracle as it stands, on the headline workload's full layer (256
+    tokens), on the host cores."""
+    import oracle as O
+    import q4k_synth as S
+    w = S.WORKLOADS["prefill_m256"]
+    wg, wu, wd, x = inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    O.mlp(x, wg, wu, wd, w.hidden, w.inter)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.M / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one full layer, {w.M} tokens (numpy float64 oracle: decode + 3 matmuls), {dt:.2f} s"}
+
+
+def secondary(args, torch):
+    import numpy as np
+
+    import q4_swiglu_mlp_amd as Z
+    import q4k_synth as S
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = []
+
+    # decode: 32 independent layers so the 2.4 GB of weights stream from HBM
+    w1 = S.WORKLOADS["decode_m1"]
+    layers = [tuple(t(a) for a in S.layer_weights(w1.seed, l, w1.hidden, w1.inter)) for l in range(w1.layers)]
+    layer_bytes = 2 * q4k_bytes(w1.inter, w1.hidden) + q4k_bytes(w1.hidden, w1.inter)
+    for name in ("decode_m1", "decode_m4"):
+        w = S.WORKLOADS[name]
+        gx = t(S.workload_x(w))
+        y = torch.empty((w.M, w.hidden), dtype=torch.float16, device=dev)
+        ws = torch.empty(Z.decode_workspace_size(w.M, w.hidden, w.inter), dtype=torch.uint8, device=dev)
+
+        def call(i, w=w, gx=gx, y=y, ws=ws):
+            lg, lu, ld = layers[i % len(layers)]
+            Z.zinc_mlp_q4k_decode(lg, lu, ld, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
+
+        steps = 32 * 10
+        wall, ms = time_calls(call, steps, 32, torch)
+        per_layer = wall / steps
+        gu_ms = sum(ms[0::2]) / len(ms[0::2])
+        dn_ms = sum(ms[1::2]) / len(ms[1::2])
+        gu_bytes = 2 * q4k_bytes(w.inter, w.hidden)
+        dn_bytes = q4k_bytes(w.hidden, w.inter)
+        out.append({
+            "workload": f"decode 4096/11008 M={w.M}, 32-layer sweep",
+            "tokens_per_s_per_layer": round(w.M / per_layer, 1),
+            "us_per_layer": round(per_layer * 1e6, 3),
+            "hbm_GBs_whole_call": round(layer_bytes / per_layer / 1e9, 1),
+            "hbm_frac_whole_call": round(layer_bytes / per_layer / 1e9 / PEAK_HBM_GBS, 4),
+            "kernels": {
+                "k_decode_mv gate+up": {"us": round(gu_ms * 1e3, 3), "GB/s": round(gu_bytes / (gu_ms * 1e-3) / 1e9, 1),
+                                         "frac": round(gu_bytes / (gu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                "k_decode_mv down": {"us": round(dn_ms * 1e3, 3), "GB/s": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
+                                      "frac": round(dn_bytes / (dn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            },
+        })
+        log(f"[bench] {out[-1]}")
+    del layers
+
+    # MoE: two rotated expert sets (340 MB > the 256 MB last-level cache)
+    w = S.WORKLOADS["moe_e64"]
+    sets = [tuple(t(a) for a in S.expert_weights(w.seed, w.n_experts, w.hidden, w.inter, layer=l)) for l in range(2)]
+    gx = t(S.workload_x(w))
+    ids, p = S.workload_routing(w)
+    gids, gp = t(ids), t(p)
+    y = torch.empty((w.M, w.hidden), dtype=torch.float16, device=dev)
+    ws = torch.empty(Z.moe_workspace_size(w.M, w.top_k, w.n_experts, w.hidden, w.inter), dtype=torch.uint8,
+                     device=dev)
+
+    def mcall(i):
+        eg, eu, ed = sets[i % 2]
+        Z.zinc_moe_q4k_experts(eg, eu, ed, w.n_experts, w.hidden, w.inter, gx, gids, gp, w.inter_shift, w.out_shift,
+                               y=y, workspace=ws)
+
+    steps = 100
+    wall, ms = time_calls(mcall, steps, 10, torch)
+    per = wall / steps
+    kern = sum(ms) / len(ms)
+    wbytes = w.n_experts * (2 * q4k_bytes(w.inter, w.hidden) + q4k_bytes(w.hidden, w.inter))
+    flops = 6.0 * w.M * w.top_k * w.hidden * w.inter
+    out.append({
+        "workload": "MoE E=64 top-8, 2048->768, M=512, two rotated expert sets",
+        "tokens_per_s": round(w.M / per, 1),
+        "us_per_call": round(per * 1e6, 3),
+        "k_moe_fused_us": round(kern * 1e3, 3),
+        "hbm_frac_fused_kernel": round(wbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "mfma_frac_fused_kernel": round(flops / (kern * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+    })
+    log(f"[bench] {out[-1]}")
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3x), the reference kernel that "
+                         "scales the FETCH_SIZE/WRITE_SIZE counters to bytes")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "copies": 3}))
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the path has no multi-GPU mode (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}). Token-parallel sharding needs no collective; see DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    log("[bench] headline: prefill 4096/11008 M=256")
+    res, inputs = headline(args, torch)
+    log(f"[bench] headline {res['value']:.1f} tok/s, kernel {res['roofline']['kernel_ms'] * 1e3:.1f} us, "
+        f"{res['roofline']['achieved']} TFLOP/s")
+    sec = None if args.no_secondary else secondary(args, torch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(inputs)
+    if cpu:
+        log(f"[bench] cpu baseline {cpu}")
+    line = {
+        "metric": METRIC,
+        "value": round(res["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "one Q4_K SwiGLU MLP layer, hidden 4096, intermediate 11008, 256-token prefill tile, "
+                               "seed 1", "hidden": 4096, "inter": 11008, "M": 256, "weights": "Q4_K",
+                   "compute": "fp16 MFMA, fp32 accumulate"},
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "whole_call_tflops": res["whole_call_tflops"],
+        "secondary": sec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

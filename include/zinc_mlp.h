@@ -144,6 +144,22 @@ int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_dow
                          void* workspace, size_t workspace_bytes, int32_t* dev_error,
                          void* stream);
 
+/*
+ * Kernel timing for benchmarks and profiles (off by default; not needed for
+ * correct use).  After zinc_timing_enable(capacity), every prefill, decode and
+ * MoE call records a HIP event pair on its stream immediately around its main
+ * kernel -- the fused unit kernel for prefill and MoE; for decode, one pair
+ * around the gate/up matvec and one around the down matvec -- for up to
+ * `capacity` pairs.  zinc_timing_collect() waits for the recorded events,
+ * writes each pair's elapsed milliseconds to ms[0..*n_out) in launch order and
+ * restarts the recording; zinc_timing_disable() stops it and destroys the
+ * events.  Not meant to be used while other threads call the library.
+ * Errors: capacity outside [1, 2^20] -> ZINC_ERR_ARG; event failures -> ZINC_ERR_HIP.
+ */
+int zinc_timing_enable(int32_t capacity);
+int zinc_timing_collect(float* ms, int32_t capacity, int32_t* n_out);
+void zinc_timing_disable(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,9 @@ EXPORTS = (
     "zinc_mlp_q4k_decode",
     "zinc_moe_q4k_experts_workspace_size",
     "zinc_moe_q4k_experts",
+    "zinc_timing_enable",
+    "zinc_timing_collect",
+    "zinc_timing_disable",
 )
 
 
@@ -81,10 +84,33 @@ def _load() -> ctypes.CDLL:
     lib.zinc_moe_q4k_experts_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.zinc_moe_q4k_experts.restype = ctypes.c_int
     lib.zinc_moe_q4k_experts.argtypes = [P, P, P, I32, I32, I32, P, I32, P, P, I32, P, I32, I32, P, SZ, P, P]
+    lib.zinc_timing_enable.restype = ctypes.c_int
+    lib.zinc_timing_enable.argtypes = [I32]
+    lib.zinc_timing_collect.restype = ctypes.c_int
+    lib.zinc_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_float), I32, ctypes.POINTER(ctypes.c_int32)]
+    lib.zinc_timing_disable.restype = None
+    lib.zinc_timing_disable.argtypes = []
     return lib
 
 
 lib = _load()
+
+
+def timing_enable(capacity: int) -> None:
+    """Record a HIP event pair around the main kernel(s) of each following call."""
+    _check(lib.zinc_timing_enable(capacity), "zinc_timing_enable")
+
+
+def timing_collect(capacity: int) -> list[float]:
+    """Wait for the recorded launches; their kernel durations in milliseconds."""
+    buf = (ctypes.c_float * capacity)()
+    n = ctypes.c_int32(0)
+    _check(lib.zinc_timing_collect(buf, capacity, ctypes.byref(n)), "zinc_timing_collect")
+    return [float(buf[i]) for i in range(n.value)]
+
+
+def timing_disable() -> None:
+    lib.zinc_timing_disable()
 
 
 def strerror(status: int) -> str:

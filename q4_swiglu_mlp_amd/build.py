@@ -44,7 +44,7 @@ def build(verbose: bool = False) -> str:
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     report = [ln for ln in proc.stdout.splitlines() if "remark:" in ln]
     other = [ln for ln in proc.stdout.splitlines()
-             if "remark:" not in ln and "packed-fp32-ops" not in ln and ln.strip()]
+             if (" error:" in ln or " warning:" in ln) and "packed-fp32-ops" not in ln]
     with open(os.path.join(LIB_DIR, "resource_usage.txt"), "w") as f:
         f.write("\n".join(report) + "\n")
     if proc.returncode != 0:

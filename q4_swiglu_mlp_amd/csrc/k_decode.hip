@@ -9,15 +9,18 @@
 //   k_decode_mv<GATEUP=false> streams W_down against that intermediate and
 //     writes y = fp16(acc * 2^(inter_shift - out_shift)).
 //
-// Work split: a 256-thread block owns NR = 8 rows; 32 threads per row.  Within
-// a row, thread q handles part p = q % 8 of each block (16 quant bytes = 16 low
-// + 16 high nibbles, i.e. half of sub-blocks 2c and 2c+1, c = p/2) for blocks
-// b = q/8, q/8 + 4, ...; the 32 partial sums are reduced with cross-lane
-// shuffles.  The activation is staged in LDS, K-chunk by K-chunk, as fp16 with
-// the middle two elements of every group of four swapped, which matches the
-// pair order the nibble unpack produces, plus per-16 sums used to remove the
-// exact fp16 nibble offsets (1024 or 64) and the mins in fp32:
-//   sum_k w_k x_k = s*(A - off*X16) - dm*X16  with A = sum (off + q_k) x_k.
+// Work split.  A wave owns 16 rows; lane l works on row l/4 and 64-weight
+// chunk c = l%4 of every block it visits (32 quant bytes: sub-blocks 2c in the
+// low nibbles, 2c+1 in the high ones), so the four lanes of a row read the
+// block's 128 quant bytes contiguously.  KSPLIT waves of a block share the same
+// 16 rows and take every KSPLIT-th block (cross-wave sums through LDS), which
+// gives the short-row down projection enough waves to keep HBM busy.  Blocks
+// are fetched UNROLL at a time so several loads per lane are in flight.
+// The activation is staged once per block of threads in LDS as fp16 with the
+// middle two elements of every group of four swapped -- the pair order the
+// nibble unpack produces -- plus fp32 sums of every 32-element sub-block, which
+// remove the exact fp16 nibble offsets (1024, 64) and the mins:
+//   sum_k w_k x_k = s*A - (off*s + dmin*m)*X32,  A = sum_k (off + q_k) x_k.
 #include "q4k_device.hpp"
 #include "launch.hpp"
 
@@ -26,45 +29,96 @@ namespace zinc {
 namespace {
 
 constexpr int DTHREADS = 256;
-constexpr int NR = 8;                    // rows per block
-constexpr int TPR = DTHREADS / NR;       // threads per row (32)
-constexpr int BPH = TPR / 8;             // block phases per row (4)
-constexpr int KC = 2048;                 // K elements staged per chunk
+constexpr int UNROLL = 4;
 
-__device__ __forceinline__ int swap_mid4(int k) {
-  const int e = k & 3;
-  return (k & ~3) | ((e == 1) ? 2 : (e == 2) ? 1 : e);
+// K elements staged per pass: the gate/up matvec stages 4096 (one pass at
+// hidden 4096); the down matvec stages as much of the intermediate as about
+// 88 KB of LDS holds.
+constexpr int KC_GATEUP = 4096;
+template <int MM>
+struct DownKC {
+  static constexpr int value = (MM <= 2) ? 16384 : (MM <= 4) ? 11264 : 5632;
+};
+
+struct BlockData {
+  uint4 hdr, q0, q1;
+};
+
+__device__ __forceinline__ BlockData load_block(const uint8_t* bp, int c) {
+  BlockData d;
+  d.hdr = *reinterpret_cast<const uint4*>(bp);
+  d.q0 = *reinterpret_cast<const uint4*>(bp + 16 + 32 * c);
+  d.q1 = *reinterpret_cast<const uint4*>(bp + 32 + 32 * c);
+  return d;
 }
 
-template <int MM, bool GATEUP>
+// Accumulate one block's contribution (this lane's chunk c) into acc[t].
+template <int MM>
+__device__ __forceinline__ void block_dot(const BlockData& bd, int c, const _Float16* __restrict__ xs,
+                                          const float* __restrict__ x32, int KC, int kl, float* acc) {
+  float Alo[MM], Ahi[MM];
+#pragma unroll
+  for (int t = 0; t < MM; ++t) Alo[t] = Ahi[t] = 0.0f;
+#pragma unroll
+  for (int dwi = 0; dwi < 8; ++dwi) {
+    const uint4& qq = (dwi < 4) ? bd.q0 : bd.q1;
+    const int k4 = dwi & 3;
+    const uint32_t Q = (k4 == 0) ? qq.x : (k4 == 1) ? qq.y : (k4 == 2) ? qq.z : qq.w;
+    const half2v a0 = bits_h2((Q & 0x000F000Fu) | 0x64006400u);
+    const half2v a1 = bits_h2(((Q >> 8) & 0x000F000Fu) | 0x64006400u);
+    const half2v a2 = bits_h2((Q & 0x00F000F0u) | 0x54005400u);
+    const half2v a3 = bits_h2(((Q >> 8) & 0x00F000F0u) | 0x54005400u);
+#pragma unroll
+    for (int t = 0; t < MM; ++t) {
+      const uint2 xl = *reinterpret_cast<const uint2*>(xs + t * KC + kl + 4 * dwi);
+      const uint2 xh = *reinterpret_cast<const uint2*>(xs + t * KC + kl + 32 + 4 * dwi);
+      Alo[t] = __builtin_amdgcn_fdot2(a0, bits_h2(xl.x), Alo[t], false);
+      Alo[t] = __builtin_amdgcn_fdot2(a1, bits_h2(xl.y), Alo[t], false);
+      Ahi[t] = __builtin_amdgcn_fdot2(a2, bits_h2(xh.x), Ahi[t], false);
+      Ahi[t] = __builtin_amdgcn_fdot2(a3, bits_h2(xh.y), Ahi[t], false);
+    }
+  }
+  const float d = half_bits_to_float(bd.hdr.x & 0xFFFFu), dmin = half_bits_to_float(bd.hdr.x >> 16);
+  const SixBit sb = unpack_sixbit(bd.hdr.y, bd.hdr.z, bd.hdr.w);
+  const float slo = d * (float)sixbit_sc(sb, 2 * c), shi = d * (float)sixbit_sc(sb, 2 * c + 1);
+  const float clo = 1024.0f * slo + dmin * (float)sixbit_m(sb, 2 * c);
+  const float chi = 64.0f * shi + dmin * (float)sixbit_m(sb, 2 * c + 1);
+  const int xi = kl >> 5;
+#pragma unroll
+  for (int t = 0; t < MM; ++t)
+    acc[t] += slo * Alo[t] - clo * x32[t * (KC / 32) + xi] + shi * Ahi[t] - chi * x32[t * (KC / 32) + xi + 1];
+}
+
+template <int MM, bool GATEUP, int KSPLIT, int KCMAX>
 __global__ __launch_bounds__(DTHREADS) void k_decode_mv(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
                                                         int K, int N, const _Float16* __restrict__ xin, int M,
                                                         _Float16* __restrict__ out, float scale) {
-  __shared__ __attribute__((aligned(16))) _Float16 xs[MM * KC];
-  __shared__ float x16[MM * (KC / 16)];
+  constexpr int RG = 4 / KSPLIT;                 // 16-row groups per block of threads
+  __shared__ __attribute__((aligned(16))) _Float16 xs[MM * KCMAX];
+  __shared__ float x32[MM * (KCMAX / 32)];
+  __shared__ float red[(KSPLIT > 1) ? (4 * 64 * MM * (GATEUP ? 2 : 1)) : 1];
 
   const int tid = threadIdx.x;
-  const int rloc = tid / TPR, q = tid % TPR;
-  const int p = q & 7, bph = q >> 3;
-  const int c = p >> 1;                      // 64-weight chunk of the block
-  const int lhalf = (p & 1) * 16;            // first position within the chunk's 32
-  const int row = blockIdx.x * NR + rloc;    // N % NR == 0 (N is a multiple of 256)
+  const int lane = tid & 63, wave = tid >> 6;
+  const int rg = wave / KSPLIT, kph = wave % KSPLIT;
+  const int r = lane >> 2, c = lane & 3;
+  const int row = (blockIdx.x * RG + rg) * 16 + r;   // N % 256 == 0
   const int nb = K / QK;
+  const int KC = min(K, KCMAX);
 
   float acc0[MM], acc1[MM];
 #pragma unroll
   for (int t = 0; t < MM; ++t) acc0[t] = acc1[t] = 0.0f;
-
   const uint8_t* r0 = W0 + (size_t)row * nb * BLOCK_BYTES;
   const uint8_t* r1 = GATEUP ? W1 + (size_t)row * nb * BLOCK_BYTES : nullptr;
 
   for (int k0 = 0; k0 < K; k0 += KC) {
-    const int kc = min(KC, K - k0);          // multiple of 256
-    __syncthreads();
-    // stage: MM x kc fp16, 8 per piece, plus sums of 16
-    const int pieces = MM * (kc / 8);
-    for (int ci = tid; ci < pieces; ci += DTHREADS) {
-      const int t = ci / (kc / 8), a = ci % (kc / 8);
+    const int kc = min(KC, K - k0);              // multiple of 256
+    if (k0 > 0) __syncthreads();
+    // stage x[0..M) x [k0, k0+kc): 8 elements per piece; 4 pieces form a 32-sum
+    const int per_row = kc / 8;
+    for (int ci = tid; ci < MM * per_row; ci += DTHREADS) {
+      const int t = ci / per_row, a = ci % per_row;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (t < M) v = *reinterpret_cast<const uint4*>(xin + (size_t)t * K + k0 + 8 * a);
       const uint32_t lo0 = (v.x & 0xFFFFu) | (v.y << 16);
@@ -76,104 +130,75 @@ __global__ __launch_bounds__(DTHREADS) void k_decode_mv(const uint8_t* __restric
       float s8 = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s8 += (float)hv[e];
-      // pieces 2i and 2i+1 of a row form one group of 16 (kc/8 is even)
-      const float other = __shfl_xor(s8, 1, 64);
-      if ((a & 1) == 0) x16[t * (KC / 16) + (a >> 1)] = s8 + other;
+      // per_row is a multiple of 32, so a group of 4 pieces never straddles
+      // rows or the active-lane boundary of the last iteration
+      s8 += __shfl_xor(s8, 1, 64);
+      s8 += __shfl_xor(s8, 2, 64);
+      if ((a & 3) == 0) x32[t * (KC / 32) + (a >> 2)] = s8;
     }
     __syncthreads();
 
-    for (int bl = bph; bl < kc / QK; bl += BPH) {
-      const int b = k0 / QK + bl;
-      const uint8_t* bp0 = r0 + (size_t)b * BLOCK_BYTES;
-      const uint4 h0 = *reinterpret_cast<const uint4*>(bp0);
-      const uint4 q0 = *reinterpret_cast<const uint4*>(bp0 + 16 + 32 * c + lhalf);
-      uint4 h1 = make_uint4(0, 0, 0, 0), q1 = make_uint4(0, 0, 0, 0);
-      if (GATEUP) {
-        const uint8_t* bp1 = r1 + (size_t)b * BLOCK_BYTES;
-        h1 = *reinterpret_cast<const uint4*>(bp1);
-        q1 = *reinterpret_cast<const uint4*>(bp1 + 16 + 32 * c + lhalf);
-      }
-      const int kl = bl * QK + 64 * c + lhalf;      // local index of the low-nibble run
-      float A0lo[MM], A0hi[MM], A1lo[MM], A1hi[MM];
+    const int b_begin = k0 / QK, b_end = (k0 + kc) / QK;
+    for (int b = b_begin + kph; b < b_end; b += UNROLL * KSPLIT) {
+      BlockData d0[UNROLL], d1[UNROLL];
 #pragma unroll
-      for (int t = 0; t < MM; ++t) A0lo[t] = A0hi[t] = A1lo[t] = A1hi[t] = 0.0f;
-#pragma unroll
-      for (int dwi = 0; dwi < 4; ++dwi) {
-        const uint32_t Q0 = (dwi == 0) ? q0.x : (dwi == 1) ? q0.y : (dwi == 2) ? q0.z : q0.w;
-        const uint32_t Q1 = (dwi == 0) ? q1.x : (dwi == 1) ? q1.y : (dwi == 2) ? q1.z : q1.w;
-        const half2v a0 = bits_h2((Q0 & 0x000F000Fu) | 0x64006400u);
-        const half2v a1 = bits_h2(((Q0 >> 8) & 0x000F000Fu) | 0x64006400u);
-        const half2v a2 = bits_h2((Q0 & 0x00F000F0u) | 0x54005400u);
-        const half2v a3 = bits_h2(((Q0 >> 8) & 0x00F000F0u) | 0x54005400u);
-        half2v b0, b1, b2, b3;
-        if (GATEUP) {
-          b0 = bits_h2((Q1 & 0x000F000Fu) | 0x64006400u);
-          b1 = bits_h2(((Q1 >> 8) & 0x000F000Fu) | 0x64006400u);
-          b2 = bits_h2((Q1 & 0x00F000F0u) | 0x54005400u);
-          b3 = bits_h2(((Q1 >> 8) & 0x00F000F0u) | 0x54005400u);
-        }
-#pragma unroll
-        for (int t = 0; t < MM; ++t) {
-          const uint2 xl = *reinterpret_cast<const uint2*>(xs + t * KC + kl + 4 * dwi);
-          const uint2 xh = *reinterpret_cast<const uint2*>(xs + t * KC + kl + 32 + 4 * dwi);
-          A0lo[t] = __builtin_amdgcn_fdot2(a0, bits_h2(xl.x), A0lo[t], false);
-          A0lo[t] = __builtin_amdgcn_fdot2(a1, bits_h2(xl.y), A0lo[t], false);
-          A0hi[t] = __builtin_amdgcn_fdot2(a2, bits_h2(xh.x), A0hi[t], false);
-          A0hi[t] = __builtin_amdgcn_fdot2(a3, bits_h2(xh.y), A0hi[t], false);
-          if (GATEUP) {
-            A1lo[t] = __builtin_amdgcn_fdot2(b0, bits_h2(xl.x), A1lo[t], false);
-            A1lo[t] = __builtin_amdgcn_fdot2(b1, bits_h2(xl.y), A1lo[t], false);
-            A1hi[t] = __builtin_amdgcn_fdot2(b2, bits_h2(xh.x), A1hi[t], false);
-            A1hi[t] = __builtin_amdgcn_fdot2(b3, bits_h2(xh.y), A1hi[t], false);
-          }
+      for (int u = 0; u < UNROLL; ++u) {
+        const int bb = b + u * KSPLIT;
+        if (bb < b_end) {
+          d0[u] = load_block(r0 + (size_t)bb * BLOCK_BYTES, c);
+          if (GATEUP) d1[u] = load_block(r1 + (size_t)bb * BLOCK_BYTES, c);
         }
       }
-      // fold: s*(A - off*X) - dm*X = s*A - (off*s + dm)*X, per sub-block
-      {
-        const float d = half_bits_to_float(h0.x & 0xFFFFu), dmin = half_bits_to_float(h0.x >> 16);
-        const SixBit sb = unpack_sixbit(h0.y, h0.z, h0.w);
-        const float slo = d * (float)sixbit_sc(sb, 2 * c), shi = d * (float)sixbit_sc(sb, 2 * c + 1);
-        const float clo = 1024.0f * slo + dmin * (float)sixbit_m(sb, 2 * c);
-        const float chi = 64.0f * shi + dmin * (float)sixbit_m(sb, 2 * c + 1);
-        const int xi = (kl >> 4);
 #pragma unroll
-        for (int t = 0; t < MM; ++t) {
-          const float Xlo = x16[t * (KC / 16) + xi], Xhi = x16[t * (KC / 16) + xi + 2];
-          acc0[t] += slo * A0lo[t] - clo * Xlo + shi * A0hi[t] - chi * Xhi;
-        }
-      }
-      if (GATEUP) {
-        const float d = half_bits_to_float(h1.x & 0xFFFFu), dmin = half_bits_to_float(h1.x >> 16);
-        const SixBit sb = unpack_sixbit(h1.y, h1.z, h1.w);
-        const float slo = d * (float)sixbit_sc(sb, 2 * c), shi = d * (float)sixbit_sc(sb, 2 * c + 1);
-        const float clo = 1024.0f * slo + dmin * (float)sixbit_m(sb, 2 * c);
-        const float chi = 64.0f * shi + dmin * (float)sixbit_m(sb, 2 * c + 1);
-        const int xi = (kl >> 4);
-#pragma unroll
-        for (int t = 0; t < MM; ++t) {
-          const float Xlo = x16[t * (KC / 16) + xi], Xhi = x16[t * (KC / 16) + xi + 2];
-          acc1[t] += slo * A1lo[t] - clo * Xlo + shi * A1hi[t] - chi * Xhi;
+      for (int u = 0; u < UNROLL; ++u) {
+        const int bb = b + u * KSPLIT;
+        if (bb < b_end) {
+          const int kl = (bb - b_begin) * QK + 64 * c;
+          block_dot<MM>(d0[u], c, xs, x32, KC, kl, acc0);
+          if (GATEUP) block_dot<MM>(d1[u], c, xs, x32, KC, kl, acc1);
         }
       }
     }
   }
 
-  // reduce over the 32 threads of the row (one half of the wave)
+  // reduce over the 4 lanes of a row, then over the KSPLIT waves
 #pragma unroll
   for (int t = 0; t < MM; ++t) {
-#pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) {
-      acc0[t] += __shfl_xor(acc0[t], m, 64);
-      if (GATEUP) acc1[t] += __shfl_xor(acc1[t], m, 64);
+    acc0[t] += __shfl_xor(acc0[t], 1, 64);
+    acc0[t] += __shfl_xor(acc0[t], 2, 64);
+    if (GATEUP) {
+      acc1[t] += __shfl_xor(acc1[t], 1, 64);
+      acc1[t] += __shfl_xor(acc1[t], 2, 64);
     }
   }
-  if (q == 0) {
+  if (KSPLIT > 1) {
+    if (c == 0) {
+#pragma unroll
+      for (int t = 0; t < MM; ++t) {
+        red[((wave * 16 + r) * MM + t) * (GATEUP ? 2 : 1)] = acc0[t];
+        if (GATEUP) red[((wave * 16 + r) * MM + t) * 2 + 1] = acc1[t];
+      }
+    }
+    __syncthreads();
+    if (kph != 0) return;
+    if (c == 0) {
+#pragma unroll
+      for (int t = 0; t < MM; ++t) {
+        float s0 = 0.0f, s1 = 0.0f;
+        for (int w = 0; w < KSPLIT; ++w) {
+          s0 += red[(((rg * KSPLIT + w) * 16 + r) * MM + t) * (GATEUP ? 2 : 1)];
+          if (GATEUP) s1 += red[(((rg * KSPLIT + w) * 16 + r) * MM + t) * 2 + 1];
+        }
+        acc0[t] = s0;
+        acc1[t] = s1;
+      }
+    }
+  }
+  if (c == 0) {
 #pragma unroll
     for (int t = 0; t < MM; ++t) {
       if (t < M) {
-        float v;
-        if (GATEUP) v = silu_f32(acc0[t]) * acc1[t] * scale;
-        else v = acc0[t] * scale;
+        const float v = GATEUP ? silu_f32(acc0[t]) * acc1[t] * scale : acc0[t] * scale;
         out[(size_t)t * N + row] = (_Float16)v;
       }
     }
@@ -184,12 +209,18 @@ template <int MM>
 hipError_t launch_decode_mm(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
                             void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
   _Float16* hbuf = static_cast<_Float16*>(ws);
-  hipLaunchKernelGGL((k_decode_mv<MM, true>), dim3(inter / NR), dim3(DTHREADS), 0, stream,
+  // gate/up: pairs of waves share 16 rows (32 rows per block of threads)
+  timing_begin(stream);
+  hipLaunchKernelGGL((k_decode_mv<MM, true, 2, KC_GATEUP>), dim3(inter / 32), dim3(DTHREADS), 0, stream,
                      static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu), hidden, inter,
                      static_cast<const _Float16*>(x), M, hbuf, ldexpf(1.0f, -inter_shift));
-  hipLaunchKernelGGL((k_decode_mv<MM, false>), dim3(hidden / NR), dim3(DTHREADS), 0, stream,
+  timing_end(stream);
+  // down: 4 waves share 16 rows, each taking every 4th block
+  timing_begin(stream);
+  hipLaunchKernelGGL((k_decode_mv<MM, false, 4, DownKC<MM>::value>), dim3(hidden / 16), dim3(DTHREADS), 0, stream,
                      static_cast<const uint8_t*>(wd), static_cast<const uint8_t*>(nullptr), inter, hidden, hbuf, M,
                      static_cast<_Float16*>(y), ldexpf(1.0f, inter_shift - out_shift));
+  timing_end(stream);
   return hipGetLastError();
 }
 

@@ -1,5 +1,18 @@
 // Dense batched prefill: the fused Q4_K SwiGLU unit (fused_core.hpp) over
-// (64-token tiles) x (128-row intermediate chunks), then a scaling epilogue.
+// (token tiles) x (intermediate chunks); every unit stores its fp32 partial of
+// the down projection, and a reduce kernel sums the chunks, scales and writes
+// y in fp16.
+//
+// Tile choice.  A unit of MT tokens x IC intermediate rows decodes every weight
+// of its chunk once for its MT tokens, so the dequant work grows with M/MT; its
+// partial output is MT x hidden fp32, so the reduction traffic grows with
+// I/IC.  Units must also cover the 256 CUs.  Configurations (MT, IC <= ICMAX):
+//   A: MT=32, ICMAX=384 -- M <= 512: 256 units at M=256 (8 tiles x 32 chunks)
+//   B: MT=64, ICMAX=640 -- large M, balanced dequant/reduction
+//   C: MT=64, ICMAX=384 -- large M, more chunks (more units, more reduction)
+#include <cstdlib>
+#include <cstring>
+
 #include "fused_core.hpp"
 #include "launch.hpp"
 #include "util_kernels.hpp"
@@ -8,20 +21,17 @@ namespace zinc {
 
 namespace {
 
-constexpr int TT_DENSE = 2;   // 64 tokens per unit
-constexpr int RT_DENSE = 1;   // 128 intermediate rows per unit
-using DenseCfg = FusedCfg<TT_DENSE, RT_DENSE>;
-
-__global__ __launch_bounds__(FU_THREADS) void k_prefill_fused(const uint8_t* __restrict__ wg,
+template <int TT, int RTW, int ICMAX>
+__global__ __launch_bounds__(64 * FuWaves<TT>::value) void k_prefill_fused(const uint8_t* __restrict__ wg,
                                                               const uint8_t* __restrict__ wu,
                                                               const uint8_t* __restrict__ wd, int H, int I,
                                                               const _Float16* __restrict__ x, int M,
-                                                              float* __restrict__ y32t, int Mpad, float inter_scale,
+                                                              float* __restrict__ P, int Mpad, float inter_scale,
                                                               int n_tiles, int n_chunks) {
-  __shared__ __attribute__((aligned(16))) _Float16 xs[DenseCfg::MT * DenseCfg::XS];
-  __shared__ __attribute__((aligned(16))) _Float16 hs[DenseCfg::MT * DenseCfg::HS];
-  __shared__ int tok[DenseCfg::MT];
-  __shared__ float wrow[DenseCfg::MT];
+  using C = FusedCfg<TT, RTW, ICMAX>;
+  __shared__ __attribute__((aligned(16))) FusedSmem<TT, RTW, ICMAX> sm;
+  __shared__ int tok[C::MT];
+  __shared__ float wrow[C::MT];
 
   // Units of the same intermediate chunk share block id mod 8, so they land on
   // the same XCD and its L2 serves that weight chunk to every token tile.
@@ -30,40 +40,140 @@ __global__ __launch_bounds__(FU_THREADS) void k_prefill_fused(const uint8_t* __r
   const int tile = rem >> 3;
   const int chunk = grp * 8 + (rem & 7);
   if (chunk >= n_chunks) return;
+  const int npan = I / 64;
+  const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
+  const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
 
-  if (threadIdx.x < DenseCfg::MT) {
-    const int t = tile * DenseCfg::MT + threadIdx.x;
+  if (threadIdx.x < C::MT) {
+    const int t = tile * C::MT + threadIdx.x;
     tok[threadIdx.x] = (t < M) ? t : -1;
     wrow[threadIdx.x] = 1.0f;
   }
   __syncthreads();
-  fused_unit<TT_DENSE, RT_DENSE>(wg, wu, wd, H, I, x, tok, wrow, chunk, y32t, Mpad, inter_scale, xs, hs);
+  OutPartial out{P, Mpad, H};
+  fused_unit<TT, RTW, ICMAX>(wg, wu, wd, H, I, x, tok, wrow, chunk, r0, r1, tile * C::MT, inter_scale, out, sm);
 }
 
+// y[t][n] = fp16(scale * sum_c P[c][n][t]) through a 64x64 LDS transpose.
+// Thread (tx, ty) sums the float4 of tokens 4tx..4tx+3 for hidden rows
+// ty + 16i (i < 4) over all chunks, four chunks' loads in flight at a time.
+__global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict__ P, int S, int H, int Mpad,
+                                                        _Float16* __restrict__ y, int M, float scale) {
+  __shared__ float tile[64][65];
+  const int n0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const size_t plane = (size_t)H * Mpad;
+  const float* base = P + (size_t)(n0 + ty) * Mpad + t0 + 4 * tx;
+  int c = 0;
+  for (; c + 4 <= S; c += 4) {
+    float4 v[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[u][i] = *reinterpret_cast<const float4*>(base + (c + u) * plane + (size_t)16 * i * Mpad);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i].x += v[u][i].x; acc[i].y += v[u][i].y; acc[i].z += v[u][i].z; acc[i].w += v[u][i].w;
+      }
+  }
+  for (; c < S; ++c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(base + c * plane + (size_t)16 * i * Mpad);
+      acc[i].x += v.x; acc[i].y += v.y; acc[i].z += v.z; acc[i].w += v.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tile[ty + 16 * i][4 * tx + 0] = acc[i].x;
+    tile[ty + 16 * i][4 * tx + 1] = acc[i].y;
+    tile[ty + 16 * i][4 * tx + 2] = acc[i].z;
+    tile[ty + 16 * i][4 * tx + 3] = acc[i].w;
+  }
+  __syncthreads();
+  const int wx = threadIdx.x & 63, wy = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = t0 + wy + 4 * i;
+    if (t < M) y[(size_t)t * H + n0 + wx] = (_Float16)(tile[wx][wy + 4 * i] * scale);
+  }
+}
+
+struct Plan {
+  char cfg;      // 'A', 'B', 'C'
+  int MT, ICMAX;
+  int n_tiles, n_chunks;
+  int Mpad;
+};
+
 int round_up(int a, int b) { return (a + b - 1) / b * b; }
+
+Plan make_plan(int M, int H, int I) {
+  (void)H;
+  Plan p;
+  p.cfg = (M <= 512) ? 'A' : 'B';
+  int chunks_wanted = 0;
+  // tuning override: ZINC_PREFILL_CFG="<A|B|C>[:<chunks>]"
+  if (const char* e = std::getenv("ZINC_PREFILL_CFG")) {
+    if (e[0] == 'A' || e[0] == 'B' || e[0] == 'C') p.cfg = e[0];
+    if (e[0] && e[1] == ':') chunks_wanted = std::atoi(e + 2);
+  }
+  p.MT = (p.cfg == 'A') ? 32 : 64;
+  p.ICMAX = (p.cfg == 'B') ? 640 : 384;
+  const int npan = I / 64;
+  const int min_chunks = (npan + p.ICMAX / 64 - 1) / (p.ICMAX / 64);
+  p.n_tiles = (M + p.MT - 1) / p.MT;
+  int chunks = min_chunks;
+  if (p.cfg == 'A') {
+    // enough units to cover the 256 CUs, up to one 64-row panel per chunk
+    const int want = (256 + p.n_tiles - 1) / p.n_tiles;
+    chunks = want > chunks ? want : chunks;
+  }
+  if (chunks_wanted > 0) chunks = chunks_wanted;
+  if (chunks < min_chunks) chunks = min_chunks;
+  if (chunks > npan) chunks = npan;
+  p.n_chunks = chunks;
+  p.Mpad = round_up(p.n_tiles * p.MT, 64);   // the reduce kernel works on 64-token tiles
+  return p;
+}
+
+template <int TT, int RTW, int ICMAX>
+void launch_cfg(const Plan& p, const void* wg, const void* wu, const void* wd, int H, int I, const void* x, int M,
+                float* P, float inter_scale, hipStream_t stream) {
+  const int n_groups = (p.n_chunks + 7) / 8;
+  hipLaunchKernelGGL((k_prefill_fused<TT, RTW, ICMAX>), dim3(n_groups * 8 * p.n_tiles), dim3(FusedCfg<TT, RTW, ICMAX>::THREADS), 0, stream,
+                     static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
+                     static_cast<const uint8_t*>(wd), H, I, static_cast<const _Float16*>(x), M, P, p.Mpad,
+                     inter_scale, p.n_tiles, p.n_chunks);
+}
 
 }  // namespace
 
 size_t prefill_workspace_bytes(int M, int hidden, int inter) {
-  (void)inter;
-  const int Mpad = round_up(M > 0 ? M : 1, 64);
-  return (size_t)hidden * Mpad * sizeof(float);
+  const Plan p = make_plan(M > 0 ? M : 1, hidden, inter);
+  return (size_t)p.n_chunks * hidden * p.Mpad * sizeof(float);
 }
 
 hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
                           void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
-  const int Mpad = round_up(M, 64);
-  float* y32t = static_cast<float*>(ws);
-  launch_fill_zero(y32t, (size_t)hidden * Mpad, stream);
-  const int n_tiles = (M + DenseCfg::MT - 1) / DenseCfg::MT;
-  const int n_chunks = (inter + DenseCfg::IC - 1) / DenseCfg::IC;
-  const int n_groups = (n_chunks + 7) / 8;
+  const Plan p = make_plan(M, hidden, inter);
+  float* P = static_cast<float*>(ws);
   const float inter_scale = ldexpf(1.0f, -inter_shift);
-  hipLaunchKernelGGL(k_prefill_fused, dim3(n_groups * 8 * n_tiles), dim3(FU_THREADS), 0, stream,
-                     static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
-                     static_cast<const uint8_t*>(wd), hidden, inter, static_cast<const _Float16*>(x), M, y32t, Mpad,
-                     inter_scale, n_tiles, n_chunks);
-  launch_y32t_to_f16(y32t, Mpad, static_cast<_Float16*>(y), hidden, M, ldexpf(1.0f, inter_shift - out_shift), stream);
+  timing_begin(stream);
+  switch (p.cfg) {
+    case 'A': launch_cfg<1, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, stream); break;
+    case 'B': launch_cfg<2, 1, 640>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, stream); break;
+    default: launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, stream); break;
+  }
+  timing_end(stream);
+  hipLaunchKernelGGL(k_reduce_partials, dim3(hidden / 64, p.Mpad / 64), dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, static_cast<_Float16*>(y), M,
+                     ldexpf(1.0f, inter_shift - out_shift));
   return hipGetLastError();
 }
 

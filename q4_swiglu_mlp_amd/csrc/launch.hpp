@@ -9,6 +9,10 @@
 
 namespace zinc {
 
+// Kernel timing hook (timing.cpp): no-ops unless zinc_timing_enable() was called.
+void timing_begin(hipStream_t stream);
+void timing_end(hipStream_t stream);
+
 hipError_t launch_q4k_dequant_f32(const void* blocks, int rows, int cols, float* out, hipStream_t stream);
 
 // Fused prefill.

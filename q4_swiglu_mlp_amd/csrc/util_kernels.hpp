@@ -10,7 +10,4 @@ namespace zinc {
 // so the call stays valid inside a captured HIP graph.
 void launch_fill_zero(float* p, size_t n, hipStream_t stream);
 
-// y[t][n] = fp16(Y32t[n][t] * scale) for t < M, n < H (H % 64 == 0, Mpad % 64 == 0).
-void launch_y32t_to_f16(const float* y32t, int Mpad, _Float16* y, int H, int M, float scale, hipStream_t stream);
-
 }  // namespace zinc

@@ -117,6 +117,19 @@ def test_prefill_m2048_workload_sampled_tokens(layer):
     assert_parity(y[rows], y_ref, f"prefill M=2048 layer {layer}, {len(rows)} sampled tokens")
 
 
+def test_prefill_intermediate_near_fp16_limit():
+    # the shift is one less than the 4x-headroom choice, so the fp16 strip holds
+    # values up to 2^14: sums of 32 such values would overflow fp16, the kernel's
+    # sub-block means must not
+    H, I, M = 512, 768, 96
+    wg, wu, wd, x = _rand_mlp(12, H, I, M)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
+    a, b = shifts_for(y_ref, h_ref)
+    a = max(a - 1, 0)
+    assert np.abs(h_ref).max() * 2.0 ** -a < 65504
+    assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, "prefill strip near fp16 limit")
+
+
 # structured probes (a layout slip inside the fused kernel shows up here even
 # when the mean-dominated random case still passes)
 def test_prefill_zero_input_is_exact_zero():
