@@ -1,227 +1,289 @@
-// Decode (1 <= M <= 8 tokens): the SwiGLU block as two HBM-bound Q4_K matvecs.
+// Decode of one token (M = 1; larger M uses the MFMA kernels of
+// k_decode_mfma.hip): the SwiGLU block as two HBM-bound Q4_K passes.
 //
-//   k_decode_mv<GATEUP=true>  streams W_gate and W_up once: both projections
-//     share one read of x (the same-input gate/up pair fusion of "Four
+//   k_decode_rows<GATEUP=true>  streams W_gate and W_up once: both projections
+//     share one staging of x (the same-input gate/up pair fusion of "Four
 //     bottlenecks, one CUDA backend", "Bottleneck 3"), SwiGLU is applied and the
-//     per-token intermediate is written as fp16(h * 2^-inter_shift) to the
-//     workspace (M x inter; small and consumed at once, as the decode Q&A of
-//     "Fused SwiGLU MLP: ZINC RDNA4 Down-Projection Bandwidth" says).
-//   k_decode_mv<GATEUP=false> streams W_down against that intermediate and
+//     per-token intermediate is written as fp16(h * 2^-inter_shift), row-major
+//     [M x inter], to the workspace (small and consumed at once, as the decode
+//     Q&A of "Fused SwiGLU MLP: ZINC RDNA4 Down-Projection Bandwidth" says).
+//   k_decode_rows<GATEUP=false> streams W_down against that intermediate and
 //     writes y = fp16(acc * 2^(inter_shift - out_shift)).
 //
-// Work split.  A wave owns 16 rows; lane l works on row l/4 and 64-weight
-// chunk c = l%4 of every block it visits (32 quant bytes: sub-blocks 2c in the
-// low nibbles, 2c+1 in the high ones), so the four lanes of a row read the
-// block's 128 quant bytes contiguously.  KSPLIT waves of a block share the same
-// 16 rows and take every KSPLIT-th block (cross-wave sums through LDS), which
-// gives the short-row down projection enough waves to keep HBM busy.  Blocks
-// are fetched UNROLL at a time so several loads per lane are in flight.
-// The activation is staged once per block of threads in LDS as fp16 with the
+// Shape.  Weight rows are independent dot products, so each wave owns whole
+// rows and walks them grid-stride (at any moment the grid reads one contiguous
+// window of the matrix): no tiles, no barriers inside the loop, no cross-wave
+// sums.  The workgroups are persistent (as many as are resident at once) and
+// stage the contraction vector once in LDS, under the latency of their first
+// rows' loads.
+//
+// Lanes.  A row's super-blocks split into 64-weight chunks; lane l takes chunks
+// q = l, l+64, ... of the row, i.e. the block's 16-byte header and its 32 quant
+// bytes (sub-block 2c in the low nibbles, 2c+1 in the high ones, c = q%4), so
+// four consecutive lanes read a block's 128 quant bytes contiguously.
+//
+// Arithmetic per chunk and token: A = sum (1024+q) x over the low nibbles and
+// sum (64+q) x over the high ones, both exact fp16 operands (the nibble OR'ed
+// into an fp16 exponent pattern) fed to v_dot2_f32_f16 with fp32 accumulation;
+// then  w.x = s*A - (off*s + dmin*m) * X  per sub-block, with X the staged
+// fp32 sub-block sum of the activation.  The activation sits in LDS with the
 // middle two elements of every group of four swapped -- the pair order the
-// nibble unpack produces -- plus fp32 sums of every 32-element sub-block, which
-// remove the exact fp16 nibble offsets (1024, 64) and the mins:
-//   sum_k w_k x_k = s*A - (off*s + dmin*m)*X32,  A = sum_k (off + q_k) x_k.
-#include "q4k_device.hpp"
+// nibble unpack produces.
+#include "fused_core.hpp"
 #include "launch.hpp"
+
+#include <algorithm>
 
 namespace zinc {
 
 namespace {
 
-constexpr int DTHREADS = 256;
-constexpr int UNROLL = 4;
-
-// K elements staged per pass: the gate/up matvec stages 4096 (one pass at
-// hidden 4096); the down matvec stages as much of the intermediate as about
-// 88 KB of LDS holds.
-constexpr int KC_GATEUP = 4096;
-template <int MM>
-struct DownKC {
-  static constexpr int value = (MM <= 2) ? 16384 : (MM <= 4) ? 11264 : 5632;
+// waves per workgroup
+template <bool GATEUP>
+struct DrShape {
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;
 };
+constexpr int DR_KMAX = 16384;               // longest contraction (the library's hidden limit)
+constexpr int DR_KQ_MAX = DR_KMAX / 64 / 64; // chunk slots per lane (4)
 
-struct BlockData {
-  uint4 hdr, q0, q1;
-};
-
-__device__ __forceinline__ BlockData load_block(const uint8_t* bp, int c) {
-  BlockData d;
-  d.hdr = *reinterpret_cast<const uint4*>(bp);
-  d.q0 = *reinterpret_cast<const uint4*>(bp + 16 + 32 * c);
-  d.q1 = *reinterpret_cast<const uint4*>(bp + 32 + 32 * c);
-  return d;
+// Cross-lane sums on the VALU (DPP).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
 }
 
-// Accumulate one block's contribution (this lane's chunk c) into acc[t].
+// Sum over the 64 lanes; the total lands in lane 63.
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp_f<0xB1>(v);          // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);          // quad_perm [2,3,0,1]
+  v += dpp_f<0x114>(v);         // row_shr:4
+  v += dpp_f<0x118>(v);         // row_shr:8
+  v += dpp_f<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xC>(v);    // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+struct Chunk {
+  uint4 hdr, q0, q1;   // block header; quant bytes [32c, 32c+16) and [32c+16, 32c+32)
+};
+
+// One chunk's contribution for MM tokens.  xs: staged activation (pair order)
+// of token 0 at this chunk's 64 weights, token stride TS halves; X: the fp32
+// sums of sub-blocks 2c and 2c+1 per token.
 template <int MM>
-__device__ __forceinline__ void block_dot(const BlockData& bd, int c, const _Float16* __restrict__ xs,
-                                          const float* __restrict__ x32, int KC, int kl, float* acc) {
-  float Alo[MM], Ahi[MM];
+__device__ __forceinline__ void chunk_dot(const Chunk& ch, int c, const _Float16* xs, int TS, const float* X2,
+                                          int X2S, const NibbleK& nk, float* acc) {
+  float alo[MM], ahi[MM];
 #pragma unroll
-  for (int t = 0; t < MM; ++t) Alo[t] = Ahi[t] = 0.0f;
+  for (int t = 0; t < MM; ++t) alo[t] = ahi[t] = 0.0f;
 #pragma unroll
-  for (int dwi = 0; dwi < 8; ++dwi) {
-    const uint4& qq = (dwi < 4) ? bd.q0 : bd.q1;
-    const int k4 = dwi & 3;
-    const uint32_t Q = (k4 == 0) ? qq.x : (k4 == 1) ? qq.y : (k4 == 2) ? qq.z : qq.w;
-    const half2v a0 = bits_h2((Q & 0x000F000Fu) | 0x64006400u);
-    const half2v a1 = bits_h2(((Q >> 8) & 0x000F000Fu) | 0x64006400u);
-    const half2v a2 = bits_h2((Q & 0x00F000F0u) | 0x54005400u);
-    const half2v a3 = bits_h2(((Q >> 8) & 0x00F000F0u) | 0x54005400u);
+  for (int h = 0; h < 2; ++h) {
+    const uint4 qq = h ? ch.q1 : ch.q0;
 #pragma unroll
-    for (int t = 0; t < MM; ++t) {
-      const uint2 xl = *reinterpret_cast<const uint2*>(xs + t * KC + kl + 4 * dwi);
-      const uint2 xh = *reinterpret_cast<const uint2*>(xs + t * KC + kl + 32 + 4 * dwi);
-      Alo[t] = __builtin_amdgcn_fdot2(a0, bits_h2(xl.x), Alo[t], false);
-      Alo[t] = __builtin_amdgcn_fdot2(a1, bits_h2(xl.y), Alo[t], false);
-      Ahi[t] = __builtin_amdgcn_fdot2(a2, bits_h2(xh.x), Ahi[t], false);
-      Ahi[t] = __builtin_amdgcn_fdot2(a3, bits_h2(xh.y), Ahi[t], false);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t Q = (k == 0) ? qq.x : (k == 1) ? qq.y : (k == 2) ? qq.z : qq.w;
+      const uint32_t Q8 = Q >> 8;
+      const half2v a0 = bits_h2((Q & nk.lo_mask) | nk.lo_magic);    // 1024 + q, bytes 0, 2 (low nibbles)
+      const half2v a1 = bits_h2((Q8 & nk.lo_mask) | nk.lo_magic);   // bytes 1, 3
+      const half2v a2 = bits_h2((Q & nk.hi_mask) | nk.hi_magic);    // 64 + q (high nibbles)
+      const half2v a3 = bits_h2((Q8 & nk.hi_mask) | nk.hi_magic);
+      const int e = 16 * h + 4 * k;   // first weight of this dword within the chunk's low half
+#pragma unroll
+      for (int t = 0; t < MM; ++t) {
+        const uint2 xl = *reinterpret_cast<const uint2*>(xs + t * TS + e);        // x[e], x[e+2], x[e+1], x[e+3]
+        const uint2 xh = *reinterpret_cast<const uint2*>(xs + t * TS + 32 + e);
+        alo[t] = __builtin_amdgcn_fdot2(a0, bits_h2(xl.x), alo[t], false);
+        alo[t] = __builtin_amdgcn_fdot2(a1, bits_h2(xl.y), alo[t], false);
+        ahi[t] = __builtin_amdgcn_fdot2(a2, bits_h2(xh.x), ahi[t], false);
+        ahi[t] = __builtin_amdgcn_fdot2(a3, bits_h2(xh.y), ahi[t], false);
+      }
     }
   }
-  const float d = half_bits_to_float(bd.hdr.x & 0xFFFFu), dmin = half_bits_to_float(bd.hdr.x >> 16);
-  const SixBit sb = unpack_sixbit(bd.hdr.y, bd.hdr.z, bd.hdr.w);
+  const float d = half_bits_to_float(ch.hdr.x & 0xFFFFu), dmin = half_bits_to_float(ch.hdr.x >> 16);
+  const SixBit sb = unpack_sixbit(ch.hdr.y, ch.hdr.z, ch.hdr.w);
   const float slo = d * (float)sixbit_sc(sb, 2 * c), shi = d * (float)sixbit_sc(sb, 2 * c + 1);
   const float clo = 1024.0f * slo + dmin * (float)sixbit_m(sb, 2 * c);
   const float chi = 64.0f * shi + dmin * (float)sixbit_m(sb, 2 * c + 1);
-  const int xi = kl >> 5;
 #pragma unroll
   for (int t = 0; t < MM; ++t)
-    acc[t] += slo * Alo[t] - clo * x32[t * (KC / 32) + xi] + shi * Ahi[t] - chi * x32[t * (KC / 32) + xi + 1];
+    acc[t] += slo * alo[t] - clo * X2[t * X2S] + shi * ahi[t] - chi * X2[t * X2S + 1];
 }
 
-template <int MM, bool GATEUP, int KSPLIT, int KCMAX>
-__global__ __launch_bounds__(DTHREADS) void k_decode_mv(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
-                                                        int K, int N, const _Float16* __restrict__ xin, int M,
-                                                        _Float16* __restrict__ out, float scale) {
-  constexpr int RG = 4 / KSPLIT;                 // 16-row groups per block of threads
-  __shared__ __attribute__((aligned(16))) _Float16 xs[MM * KCMAX];
-  __shared__ float x32[MM * (KCMAX / 32)];
-  __shared__ float red[(KSPLIT > 1) ? (4 * 64 * MM * (GATEUP ? 2 : 1)) : 1];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int rg = wave / KSPLIT, kph = wave % KSPLIT;
-  const int r = lane >> 2, c = lane & 3;
-  const int row = (blockIdx.x * RG + rg) * 16 + r;   // N % 256 == 0
+template <int MM, bool GATEUP, int KQ>
+__global__ __launch_bounds__(DrShape<GATEUP>::THREADS) void k_decode_rows(const uint8_t* __restrict__ W0,
+                                                            const uint8_t* __restrict__ W1, int K, int N,
+                                                            const _Float16* __restrict__ xin, int M,
+                                                            _Float16* __restrict__ out, float scale) {
+  constexpr int NMAT = GATEUP ? 2 : 1;
+  constexpr int DR_WAVES = DrShape<GATEUP>::WAVES, DR_THREADS = DrShape<GATEUP>::THREADS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char dr_smem[];
   const int nb = K / QK;
-  const int KC = min(K, KCMAX);
+  const int Q = 4 * nb;                   // chunks per row
+  const int TS = K + 8;                   // staged token stride (halves)
+  _Float16* xs = reinterpret_cast<_Float16*>(dr_smem);
+  float* X2 = reinterpret_cast<float*>(dr_smem + (size_t)MM * TS * 2);   // [MM][2*Q] sub-block sums
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const NibbleK nk = nibble_consts();
 
-  float acc0[MM], acc1[MM];
+  const size_t row_bytes = (size_t)nb * BLOCK_BYTES;
+  const int nwaves = gridDim.x * DR_WAVES;
+  const int w0 = blockIdx.x * DR_WAVES + wave;
+  // this lane's chunks: q = lane + 64k; byte offsets within a row
+  int cq[KQ];
+  size_t boff[KQ], qoff[KQ];
+  bool has[KQ];
 #pragma unroll
-  for (int t = 0; t < MM; ++t) acc0[t] = acc1[t] = 0.0f;
-  const uint8_t* r0 = W0 + (size_t)row * nb * BLOCK_BYTES;
-  const uint8_t* r1 = GATEUP ? W1 + (size_t)row * nb * BLOCK_BYTES : nullptr;
-
-  for (int k0 = 0; k0 < K; k0 += KC) {
-    const int kc = min(KC, K - k0);              // multiple of 256
-    if (k0 > 0) __syncthreads();
-    // stage x[0..M) x [k0, k0+kc): 8 elements per piece; 4 pieces form a 32-sum
-    const int per_row = kc / 8;
-    for (int ci = tid; ci < MM * per_row; ci += DTHREADS) {
-      const int t = ci / per_row, a = ci % per_row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < M) v = *reinterpret_cast<const uint4*>(xin + (size_t)t * K + k0 + 8 * a);
-      const uint32_t lo0 = (v.x & 0xFFFFu) | (v.y << 16);
-      const uint32_t lo1 = (v.x >> 16) | (v.y & 0xFFFF0000u);
-      const uint32_t hi0 = (v.z & 0xFFFFu) | (v.w << 16);
-      const uint32_t hi1 = (v.z >> 16) | (v.w & 0xFFFF0000u);
-      *reinterpret_cast<uint4*>(xs + t * KC + 8 * a) = make_uint4(lo0, lo1, hi0, hi1);
-      const half8 hv = __builtin_bit_cast(half8, v);
-      float s8 = 0.0f;
+  for (int k = 0; k < KQ; ++k) {
+    const int q = lane + 64 * k;
+    has[k] = q < Q;
+    const int qc = has[k] ? q : 0;
+    cq[k] = qc & 3;
+    boff[k] = (size_t)(qc >> 2) * BLOCK_BYTES;
+    qoff[k] = boff[k] + 16 + 32 * (qc & 3);
+  }
+  using Buf = Chunk[NMAT][KQ];
+  auto load_row = [&](int j, Buf& buf) __attribute__((always_inline)) {
+    const int jj = j < N ? j : 0;   // past the last row: re-read row 0 (never used)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s8 += (float)hv[e];
-      // per_row is a multiple of 32, so a group of 4 pieces never straddles
-      // rows or the active-lane boundary of the last iteration
-      s8 += __shfl_xor(s8, 1, 64);
-      s8 += __shfl_xor(s8, 2, 64);
-      if ((a & 3) == 0) x32[t * (KC / 32) + (a >> 2)] = s8;
-    }
-    __syncthreads();
-
-    const int b_begin = k0 / QK, b_end = (k0 + kc) / QK;
-    for (int b = b_begin + kph; b < b_end; b += UNROLL * KSPLIT) {
-      BlockData d0[UNROLL], d1[UNROLL];
+    for (int m = 0; m < NMAT; ++m) {
+      const uint8_t* row = (m ? W1 : W0) + (size_t)jj * row_bytes;
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int bb = b + u * KSPLIT;
-        if (bb < b_end) {
-          d0[u] = load_block(r0 + (size_t)bb * BLOCK_BYTES, c);
-          if (GATEUP) d1[u] = load_block(r1 + (size_t)bb * BLOCK_BYTES, c);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int bb = b + u * KSPLIT;
-        if (bb < b_end) {
-          const int kl = (bb - b_begin) * QK + 64 * c;
-          block_dot<MM>(d0[u], c, xs, x32, KC, kl, acc0);
-          if (GATEUP) block_dot<MM>(d1[u], c, xs, x32, KC, kl, acc1);
-        }
+      for (int k = 0; k < KQ; ++k) {
+        buf[m][k].hdr = *reinterpret_cast<const uint4*>(row + boff[k]);
+        buf[m][k].q0 = *reinterpret_cast<const uint4*>(row + qoff[k]);
+        buf[m][k].q1 = *reinterpret_cast<const uint4*>(row + qoff[k] + 16);
       }
     }
-  }
-
-  // reduce over the 4 lanes of a row, then over the KSPLIT waves
+  };
+  auto compute_row = [&](int j, const Buf& buf) __attribute__((always_inline)) {
+    float acc[NMAT][MM];
 #pragma unroll
-  for (int t = 0; t < MM; ++t) {
-    acc0[t] += __shfl_xor(acc0[t], 1, 64);
-    acc0[t] += __shfl_xor(acc0[t], 2, 64);
-    if (GATEUP) {
-      acc1[t] += __shfl_xor(acc1[t], 1, 64);
-      acc1[t] += __shfl_xor(acc1[t], 2, 64);
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int t = 0; t < MM; ++t) acc[m][t] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KQ; ++k) {
+      if (!has[k]) continue;
+      const int q = lane + 64 * k;
+      const _Float16* xq = xs + 64 * q;        // chunk q covers weights [64q, 64q+64)
+      const float* xq2 = X2 + 2 * q;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) chunk_dot<MM>(buf[m][k], cq[k], xq, TS, xq2, 2 * Q, nk, acc[m]);
     }
-  }
-  if (KSPLIT > 1) {
-    if (c == 0) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int t = 0; t < MM; ++t) acc[m][t] = wave_sum_to_lane63(acc[m][t]);
+    if (lane == 63) {
 #pragma unroll
       for (int t = 0; t < MM; ++t) {
-        red[((wave * 16 + r) * MM + t) * (GATEUP ? 2 : 1)] = acc0[t];
-        if (GATEUP) red[((wave * 16 + r) * MM + t) * 2 + 1] = acc1[t];
-      }
-    }
-    __syncthreads();
-    if (kph != 0) return;
-    if (c == 0) {
-#pragma unroll
-      for (int t = 0; t < MM; ++t) {
-        float s0 = 0.0f, s1 = 0.0f;
-        for (int w = 0; w < KSPLIT; ++w) {
-          s0 += red[(((rg * KSPLIT + w) * 16 + r) * MM + t) * (GATEUP ? 2 : 1)];
-          if (GATEUP) s1 += red[(((rg * KSPLIT + w) * 16 + r) * MM + t) * 2 + 1];
+        if (t < M) {
+          const float v = GATEUP ? silu_f32(acc[0][t]) * acc[NMAT - 1][t] * scale : acc[0][t] * scale;
+          out[(size_t)t * N + j] = (_Float16)v;
         }
-        acc0[t] = s0;
-        acc1[t] = s1;
       }
     }
-  }
-  if (c == 0) {
+  };
+
+  // Order of the memory traffic (loads complete in issue order): the
+  // activation pieces first, then the first two rows' weights, then the
+  // staging arithmetic, which waits for the activation only.
+  constexpr int NXG = (MM * (DR_KMAX / 8) + DR_THREADS - 1) / DR_THREADS;   // 16-byte groups per thread (bound)
+  const int ngroups = MM * (K / 8);
+  uint4 xv[NXG];
 #pragma unroll
-    for (int t = 0; t < MM; ++t) {
-      if (t < M) {
-        const float v = GATEUP ? silu_f32(acc0[t]) * acc1[t] * scale : acc0[t] * scale;
-        out[(size_t)t * N + row] = (_Float16)v;
-      }
-    }
+  for (int u = 0; u < NXG; ++u) {
+    const int g = tid + u * DR_THREADS;
+    const int t = g / (K / 8), a = g % (K / 8);
+    xv[u] = make_uint4(0, 0, 0, 0);
+    if (g < ngroups && t < M) xv[u] = *reinterpret_cast<const uint4*>(xin + (size_t)t * K + 8 * a);
+  }
+  // One row in flight per wave: with every wave of the grid streaming, more
+  // rows in flight only lengthened the queues (measured slower), so a wave
+  // loads row j, computes it, and moves on.
+  Buf buf;
+  int j = w0;
+  load_row(j, buf);
+  // stage x: groups of four with the middle two swapped; fp32 sums of every 32
+  // elements (four consecutive groups = four consecutive lanes of a quad)
+#pragma unroll
+  for (int u = 0; u < NXG; ++u) {
+    const int g = tid + u * DR_THREADS;
+    const int t = g / (K / 8), a = g % (K / 8);
+    const uint4 v = xv[u];
+    if (g < ngroups)
+      *reinterpret_cast<uint4*>(xs + t * TS + 8 * a) =
+          make_uint4((v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
+                     (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u));
+    const half8 hv = __builtin_bit_cast(half8, v);
+    float s8 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8 += (float)hv[e];
+    s8 += dpp_f<0xB1>(s8);
+    s8 += dpp_f<0x4E>(s8);
+    if (g < ngroups && (a & 3) == 0) X2[t * 2 * Q + (a >> 2)] = s8;
+  }
+  __syncthreads();
+
+  for (; j < N; j += nwaves) {
+    if (j != w0) load_row(j, buf);
+    compute_row(j, buf);
   }
 }
 
-template <int MM>
-hipError_t launch_decode_mm(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
-                            void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
-  _Float16* hbuf = static_cast<_Float16*>(ws);
-  // gate/up: pairs of waves share 16 rows (32 rows per block of threads)
-  timing_begin(stream);
-  hipLaunchKernelGGL((k_decode_mv<MM, true, 2, KC_GATEUP>), dim3(inter / 32), dim3(DTHREADS), 0, stream,
-                     static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu), hidden, inter,
-                     static_cast<const _Float16*>(x), M, hbuf, ldexpf(1.0f, -inter_shift));
-  timing_end(stream);
-  // down: 4 waves share 16 rows, each taking every 4th block
-  timing_begin(stream);
-  hipLaunchKernelGGL((k_decode_mv<MM, false, 4, DownKC<MM>::value>), dim3(hidden / 16), dim3(DTHREADS), 0, stream,
-                     static_cast<const uint8_t*>(wd), static_cast<const uint8_t*>(nullptr), inter, hidden, hbuf, M,
-                     static_cast<_Float16*>(y), ldexpf(1.0f, inter_shift - out_shift));
-  timing_end(stream);
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int& c = cache[dev & 63];
+  if (c == 0) {
+    int n = 0;
+    c = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return c;
+}
+
+// Persistent grid: as many workgroups as are resident at once (occupancy of
+// this instantiation at this LDS size), so no workgroup waits for another to end.
+template <int MM, bool GATEUP, int KQ>
+hipError_t launch_rows(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
+                       float scale, hipStream_t stream) {
+  const size_t smem = (size_t)MM * (K + 8) * 2 + (size_t)MM * 2 * (4 * (K / QK)) * 4;
+  static size_t attr_set = 0;   // largest dynamic LDS size allowed so far
+  if (smem > attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_rows<MM, GATEUP, KQ>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = smem;
+  }
+  static size_t occ_smem = 0;
+  static int occ = 0;
+  if (occ == 0 || occ_smem != smem) {
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_rows<MM, GATEUP, KQ>,
+                                                                DrShape<GATEUP>::THREADS, smem);
+    if (e != hipSuccess) return e;
+    occ = per_cu < 1 ? 1 : per_cu;
+    occ_smem = smem;
+  }
+  const int per_cu = occ;
+  constexpr int WAVES = DrShape<GATEUP>::WAVES;
+  const int grid = std::max(1, std::min(cu_count() * per_cu, (N + WAVES - 1) / WAVES));
+  hipLaunchKernelGGL((k_decode_rows<MM, GATEUP, KQ>), dim3(grid), dim3(DrShape<GATEUP>::THREADS), smem, stream,
+                     static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), K, N, x, M, out, scale);
   return hipGetLastError();
+}
+
+template <int MM, bool GATEUP>
+hipError_t launch_rows_k(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
+                         float scale, hipStream_t stream) {
+  const int Q = 4 * (K / QK);
+  if (Q <= 64) return launch_rows<MM, GATEUP, 1>(W0, W1, K, N, x, M, out, scale, stream);
+  if (Q <= 128) return launch_rows<MM, GATEUP, 2>(W0, W1, K, N, x, M, out, scale, stream);
+  if (Q <= 192) return launch_rows<MM, GATEUP, 3>(W0, W1, K, N, x, M, out, scale, stream);
+  return launch_rows<MM, GATEUP, 4>(W0, W1, K, N, x, M, out, scale, stream);
 }
 
 }  // namespace
@@ -233,10 +295,18 @@ size_t decode_workspace_bytes(int M, int hidden, int inter) {
 
 hipError_t launch_decode(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x, void* y,
                          int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
-  if (M <= 1) return launch_decode_mm<1>(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream);
-  if (M <= 2) return launch_decode_mm<2>(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream);
-  if (M <= 4) return launch_decode_mm<4>(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream);
-  return launch_decode_mm<8>(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream);
+  if (M >= 2) return launch_decode_mfma(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream);
+  const float gu_scale = ldexpf(1.0f, -inter_shift), dn_scale = ldexpf(1.0f, inter_shift - out_shift);
+  _Float16* hbuf = static_cast<_Float16*>(ws);
+  timing_begin(stream);
+  hipError_t e = launch_rows_k<1, true>(wg, wu, hidden, inter, static_cast<const _Float16*>(x), M, hbuf, gu_scale,
+                                        stream);
+  timing_end(stream);
+  if (e != hipSuccess) return e;
+  timing_begin(stream);
+  e = launch_rows_k<1, false>(wd, nullptr, inter, hidden, hbuf, M, static_cast<_Float16*>(y), dn_scale, stream);
+  timing_end(stream);
+  return e;
 }
 
 }  // namespace zinc

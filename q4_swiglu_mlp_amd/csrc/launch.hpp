@@ -21,11 +21,16 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
                           const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
                           hipStream_t stream);
 
-// Decode matvec pair, 1 <= M <= 8.
+// Decode, 1 <= M <= 8: row-streaming dot products for M = 1 (k_decode.hip),
+// 16x16x32 MFMA tiles for M >= 2 (k_decode_mfma.hip); both write the fp16
+// intermediate [M x inter] into the workspace between their two kernels.
 size_t decode_workspace_bytes(int M, int hidden, int inter);
 hipError_t launch_decode(const void* wg, const void* wu, const void* wd, int hidden, int inter,
                          const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
                          hipStream_t stream);
+hipError_t launch_decode_mfma(const void* wg, const void* wu, const void* wd, int hidden, int inter,
+                              const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
+                              hipStream_t stream);
 
 // Batched-expert MoE.
 size_t moe_workspace_bytes(int M, int top_k, int n_experts, int hidden, int inter);

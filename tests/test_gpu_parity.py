@@ -203,6 +203,25 @@ def test_decode_workloads(name, layer):
     assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift), y_ref, f"{name} layer {layer}")
 
 
+@pytest.mark.parametrize("M", [1, 4])
+def test_decode_repeated_calls_reuse_workspace(M):
+    # back-to-back calls on one workspace (filled with garbage first) give the
+    # same result bit for bit: every row is summed in a fixed order
+    w = S.WORKLOADS["decode_m4"]
+    wts = S.layer_weights(w.seed, 3, w.hidden, w.inter)
+    wg, wu, wd = (dev(a) for a in wts)
+    x = S.workload_x(w)[:M]
+    y_ref, _ = O.mlp(x, *wts, w.hidden, w.inter)
+    ws = torch.full((Z.decode_workspace_size(M, w.hidden, w.inter),), 0x5A, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        y = Z.zinc_mlp_q4k_decode(wg, wu, wd, w.hidden, w.inter, dev(x), w.inter_shift, w.out_shift, workspace=ws)
+        outs.append(unscale(y, w.out_shift))
+    for y in outs:
+        assert_parity(y, y_ref, f"decode M={M} repeated")
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
 def test_decode_and_prefill_agree_at_m8():
     w = S.WORKLOADS["tiny"]
     wg, wu, wd = S.layer_weights(w.seed, 0, w.hidden, w.inter)
