@@ -180,20 +180,25 @@ struct XPieces {
   static constexpr int PIECES = MT * (QK / 8);                   // 16-byte pieces per column
   static constexpr int N = (PIECES + THREADS - 1) / THREADS;     // per thread (the last may be idle)
   uint4 v[N];
+  bool live[N];   // false: padding row or past the tile, staged as zeros
 };
 
 template <int MT>
 __device__ __forceinline__ XPieces<MT> fu_load_x(const _Float16* __restrict__ x, int H,
                                                  const int* __restrict__ tok, int k0) {
+  // No branches around the loads (so the compiler's wait counts stay exact):
+  // pieces past the tile or of padding rows read token 0's piece, and are
+  // zeroed when staged.
   XPieces<MT> r;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int it = 0; it < XPieces<MT>::N; ++it) {
     const int ci = threadIdx.x + XPieces<MT>::THREADS * it;
-    r.v[it] = make_uint4(0, 0, 0, 0);
-    if (ci < XPieces<MT>::PIECES) {
-      const int token = tok[ci >> 5];
-      if (token >= 0) r.v[it] = *reinterpret_cast<const uint4*>(x + (size_t)token * H + k0 + 8 * (ci & 31));
-    }
+    // PIECES is a multiple of 64, so whole waves are in or out: a uniform test
+    const bool wave_in = wv * 64 + XPieces<MT>::THREADS * it < XPieces<MT>::PIECES;
+    const int token = wave_in ? tok[min(ci, XPieces<MT>::PIECES - 1) >> 5] : -1;
+    r.live[it] = token >= 0;
+    r.v[it] = *reinterpret_cast<const uint4*>(x + (size_t)(token >= 0 ? token : 0) * H + k0 + 8 * (ci & 31));
   }
   return r;
 }
@@ -202,15 +207,15 @@ __device__ __forceinline__ XPieces<MT> fu_load_x(const _Float16* __restrict__ x,
 template <int MT, int XS>
 __device__ __forceinline__ void fu_store_x(const XPieces<MT>& xp, _Float16* __restrict__ xs,
                                            _Float16* __restrict__ xsum) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int it = 0; it < XPieces<MT>::N; ++it) {
     const int ci = threadIdx.x + XPieces<MT>::THREADS * it;
-    // THREADS and PIECES are multiples of 4, so the four lanes of a 32-mean
-    // below are all in range or all out of it
-    if (ci >= XPieces<MT>::PIECES) continue;
+    // PIECES is a multiple of 64: whole waves are in range or out of it
+    if (wv * 64 + XPieces<MT>::THREADS * it >= XPieces<MT>::PIECES) continue;
     const int t = ci >> 5;          // row within the unit
     const int a = ci & 31;          // 8-element group within the super-block column
-    const uint4 v = xp.v[it];
+    const uint4 v = xp.live[it] ? xp.v[it] : make_uint4(0, 0, 0, 0);
     const int c = a >> 3;           // 64-wide panel
     const int kl = (8 * a) & 63;    // position within the panel (multiple of 8)
     // elements e0..e3 -> slots (e0, e2, e1, e3); same for e4..e7
@@ -305,7 +310,7 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
   constexpr int HS = C::HS, HSS = C::HSS;
   constexpr int NB = C::NBMAX;
   constexpr int NP = ICMAX / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int npan = (r1 - r0) / 64;
   const int b0 = r0 >> 8;
@@ -321,7 +326,7 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
   }
   const uint8_t* blk_base = wd + (size_t)l32 * row_bytes + (size_t)b0 * BLOCK_BYTES;   // row l32 of tile 0
 
-  auto down_tile = [&](DownTileData<NP, NB>& dt, int nt, bool more, const uint8_t* nxt) {
+  auto down_tile = [&](DownTileData<NP, NB>& dt, int nt, const uint8_t* nxt) {
     const uint8_t* nq = nxt + 16 + 16 * h;
     float16v acc[TT];
 #pragma unroll
@@ -335,17 +340,17 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
     for (int p = 0; p < NP; ++p) {
       if (p < npan) {
         const ChunkS cs = chunk_s(sp[(p + OFF) >> 2], (p + OFF) & 3);
-        const uint4 q = dt.qs[p];
-        if (more) dt.qs[p] = *reinterpret_cast<const uint4*>(nq + ((p + OFF) >> 2) * BLOCK_BYTES + 32 * ((p + OFF) & 3));
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const half8 a = dequant_dword_scaled(dword_of(q, s), cs.s_lo, cs.c_lo, cs.s_hi, cs.c_hi, nk);
+          const half8 a = dequant_dword_scaled(dword_of(dt.qs[p], s), cs.s_lo, cs.c_lo, cs.s_hi, cs.c_hi, nk);
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) {
             const half8 bf = *reinterpret_cast<const half8*>(sm.hs + (tt * 32 + l32) * HS + p * 64 + (2 * s + h) * 8);
             acc[tt] = mfma32(a, bf, acc[tt]);
           }
         }
+        // panel used up: refill it with the next tile's bytes
+        dt.qs[p] = *reinterpret_cast<const uint4*>(nq + ((p + OFF) >> 2) * BLOCK_BYTES + 32 * ((p + OFF) & 3));
       }
     }
     // min correction: lane half h covers block k = 2g + h (block-aligned strip means)
@@ -368,11 +373,9 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
         }
       }
     }
-    if (more) {
 #pragma unroll
-      for (int k = 0; k < NB; ++k)
-        if (k < nblk) dt.hdr[k] = *reinterpret_cast<const uint4*>(nxt + k * BLOCK_BYTES);
-    }
+    for (int k = 0; k < NB; ++k)
+      if (k < nblk) dt.hdr[k] = *reinterpret_cast<const uint4*>(nxt + k * BLOCK_BYTES);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
@@ -389,9 +392,10 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
   if (wave >= NT) return;   // wave-uniform: fewer output tiles than waves
   DownTileData<NP, NB> d = load_down_tile<NP, NB, OFF>(blk_base + (size_t)wave * tile_step, nblk, npan, h);
   for (int nt = wave; nt < NT; nt += C::WAVES) {
-    const bool more = nt + C::WAVES < NT;
-    const uint8_t* nb_ptr = blk_base + (size_t)(nt + C::WAVES) * tile_step;
-    down_tile(d, nt, more, nb_ptr);
+    // refills read the next tile of this wave; after the last one, this tile
+    // again (in bounds, never used)
+    const int nn = (nt + C::WAVES < NT) ? nt + C::WAVES : nt;
+    down_tile(d, nt, blk_base + (size_t)nn * tile_step);
   }
 }
 
@@ -407,7 +411,7 @@ __device__ __forceinline__ void fused_unit(const uint8_t* __restrict__ wg, const
                                            float inter_scale, const Out& out, FusedSmem<TT, RTW, ICMAX>& sm) {
   using C = FusedCfg<TT, RTW, ICMAX>;
   constexpr int MT = C::MT, XS = C::XS, HS = C::HS, HSS = C::HSS;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int nbH = H / QK;
   const NibbleK nk = nibble_consts();
@@ -442,8 +446,12 @@ __device__ __forceinline__ void fused_unit(const uint8_t* __restrict__ wg, const
 #pragma unroll
       for (int e = 0; e < 8; ++e) xsum_even[tt][e] = (_Float16)0.0f;
 
+    // byte offset of (row tile i of this pass, block column kb) for this lane;
+    // a wave without that row tile gets the chunk's last row tile (an
+    // in-bounds address: its loads are never used)
     auto row_blk = [&](int i, int kb) -> const uint8_t* {
-      return (const uint8_t*)0 + ((size_t)(r0 + (wave + C::WAVES * (first + i)) * 32 + l32) * nbH + kb) * BLOCK_BYTES;
+      const int rt = min(wave + C::WAVES * (first + i), nrt - 1);
+      return (const uint8_t*)0 + ((size_t)(r0 + rt * 32 + l32) * nbH + kb) * BLOCK_BYTES;
     };
 
     // One super-block column.  D holds this column's weight bytes (loaded one
@@ -455,42 +463,43 @@ __device__ __forceinline__ void fused_unit(const uint8_t* __restrict__ wg, const
       const int buf = kb & 1;
       const bool odd = (kb & 1) != 0;
       const bool pair_end = odd || (kb == nbH - 1);
-      const bool more = kb + 1 < nbH;
-      __syncthreads();   // x[buf] is staged; everyone is done with x[buf ^ 1]
-      XPieces<MT> xp;
-      if (more) xp = fu_load_x<MT>(x, H, tok, (kb + 1) * QK);
+      // refills read block column kn; on the last step that is the current
+      // column again (never used): the loads stay unconditional
+      const int kn = (kb + 1 < nbH) ? kb + 1 : kb;
+      lds_barrier();   // x[buf] is staged; everyone is done with x[buf ^ 1]
+      const XPieces<MT> xp = fu_load_x<MT>(x, H, tok, kn * QK);
       if (!odd) {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
           xsum_even[tt] = *reinterpret_cast<const half8*>(sm.xsum[buf] + (tt * 32 + l32) * 8);
       }
+      // The refill loads are issued by every wave (a wave without a row tile
+      // re-reads an in-bounds one), so no branch ever surrounds a load and the
+      // compiler's wait counts stay exact; only the arithmetic is skipped.
 #pragma unroll
       for (int i = 0; i < RTW; ++i) {
-        if (i >= nv) continue;   // wave-uniform
-        const size_t nb_off = (size_t)(row_blk(i, kb + 1) - (const uint8_t*)0);
-        const Pairs8 spg = block_scale_pairs(D[i].hg);
-        const Pairs8 spu = block_scale_pairs(D[i].hu);
-        if ((kb & 1) == h) {
-          dmg[i] = block_neg_dm32(D[i].hg);
-          dmu[i] = block_neg_dm32(D[i].hu);
+        const bool act = i < nv;   // wave-uniform
+        const size_t nb_off = (size_t)(row_blk(i, kn) - (const uint8_t*)0);
+        Pairs8 spg, spu;
+        if (act) {
+          spg = block_scale_pairs(D[i].hg);
+          spu = block_scale_pairs(D[i].hu);
+          if ((kb & 1) == h) {
+            dmg[i] = block_neg_dm32(D[i].hg);
+            dmu[i] = block_neg_dm32(D[i].hu);
+          }
         }
-        if (more) {
-          D[i].hg = *reinterpret_cast<const uint4*>(wg + nb_off);
-          D[i].hu = *reinterpret_cast<const uint4*>(wu + nb_off);
-        }
+        D[i].hg = *reinterpret_cast<const uint4*>(wg + nb_off);
+        D[i].hu = *reinterpret_cast<const uint4*>(wu + nb_off);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const ChunkS sg = chunk_s(spg, c);
           const ChunkS su = chunk_s(spu, c);
-          const uint4 qg = D[i].qg[c], qu = D[i].qu[c];
-          if (more) {
-            D[i].qg[c] = *reinterpret_cast<const uint4*>(wg + nb_off + 16 + 32 * c + 16 * h);
-            D[i].qu[c] = *reinterpret_cast<const uint4*>(wu + nb_off + 16 + 32 * c + 16 * h);
-          }
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const half8 ag = dequant_dword_scaled(dword_of(qg, s), sg.s_lo, sg.c_lo, sg.s_hi, sg.c_hi, nk);
-            const half8 au = dequant_dword_scaled(dword_of(qu, s), su.s_lo, su.c_lo, su.s_hi, su.c_hi, nk);
+            if (!act) break;
+            const half8 ag = dequant_dword_scaled(dword_of(D[i].qg[c], s), sg.s_lo, sg.c_lo, sg.s_hi, sg.c_hi, nk);
+            const half8 au = dequant_dword_scaled(dword_of(D[i].qu[c], s), su.s_lo, su.c_lo, su.s_hi, su.c_hi, nk);
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
               const half8 b =
@@ -499,8 +508,11 @@ __device__ __forceinline__ void fused_unit(const uint8_t* __restrict__ wg, const
               accu[i][tt] = mfma32(au, b, accu[i][tt]);
             }
           }
+          // this chunk's bytes are used up: refill them in place
+          D[i].qg[c] = *reinterpret_cast<const uint4*>(wg + nb_off + 16 + 32 * c + 16 * h);
+          D[i].qu[c] = *reinterpret_cast<const uint4*>(wu + nb_off + 16 + 32 * c + 16 * h);
         }
-        if (pair_end) {
+        if (act && pair_end) {
           // min correction for the block pair (kb-1, kb), or the lone last block:
           // lane half 0 holds the even block's -32*dmin*m and means, half 1 the odd one's
 #pragma unroll
@@ -517,18 +529,19 @@ __device__ __forceinline__ void fused_unit(const uint8_t* __restrict__ wg, const
           for (int e = 0; e < 8; ++e) dmg[i][e] = dmu[i][e] = (_Float16)0.0f;
         }
       }
-      if (more) fu_store_x<MT, XS>(xp, sm.xs[buf ^ 1], sm.xsum[buf ^ 1]);
+      // next column's x into the other buffer (on the last step a harmless
+      // rewrite of it: nobody reads that buffer again in this pass)
+      fu_store_x<MT, XS>(xp, sm.xs[buf ^ 1], sm.xsum[buf ^ 1]);
     };
 
     // prologue: x of block column 0 and this wave's weights for it
-    __syncthreads();   // the previous pass is done with both x buffers
+    lds_barrier();   // the previous pass is done with both x buffers
     {
       const XPieces<MT> xp0 = fu_load_x<MT>(x, H, tok, 0);
       fu_store_x<MT, XS>(xp0, sm.xs[0], sm.xsum[0]);
     }
 #pragma unroll
-    for (int i = 0; i < RTW; ++i)
-      if (i < nv) D[i] = load_row_tile(wg, wu, (size_t)(row_blk(i, 0) - (const uint8_t*)0) / BLOCK_BYTES, h);
+    for (int i = 0; i < RTW; ++i) D[i] = load_row_tile(wg, wu, (size_t)(row_blk(i, 0) - (const uint8_t*)0) / BLOCK_BYTES, h);
     for (int kb = 0; kb < nbH; ++kb) kstep(kb);
 
     // SwiGLU in registers -> fp16 strip and its 32-row means.  Accumulator r
@@ -567,7 +580,7 @@ __device__ __forceinline__ void fused_unit(const uint8_t* __restrict__ wg, const
       }
     }
   }
-  __syncthreads();
+  lds_barrier();   // the strip and its means are complete
 
   // ---------------- phase 2: down projection over this chunk ----------------
   switch (off) {

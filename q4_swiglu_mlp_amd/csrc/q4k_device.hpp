@@ -174,6 +174,13 @@ __device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
 }
 __device__ __forceinline__ int mfma32_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also fences
+// global memory, which waits for every outstanding global load -- including
+// weight prefetches meant to stay in flight across the barrier.  Here each wave
+// waits for its own LDS operations, then meets the others; the memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float silu_f32(float g) {
   // g / (1 + e^-g); for g << 0 the exponential overflows to +inf and the
   // quotient is -0, the correct limit.
