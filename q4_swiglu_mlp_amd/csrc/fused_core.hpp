@@ -284,15 +284,18 @@ __device__ __forceinline__ DownTileData<NP, NB> load_down_tile(const uint8_t* __
   return d;
 }
 
-// Dense-prefill output: plain fp32 partial stores P[chunk][n][t] (t < Mpad).
+// Dense-prefill output: fp16 partial sums P[chunk][n][t] (t < Mpad), already
+// multiplied by the output scale 2^(inter_shift - out_shift), so each is of
+// the order of y itself (fp16-safe by the choice of out_shift).
 struct OutPartial {
-  float* P;
+  _Float16* P;
   int Mpad;
   int H;
+  float scale;
   __device__ __forceinline__ void put(int chunk, int n, int row_in_unit, int tok, float w, float v) const {
     (void)tok;
     (void)w;
-    P[((size_t)chunk * H + n) * Mpad + row_in_unit] = v;
+    P[((size_t)chunk * H + n) * Mpad + row_in_unit] = (_Float16)(v * scale);
   }
 };
 

@@ -26,8 +26,8 @@ __global__ __launch_bounds__(64 * FuWaves<TT>::value) void k_prefill_fused(const
                                                               const uint8_t* __restrict__ wu,
                                                               const uint8_t* __restrict__ wd, int H, int I,
                                                               const _Float16* __restrict__ x, int M,
-                                                              float* __restrict__ P, int Mpad, float inter_scale,
-                                                              int n_tiles, int n_chunks) {
+                                                              _Float16* __restrict__ P, int Mpad, float inter_scale,
+                                                              float out_scale, int n_tiles, int n_chunks) {
   using C = FusedCfg<TT, RTW, ICMAX>;
   __shared__ __attribute__((aligned(16))) FusedSmem<TT, RTW, ICMAX> sm;
   __shared__ int tok[C::MT];
@@ -50,58 +50,57 @@ __global__ __launch_bounds__(64 * FuWaves<TT>::value) void k_prefill_fused(const
     wrow[threadIdx.x] = 1.0f;
   }
   __syncthreads();
-  OutPartial out{P, Mpad, H};
+  OutPartial out{P, Mpad, H, out_scale};
   fused_unit<TT, RTW, ICMAX>(wg, wu, wd, H, I, x, tok, wrow, chunk, r0, r1, tile * C::MT, inter_scale, out, sm);
 }
 
-// y[t][n] = fp16(scale * sum_c P[c][n][t]) through a 64x64 LDS transpose.
-// Thread (tx, ty) sums the float4 of tokens 4tx..4tx+3 for hidden rows
-// ty + 16i (i < 4) over all chunks, four chunks' loads in flight at a time.
-__global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict__ P, int S, int H, int Mpad,
-                                                        _Float16* __restrict__ y, int M, float scale) {
+// y[t][n] = fp16(sum_c P[c][n][t]) through a 64x64 LDS transpose.  Thread
+// (tx, ty) sums tokens 8tx..8tx+7 (one 16-byte load) of hidden rows ty and
+// ty + 32 over all chunks in fp32, four chunks' loads in flight at a time.
+__global__ __launch_bounds__(256) void k_reduce_partials(const _Float16* __restrict__ P, int S, int H, int Mpad,
+                                                        _Float16* __restrict__ y, int M) {
   __shared__ float tile[64][65];
   const int n0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float4 acc[4];
+  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
+  float acc[2][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
   const size_t plane = (size_t)H * Mpad;
-  const float* base = P + (size_t)(n0 + ty) * Mpad + t0 + 4 * tx;
+  const _Float16* base = P + (size_t)(n0 + ty) * Mpad + t0 + 8 * tx;
+  auto add = [&](int i, const uint4& v) {
+    const half8 h = __builtin_bit_cast(half8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] += (float)h[e];
+  };
   int c = 0;
   for (; c + 4 <= S; c += 4) {
-    float4 v[4][4];
+    uint4 v[4][2];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        v[u][i] = *reinterpret_cast<const float4*>(base + (c + u) * plane + (size_t)16 * i * Mpad);
+      for (int i = 0; i < 2; ++i)
+        v[u][i] = *reinterpret_cast<const uint4*>(base + (c + u) * plane + (size_t)32 * i * Mpad);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i].x += v[u][i].x; acc[i].y += v[u][i].y; acc[i].z += v[u][i].z; acc[i].w += v[u][i].w;
-      }
+      for (int i = 0; i < 2; ++i) add(i, v[u][i]);
   }
   for (; c < S; ++c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 v = *reinterpret_cast<const float4*>(base + c * plane + (size_t)16 * i * Mpad);
-      acc[i].x += v.x; acc[i].y += v.y; acc[i].z += v.z; acc[i].w += v.w;
-    }
+    for (int i = 0; i < 2; ++i) add(i, *reinterpret_cast<const uint4*>(base + c * plane + (size_t)32 * i * Mpad));
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    tile[ty + 16 * i][4 * tx + 0] = acc[i].x;
-    tile[ty + 16 * i][4 * tx + 1] = acc[i].y;
-    tile[ty + 16 * i][4 * tx + 2] = acc[i].z;
-    tile[ty + 16 * i][4 * tx + 3] = acc[i].w;
-  }
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[ty + 32 * i][8 * tx + e] = acc[i][e];
   __syncthreads();
   const int wx = threadIdx.x & 63, wy = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int t = t0 + wy + 4 * i;
-    if (t < M) y[(size_t)t * H + n0 + wx] = (_Float16)(tile[wx][wy + 4 * i] * scale);
+    if (t < M) y[(size_t)t * H + n0 + wx] = (_Float16)tile[wx][wy + 4 * i];
   }
 }
 
@@ -145,35 +144,36 @@ Plan make_plan(int M, int H, int I) {
 
 template <int TT, int RTW, int ICMAX>
 void launch_cfg(const Plan& p, const void* wg, const void* wu, const void* wd, int H, int I, const void* x, int M,
-                float* P, float inter_scale, hipStream_t stream) {
+                _Float16* P, float inter_scale, float out_scale, hipStream_t stream) {
   const int n_groups = (p.n_chunks + 7) / 8;
   hipLaunchKernelGGL((k_prefill_fused<TT, RTW, ICMAX>), dim3(n_groups * 8 * p.n_tiles), dim3(FusedCfg<TT, RTW, ICMAX>::THREADS), 0, stream,
                      static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
                      static_cast<const uint8_t*>(wd), H, I, static_cast<const _Float16*>(x), M, P, p.Mpad,
-                     inter_scale, p.n_tiles, p.n_chunks);
+                     inter_scale, out_scale, p.n_tiles, p.n_chunks);
 }
 
 }  // namespace
 
 size_t prefill_workspace_bytes(int M, int hidden, int inter) {
   const Plan p = make_plan(M > 0 ? M : 1, hidden, inter);
-  return (size_t)p.n_chunks * hidden * p.Mpad * sizeof(float);
+  return (size_t)p.n_chunks * hidden * p.Mpad * sizeof(_Float16);
 }
 
 hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
                           void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
   const Plan p = make_plan(M, hidden, inter);
-  float* P = static_cast<float*>(ws);
+  _Float16* P = static_cast<_Float16*>(ws);
   const float inter_scale = ldexpf(1.0f, -inter_shift);
+  const float out_scale = ldexpf(1.0f, inter_shift - out_shift);
   timing_begin(stream);
   switch (p.cfg) {
-    case 'A': launch_cfg<1, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, stream); break;
-    case 'B': launch_cfg<2, 1, 640>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, stream); break;
-    default: launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, stream); break;
+    case 'A': launch_cfg<1, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
+    case 'B': launch_cfg<2, 1, 640>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
+    default: launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
   }
   timing_end(stream);
-  hipLaunchKernelGGL(k_reduce_partials, dim3(hidden / 64, p.Mpad / 64), dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, static_cast<_Float16*>(y), M,
-                     ldexpf(1.0f, inter_shift - out_shift));
+  hipLaunchKernelGGL(k_reduce_partials, dim3(hidden / 64, p.Mpad / 64), dim3(256), 0, stream, P, p.n_chunks, hidden,
+                     p.Mpad, static_cast<_Float16*>(y), M);
   return hipGetLastError();
 }
 
