@@ -32,8 +32,8 @@ METRIC = "Q4_K SwiGLU-MLP tokens/s at 4096/11008 M=256; % of MFMA/HBM roofline"
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_fused_m256_traffic.json")
-KERNEL_SOURCES = ("q4_swiglu_mlp_amd/csrc/fused_core.hpp", "q4_swiglu_mlp_amd/csrc/q4k_device.hpp",
-                  "q4_swiglu_mlp_amd/csrc/k_prefill.hip")
+KERNEL_SOURCES = ("q4_swiglu_mlp_amd/csrc/fused16.hpp", "q4_swiglu_mlp_amd/csrc/fused_core.hpp",
+                  "q4_swiglu_mlp_amd/csrc/q4k_device.hpp", "q4_swiglu_mlp_amd/csrc/k_prefill.hip")
 
 
 def kernel_source_hash() -> str:
@@ -99,7 +99,7 @@ def headline(args, torch):
             traffic = rec.get("hbm_bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "k_prefill_fused", "kernel_ms": round(kern_ms, 5),
+                "kernel": "k_prefill_fused16", "kernel_ms": round(kern_ms, 5),
                 "flops_per_launch": flops}
     res = {
         "value": w.M * args.steps / wall,

@@ -92,8 +92,10 @@ int zinc_q4k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* 
  * tokens x intermediate strip in LDS and runs the down projection on it, so
  * the intermediate never reaches device memory ("Fused SwiGLU MLP: ZINC RDNA4
  * Down-Projection Bandwidth", sections "Why this fusion is harder than the
- * last one" and "What it is worth").  Partial down-projection sums of the
- * intermediate chunks are reduced in fp32 in `workspace`.
+ * last one" and "What it is worth").  `workspace` holds the activation
+ * rearranged into the MFMA operand order (written first, by a small kernel)
+ * and the down-projection partial sums of the intermediate chunks, stored as
+ * fp16 at the output scale and summed in fp32 by a reduce kernel.
  * Limits: hidden, inter multiples of 256, hidden <= 16384, inter <= 65536.
  */
 size_t zinc_mlp_q4k_prefill_workspace_size(int32_t M, int32_t hidden, int32_t inter);

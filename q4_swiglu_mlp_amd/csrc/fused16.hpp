@@ -1,0 +1,398 @@
+// Fused Q4_K SwiGLU unit for 64-token tiles (the dense prefill).
+//
+// A unit is one (64-token tile, intermediate chunk of at most ICMAX rows)
+// pair, run by one workgroup of 12 waves:
+//
+//   phase 1  gate and up for the chunk: each wave owns a 16-row tile of the
+//            chunk and walks the whole hidden dimension one Q4_K super-block
+//            column at a time with 16x16x32 fp16 MFMAs (fp32 accumulation).  A
+//            lane decodes eight weights per MFMA step (its row r = l%16, octet
+//            o = l/16) and that operand meets all four 16-token groups of the
+//            tile, so each decoded weight serves 64 tokens.  SwiGLU is applied
+//            in registers and the fp16 strip [64 tokens x chunk] lands in LDS.
+//   phase 2  the down projection of the strip (fu_phase2, 32x32x16 MFMAs, two
+//            32-token tiles per decoded W_down operand).
+//
+// Weights are decoded in registers on the way into the multiply ("VGPR
+// pressure caps the fused RDNA4 prefill GEMM at nine waves", "What the fused
+// GEMM actually spends registers on"); the strip never leaves the chip ("Fused
+// SwiGLU MLP: ZINC RDNA4 Down-Projection Bandwidth", "Why this fusion is harder
+// than the last one").
+//
+// Lane layout of phase 1 (as in the decode MFMA kernels): per block a lane
+// loads the 16-byte header and the quant runs [16o, +16) and [64+16o, +16);
+// MFMA i (0..7) takes dword i%4 of the first run (i < 4) or of the second, whose
+// eight slots are weights {0,2,1,3,32,34,33,35} + 64c + 16(o%2) + 4(i%4) of the
+// block (c = o/2, or 2 + o/2).  The activation is staged once per call by
+// k_stage_x16 in exactly that order, with the 32-element means the -dmin*m
+// term is contracted against (one MFMA per four blocks, lane octet o supplying
+// block 4g+o's eight -32*dmin*m values), so a unit copies its columns into LDS
+// with plain 16-byte moves.
+#pragma once
+
+#include <type_traits>
+
+#include "fused_core.hpp"
+
+namespace zinc {
+
+typedef float f32x4_16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_16 __attribute__((ext_vector_type(4)));   // native 128-bit vector: no struct copies
+
+__device__ __forceinline__ uint4 as_u4(u32x4_16 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+__device__ __forceinline__ f32x4_16 mfma16x16(half8 a, half8 b, f32x4_16 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Staged activation, per (64-token tile, block column): 64 token rows of
+// X16_ROW halves (32 operand pieces of eight fp16, then one piece of padding
+// that staggers the LDS banks of consecutive tokens), then 64 pieces of
+// 32-means (token t's eight sub-block means, sb_slot order).
+constexpr int X16_ROW = QK + 8;
+constexpr int X16_XPIECES = 64 * (X16_ROW / 8);   // 2112
+constexpr int X16_PIECES = X16_XPIECES + 64;      // 2176 = 34 waves of 16-byte pieces
+constexpr int X16_COL = X16_PIECES * 8;           // halves per column
+
+// Operand slot of the eight activations 64c + 4j + {0..3} and 64c + 32 + 4j +
+// {0..3} of a block: MFMA i = 4(c/2) + j%4, octet o = 2(c%2) + j/4.
+__host__ __device__ constexpr int x16_slot(int c, int j) { return (4 * (c >> 1) + (j & 3)) * 4 + 2 * (c & 1) + (j >> 2); }
+
+template <int ICMAX>
+struct Fused16Cfg {
+  static constexpr int MT = 64;                       // tokens per unit
+  static constexpr int WAVES = 12;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int XS = X16_ROW;
+  static constexpr int HS = ICMAX + 8;                // strip row stride (halves)
+  static constexpr int NBMAX = (ICMAX - 64) / 256 + 2;  // W_down blocks a chunk can touch
+  static constexpr int HSS = ((8 * NBMAX + 15) / 16) * 16;
+  static constexpr int XRING = 8;                     // block columns of means kept (two correction groups)
+  static constexpr int NCOPY = (X16_PIECES + THREADS - 1) / THREADS;
+  static constexpr int NJUNK = NCOPY * THREADS - X16_PIECES;   // copy slots past the column
+  static_assert(ICMAX % 64 == 0, "chunks are whole 64-row panels");
+  static_assert(ICMAX / 16 <= WAVES, "one 16-row tile per wave");
+};
+
+template <int ICMAX>
+struct Fused16Smem {
+  using C = Fused16Cfg<ICMAX>;
+  union {
+    // phase 1: activation columns in operand order, slot = column % 4 (the
+    // column being read, the next one, and the two being staged)
+    _Float16 xs[4][C::MT * C::XS];
+    // after phase 1 (the same memory): the intermediate strip in panel order
+    // and its 32-row means (block-aligned, zero-padded)
+    struct {
+      _Float16 hs[C::MT * C::HS];
+      _Float16 hsum[C::MT * C::HSS];
+    } s;
+  } u;
+  _Float16 xm[C::XRING][C::MT * 8];     // 32-means per block column, ring
+  float hsum32[C::MT * C::HSS];         // the strip's 32-row sums while phase 1 runs
+  _Float16 junk[(C::NJUNK > 0 ? C::NJUNK : 1) * 8];   // stores of the copy slots past a column
+};
+
+// Scales of the two chunks a lane decodes per block (chunk c0 = sel, c1 =
+// 2 + sel): s = RNE16(d*sc) as (1024 + sc)*d - 1024*d, rounded once, each
+// packed with its offset constant (-1024*s for the low-nibble sub-block, -64*s
+// for the high one) as (s, c): one register per sub-block.
+struct Lane16S {
+  half2v lo0, hi0, lo1, hi1;
+};
+
+__device__ __forceinline__ Lane16S lane16_scales(uint4 hdr, int sel) {
+  const SixBit sb = unpack_sixbit(hdr.y, hdr.z, hdr.w);
+  const uint32_t a = sb.sc03 >> (16 * sel);
+  const uint32_t b = sb.sc47 >> (16 * sel);
+  const uint32_t pl = (a & 0xFFu) | ((b & 0xFFu) << 16);
+  const uint32_t ph = ((a >> 8) & 0xFFu) | (((b >> 8) & 0xFFu) << 16);
+  const half2v d2 = splat_lo(hdr.x);
+  const half2v nd = d2 * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const half2v slo = __builtin_elementwise_fma(bits_h2(pl | 0x64006400u), d2, nd);   // (s_2c0, s_2c1)
+  const half2v shi = __builtin_elementwise_fma(bits_h2(ph | 0x64006400u), d2, nd);   // (s_2c0+1, s_2c1+1)
+  const half2v klo = {(_Float16)1.0f, (_Float16)-1024.0f};
+  const half2v khi = {(_Float16)1.0f, (_Float16)-64.0f};
+  Lane16S r;
+  r.lo0 = half2v{slo[0], slo[0]} * klo;
+  r.lo1 = half2v{slo[1], slo[1]} * klo;
+  r.hi0 = half2v{shi[0], shi[0]} * khi;
+  r.hi1 = half2v{shi[1], shi[1]} * khi;
+  return r;
+}
+
+// dequant_dword_scaled with the packed (s, c) registers.
+__device__ __forceinline__ half8 dequant_dword_sc(uint32_t Q, half2v sc_lo, half2v sc_hi, const NibbleK& k) {
+  const half2v s_lo = __builtin_shufflevector(sc_lo, sc_lo, 0, 0), c_lo = __builtin_shufflevector(sc_lo, sc_lo, 1, 1);
+  const half2v s_hi = __builtin_shufflevector(sc_hi, sc_hi, 0, 0), c_hi = __builtin_shufflevector(sc_hi, sc_hi, 1, 1);
+  return dequant_dword_scaled(Q, s_lo, c_lo, s_hi, c_hi, k);
+}
+
+// The nibble masks in SGPRs (a VALU operation may read one), the exponent
+// patterns in VGPRs: (q & mask) | magic stays one v_and_or_b32.
+__device__ __forceinline__ NibbleK nibble_consts_s() {
+  NibbleK k;
+  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(k.lo_mask));
+  asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(k.hi_mask));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.lo_magic));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(k.hi_magic));
+  return k;
+}
+
+// One staged column in flight: NCOPY 16-byte pieces per thread.  Waves past
+// the column's 34 waves of pieces re-read piece 0 (in bounds, never stored),
+// so no branch surrounds a load.
+template <int N>
+struct X16Copy {
+  u32x4_16 v[N];
+};
+
+template <class C>
+__device__ __forceinline__ X16Copy<C::NCOPY> fu16_load_col(const _Float16* __restrict__ col) {
+  X16Copy<C::NCOPY> r;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int it = 0; it < C::NCOPY; ++it) {
+    const bool wave_in = wv * 64 + C::THREADS * it < X16_PIECES;   // uniform
+    const int p = wave_in ? (int)threadIdx.x + C::THREADS * it : 0;
+    r.v[it] = *reinterpret_cast<const u32x4_16*>(col + 8 * p);
+  }
+  return r;
+}
+
+// Every copy slot stores (no branch: a load whose only use sits behind one is
+// sunk to it by the compiler, with a full wait); slots past the column's
+// pieces land in a junk area.
+template <class C>
+__device__ __forceinline__ void fu16_store_col(const X16Copy<C::NCOPY>& xc, _Float16* __restrict__ xs,
+                                               _Float16* __restrict__ xm, _Float16* __restrict__ junk) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int it = 0; it < C::NCOPY; ++it) {
+    const int p = (int)threadIdx.x + C::THREADS * it;
+    const int w0 = wv * 64 + C::THREADS * it;   // the wave's first piece: whole waves share a destination
+    _Float16* dst = (w0 < X16_XPIECES) ? xs + 8 * p
+                    : (w0 < X16_PIECES) ? xm + 8 * (p - X16_XPIECES)
+                                        : junk + 8 * (p - X16_PIECES);
+    *reinterpret_cast<u32x4_16*>(dst) = xc.v[it];
+  }
+}
+
+// One fused 64-token unit.  xcol = the tile's staged columns (k_stage_x16);
+// tok/wrow (LDS, 64 entries) map unit rows to tokens and output weights for
+// phase 2 and are visible to all threads before the call; row0 is the unit's
+// first output row handed to the output policy.
+template <int ICMAX, class Out>
+__device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+                                             const uint8_t* __restrict__ wd, int H, int I,
+                                             const _Float16* __restrict__ xcol, const int* __restrict__ tok,
+                                             const float* __restrict__ wrow, int chunk, int r0, int r1, int row0,
+                                             float inter_scale, const Out& out, Fused16Smem<ICMAX>& sm) {
+  using C = Fused16Cfg<ICMAX>;
+  constexpr int XS = C::XS, HS = C::HS, HSS = C::HSS, MT = C::MT;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, o = lane >> 4, sel = (o >> 1) & 1;
+  const int nbH = H / QK;
+  const size_t rowb = (size_t)nbH * BLOCK_BYTES;
+  const NibbleK nk = nibble_consts_s();
+  const int nrt = (r1 - r0) / 16;                 // 16-row tiles in the chunk (<= WAVES)
+  const int off = (r0 >> 6) & 3;                  // chunk's first panel within its W_down block
+  const int rt = wave;
+  const bool act = rt < nrt;                      // wave-uniform
+  const int rtc = act ? rt : nrt - 1;             // idle waves stream an in-bounds tile (never used)
+  // weight rows as 32-bit offsets from the (uniform) matrix bases, so loads
+  // take the scalar-base form
+  const uint32_t wrow_off = (uint32_t)((size_t)(r0 + rtc * 16 + r) * rowb);
+
+  for (int i = threadIdx.x; i < MT * HSS; i += C::THREADS) sm.hsum32[i] = 0.0f;
+  // the means ring: octets past the last block of a short final group read
+  // slots never written in this unit; zero operands need finite partners
+  for (int i = threadIdx.x; i < C::XRING * MT * 8; i += C::THREADS) (&sm.xm[0][0])[i] = (_Float16)0.0f;
+
+  f32x4_16 accg[4], accu[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) accg[g][e] = accu[g][e] = 0.0f;
+
+  // prologue: columns 0 and 1 staged
+  {
+    const X16Copy<C::NCOPY> x0 = fu16_load_col<C>(xcol);
+    const int c1 = nbH > 1 ? 1 : 0;
+    const X16Copy<C::NCOPY> x1 = fu16_load_col<C>(xcol + (size_t)c1 * X16_COL);
+    lds_barrier();   // ring zeroed before the means land in it
+    fu16_store_col<C>(x0, sm.u.xs[0], sm.xm[0], sm.junk);
+    fu16_store_col<C>(x1, sm.u.xs[1], sm.xm[c1], sm.junk);
+  }
+
+  // The column loop, once for waves with a row tile (ACT) and once for idle
+  // waves, which only help stage the activation; both meet the same barriers.
+  //
+  // Staging.  Column c is copied into slot c % 4 during block c-2 (MFMA step
+  // 4); a barrier at the top of every even block publishes the two columns
+  // copied in the two blocks before and releases the two slots read there.
+  //
+  // Pipeline.  Within a block an active wave's MFMA steps are
+  // software-pipelined: the B operands and the decoded A operands of step i+1
+  // are fetched while step i's eight MFMAs run.
+  auto column_loop = [&](auto act_tag) {
+    constexpr bool ACT = decltype(act_tag)::value;
+    u32x4_16 hg, hu, qg0, qu0, qg1, qu1;
+    u32x4_16 cg = {0u, 0u, 0u, 0u}, cu = {0u, 0u, 0u, 0u};   // headers for the min correction
+    if constexpr (ACT) {
+      hg = *reinterpret_cast<const u32x4_16*>(wg + wrow_off);
+      hu = *reinterpret_cast<const u32x4_16*>(wu + wrow_off);
+      qg0 = *reinterpret_cast<const u32x4_16*>(wg + (wrow_off + 16 + 16 * o));
+      qu0 = *reinterpret_cast<const u32x4_16*>(wu + (wrow_off + 16 + 16 * o));
+      qg1 = *reinterpret_cast<const u32x4_16*>(wg + (wrow_off + 80 + 16 * o));
+      qu1 = *reinterpret_cast<const u32x4_16*>(wu + (wrow_off + 80 + 16 * o));
+    }
+    const int xlane = r * XS + o * 8;   // lane's token r of group 0, octet o
+    for (int kb = 0; kb < nbH; ++kb) {
+      // weight refills read column kn, the staging copy column kx; past the
+      // end they re-read the last column (never used), so no branch ever
+      // surrounds a load
+      const int kn = (kb + 1 < nbH) ? kb + 1 : kb;
+      const int kx = (kb + 2 < nbH) ? kb + 2 : nbH - 1;
+      const uint32_t noff = wrow_off + (uint32_t)kn * BLOCK_BYTES;
+      if ((kb & 1) == 0) lds_barrier();
+      const X16Copy<C::NCOPY> xc = fu16_load_col<C>(xcol + (size_t)kx * X16_COL);
+      _Float16* const xs_next = sm.u.xs[(kb + 2) & 3];
+      _Float16* const xm_next = sm.xm[kx & (C::XRING - 1)];
+      if constexpr (ACT) {
+        const Lane16S sg = lane16_scales(as_u4(hg), sel), su = lane16_scales(as_u4(hu), sel);
+        // octet o keeps block (kb & ~3) + o's headers for the correction
+        const bool mine = o == (kb & 3);
+        cg = mine ? hg : cg;
+        cu = mine ? hu : cu;
+        hg = *reinterpret_cast<const u32x4_16*>(wg + noff);
+        hu = *reinterpret_cast<const u32x4_16*>(wu + noff);
+        // keep the column's loads here, a whole block step ahead of their use
+        // (left alone, the scheduler sinks them below the MFMAs)
+        __builtin_amdgcn_sched_barrier(0);
+        const _Float16* xb = sm.u.xs[kb & 3] + xlane;
+        auto load_b = [&](int i, half8 (&b)[4]) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const half8*>(xb + g * 16 * XS + i * 32);
+        };
+        auto decode = [&](int i, half8& ag, half8& au) {
+          const uint32_t qg = (i < 4) ? qg0[i & 3] : qg1[i & 3];
+          const uint32_t qu = (i < 4) ? qu0[i & 3] : qu1[i & 3];
+          ag = (i < 4) ? dequant_dword_sc(qg, sg.lo0, sg.hi0, nk) : dequant_dword_sc(qg, sg.lo1, sg.hi1, nk);
+          au = (i < 4) ? dequant_dword_sc(qu, su.lo0, su.hi0, nk) : dequant_dword_sc(qu, su.lo1, su.hi1, nk);
+        };
+        half8 bc[4], bn[4], agc, auc, agn, aun;
+        load_b(0, bc);
+        decode(0, agc, auc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i < 7) {
+            load_b(i + 1, bn);
+            decode(i + 1, agn, aun);
+          }
+          if (i == 3) {   // the first quant run is decoded: refill it in place
+            qg0 = *reinterpret_cast<const u32x4_16*>(wg + (noff + 16 + 16 * o));
+            qu0 = *reinterpret_cast<const u32x4_16*>(wu + (noff + 16 + 16 * o));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (i == 4) {
+            // column kx into its slot and the means ring: the last barrier
+            // released that slot, and the ring slot written is none of the
+            // four the corrections of blocks up to kb+1 read (past the end a
+            // rewrite of data nobody reads again, or of the same values)
+            fu16_store_col<C>(xc, xs_next, xm_next, sm.junk);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (i == 6) {   // and the second
+            qg1 = *reinterpret_cast<const u32x4_16*>(wg + (noff + 80 + 16 * o));
+            qu1 = *reinterpret_cast<const u32x4_16*>(wu + (noff + 80 + 16 * o));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            accg[g] = mfma16x16(agc, bc[g], accg[g]);
+            accu[g] = mfma16x16(auc, bc[g], accu[g]);
+          }
+          if (i < 7) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) bc[g] = bn[g];
+            agc = agn;
+            auc = aun;
+          }
+          // issue order of the step: the next B reads, then the MFMAs with
+          // the next decode's VALU work threaded between them
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
+        }
+        // min correction once per four blocks (or at the last): octet o holds
+        // block (kb & ~3) + o's headers (zero past the last block: zero
+        // operand), contracted with that block's means
+        if ((kb & 3) == 3 || kb == nbH - 1) {
+          const half8 dmg = block_neg_dm32(as_u4(cg)), dmu = block_neg_dm32(as_u4(cu));
+          const _Float16* mb = sm.xm[((kb & ~3) + o) & (C::XRING - 1)] + r * 8;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const half8 b = *reinterpret_cast<const half8*>(mb + g * 16 * 8);
+            accg[g] = mfma16x16(dmg, b, accg[g]);
+            accu[g] = mfma16x16(dmu, b, accu[g]);
+          }
+          cg = u32x4_16{0u, 0u, 0u, 0u};
+          cu = u32x4_16{0u, 0u, 0u, 0u};
+        }
+      } else {
+        fu16_store_col<C>(xc, xs_next, xm_next, sm.junk);
+      }
+    }
+  };
+  if (act)
+    column_loop(std::true_type{});
+  else
+    column_loop(std::false_type{});
+  lds_barrier();   // the strip below overwrites the activation slots
+
+  // SwiGLU in registers -> fp16 strip (panel order) and the 32-row sums.
+  // Accumulator e of lane (r, o) in group g: row 4o + e of the tile, token 16g + r.
+  if (act) {
+    const int jl = rt * 16 + 4 * o;                     // chunk-local row, multiple of 4
+    const int jg = off * 64 + rt * 16;                  // row from the start of the chunk's first W_down block
+    const int slot = 8 * (jg >> 8) + sb_slot((jg >> 5) & 7);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      _Float16 hv[4];
+      float s4 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hv[e] = (_Float16)(silu_f32(accg[g][e]) * accu[g][e] * inter_scale);
+        s4 += (float)hv[e];
+      }
+      const int t = g * 16 + r;
+      // rows jl..jl+3 sit at panel_pos(jl % 64) + {0, 2, 1, 3}
+      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, hv[0]) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, hv[2]) << 16);
+      const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, hv[1]) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, hv[3]) << 16);
+      *reinterpret_cast<uint2*>(sm.u.s.hs + t * HS + (jl & ~63) + panel_pos(jl & 63)) = make_uint2(w0, w1);
+      // the tile's 16 rows of token t: octets of lanes r, r+16, r+32, r+48
+      s4 += __shfl_xor(s4, 16, 64);
+      s4 += __shfl_xor(s4, 32, 64);
+      if (o == 0) atomicAdd(&sm.hsum32[t * HSS + slot], s4);
+    }
+  }
+  lds_barrier();   // strip and sums complete
+  for (int i = threadIdx.x; i < MT * HSS; i += C::THREADS) sm.u.s.hsum[i] = (_Float16)(sm.hsum32[i] * 0.03125f);
+  lds_barrier();
+
+  // ---------------- phase 2: down projection over this chunk ----------------
+  switch (off) {
+    case 0: fu_phase2<C, 2, ICMAX, 0>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    case 1: fu_phase2<C, 2, ICMAX, 1>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    case 2: fu_phase2<C, 2, ICMAX, 2>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    default: fu_phase2<C, 2, ICMAX, 3>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+  }
+}
+
+}  // namespace zinc

@@ -27,7 +27,7 @@
 //   means of the strip standing in for those of x); each 32-row tile of the
 //   hidden output is produced
 //   from the strip held in LDS and handed to the output policy (dense: a plain
-//   fp32 partial store per chunk; MoE: see k_moe.hip).
+//   an fp16 partial store per chunk at the output scale; MoE: see k_moe.hip).
 //
 // This is the dataflow of "Fused SwiGLU MLP: ZINC RDNA4 Down-Projection
 // Bandwidth" ("Why this fusion is harder than the last one": compute a block of
@@ -305,11 +305,11 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int s) {
 
 // Phase 2 of a unit: the down projection of the chunk [r0, r1) over all
 // hidden output rows, from the strip in LDS.  OFF = (r0 / 64) % 4.
-template <int TT, int RTW, int ICMAX, int OFF, class Out>
+template <class C, int TT, int ICMAX, int OFF, class Out>
 __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H, int I, const int* __restrict__ tok,
                                           const float* __restrict__ wrow, int chunk, int r0, int r1, int row0,
-                                          const Out& out, FusedSmem<TT, RTW, ICMAX>& sm, const NibbleK& nk) {
-  using C = FusedCfg<TT, RTW, ICMAX>;
+                                          const Out& out, const _Float16* __restrict__ hs,
+                                          const _Float16* __restrict__ hsum, const NibbleK& nk) {
   constexpr int HS = C::HS, HSS = C::HSS;
   constexpr int NB = C::NBMAX;
   constexpr int NP = ICMAX / 64;
@@ -348,7 +348,7 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
           const half8 a = dequant_dword_scaled(dword_of(dt.qs[p], s), cs.s_lo, cs.c_lo, cs.s_hi, cs.c_hi, nk);
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) {
-            const half8 bf = *reinterpret_cast<const half8*>(sm.hs + (tt * 32 + l32) * HS + p * 64 + (2 * s + h) * 8);
+            const half8 bf = *reinterpret_cast<const half8*>(hs + (tt * 32 + l32) * HS + p * 64 + (2 * s + h) * 8);
             acc[tt] = mfma32(a, bf, acc[tt]);
           }
         }
@@ -371,7 +371,7 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
         const half8 a = (h == 0) ? n0 : n1;
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-          const half8 bf = *reinterpret_cast<const half8*>(sm.hsum + (tt * 32 + l32) * HSS + 16 * g + 8 * h);
+          const half8 bf = *reinterpret_cast<const half8*>(hsum + (tt * 32 + l32) * HSS + 16 * g + 8 * h);
           acc[tt] = mfma32(a, bf, acc[tt]);
         }
       }
@@ -587,10 +587,10 @@ __device__ __forceinline__ void fused_unit(const uint8_t* __restrict__ wg, const
 
   // ---------------- phase 2: down projection over this chunk ----------------
   switch (off) {
-    case 0: fu_phase2<TT, RTW, ICMAX, 0>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm, nk); break;
-    case 1: fu_phase2<TT, RTW, ICMAX, 1>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm, nk); break;
-    case 2: fu_phase2<TT, RTW, ICMAX, 2>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm, nk); break;
-    default: fu_phase2<TT, RTW, ICMAX, 3>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm, nk); break;
+    case 0: fu_phase2<C, TT, ICMAX, 0>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.hs, sm.hsum, nk); break;
+    case 1: fu_phase2<C, TT, ICMAX, 1>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.hs, sm.hsum, nk); break;
+    case 2: fu_phase2<C, TT, ICMAX, 2>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.hs, sm.hsum, nk); break;
+    default: fu_phase2<C, TT, ICMAX, 3>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.hs, sm.hsum, nk); break;
   }
 }
 

@@ -1,19 +1,23 @@
-// Dense batched prefill: the fused Q4_K SwiGLU unit (fused_core.hpp) over
-// (token tiles) x (intermediate chunks); every unit stores its fp32 partial of
-// the down projection, and a reduce kernel sums the chunks, scales and writes
-// y in fp16.
+// Dense batched prefill: a fused Q4_K SwiGLU unit over (token tiles) x
+// (intermediate chunks); every unit stores its fp16 partial of the down
+// projection (already at the output scale), and a reduce kernel sums the
+// chunks in fp32 and writes y in fp16.
 //
 // Tile choice.  A unit of MT tokens x IC intermediate rows decodes every weight
 // of its chunk once for its MT tokens, so the dequant work grows with M/MT; its
-// partial output is MT x hidden fp32, so the reduction traffic grows with
+// partial output is MT x hidden fp16, so the reduction traffic grows with
 // I/IC.  Units must also cover the 256 CUs.  Configurations (MT, IC <= ICMAX):
-//   A: MT=32, ICMAX=384 -- M <= 512: 256 units at M=256 (8 tiles x 32 chunks)
-//   B: MT=64, ICMAX=640 -- large M, balanced dequant/reduction
-//   C: MT=64, ICMAX=384 -- large M, more chunks (more units, more reduction)
+//   D: MT=64, ICMAX=192 -- the 64-token 16x16x32 unit (fused16.hpp) on an
+//      activation staged once per call (k_stage_x16): 256 units at M=256
+//      (4 tiles x 64 chunks).  The default: fastest measured at every M from
+//      32 to 1024.
+//   A: MT=32, ICMAX=384, B: MT=64, ICMAX=640, C: MT=64, ICMAX=384 -- the
+//      32x32x16 unit of fused_core.hpp, kept as tuning alternatives
+//      (ZINC_PREFILL_CFG).
 #include <cstdlib>
 #include <cstring>
 
-#include "fused_core.hpp"
+#include "fused16.hpp"
 #include "launch.hpp"
 #include "util_kernels.hpp"
 
@@ -52,6 +56,80 @@ __global__ __launch_bounds__(64 * FuWaves<TT>::value) void k_prefill_fused(const
   __syncthreads();
   OutPartial out{P, Mpad, H, out_scale};
   fused_unit<TT, RTW, ICMAX>(wg, wu, wd, H, I, x, tok, wrow, chunk, r0, r1, tile * C::MT, inter_scale, out, sm);
+}
+
+// The 64-token unit (fused16.hpp) over (token tiles) x (chunks), same
+// XCD-aware unit order as above.  xg = the staged activation (k_stage_x16).
+template <int ICMAX>
+__global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused16(
+    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, const uint8_t* __restrict__ wd, int H, int I,
+    const _Float16* __restrict__ xg, int M, _Float16* __restrict__ P, int Mpad, float inter_scale, float out_scale,
+    int n_tiles, int n_chunks) {
+  __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX> sm;
+  __shared__ int tok[64];
+  __shared__ float wrow[64];
+  const int bid = blockIdx.x;
+  const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
+  const int tile = rem >> 3;
+  const int chunk = grp * 8 + (rem & 7);
+  if (chunk >= n_chunks) return;
+  const int npan = I / 64;
+  const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
+  const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
+  if (threadIdx.x < 64) {
+    const int t = tile * 64 + threadIdx.x;
+    tok[threadIdx.x] = (t < M) ? t : -1;
+    wrow[threadIdx.x] = 1.0f;
+  }
+  __syncthreads();
+  OutPartial out{P, Mpad, H, out_scale};
+  const _Float16* xcol = xg + (size_t)tile * (H / QK) * X16_COL;
+  fused_unit16<ICMAX>(wg, wu, wd, H, I, xcol, tok, wrow, chunk, r0, r1, tile * 64, inter_scale, out, sm);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_src(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// The activation of every 64-token tile in the 64-token unit's operand order
+// (X16_* layout of fused16.hpp), with its 32-element means; tokens past M are
+// zero.  Grid (8, H/256, n_tiles), 256 threads = 8 tokens x 32 pieces: piece
+// (c, j) of a token is x[64c + 4j + {0..3}] and x[64c + 32 + 4j + {0..3}].
+__global__ __launch_bounds__(256) void k_stage_x16(const _Float16* __restrict__ x, int H, int M,
+                                                   _Float16* __restrict__ xg) {
+  const int kb = blockIdx.y, tile = blockIdx.z;
+  const int t = blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int p = threadIdx.x & 31, c = p >> 3, j = p & 7;
+  const int token = tile * 64 + t;
+  _Float16* col = xg + ((size_t)tile * (H / QK) + kb) * X16_COL;
+  uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
+  if (token < M) {
+    const _Float16* src = x + (size_t)token * H + (size_t)kb * QK + 64 * c + 4 * j;
+    lo = *reinterpret_cast<const uint2*>(src);
+    hi = *reinterpret_cast<const uint2*>(src + 32);
+  }
+  // slot order {0,2,1,3} within each group of four
+  const uint32_t l0 = (lo.x & 0xFFFFu) | (lo.y << 16), l1 = (lo.x >> 16) | (lo.y & 0xFFFF0000u);
+  const uint32_t h0 = (hi.x & 0xFFFFu) | (hi.y << 16), h1 = (hi.x >> 16) | (hi.y & 0xFFFF0000u);
+  *reinterpret_cast<uint4*>(col + t * X16_ROW + 8 * x16_slot(c, j)) = make_uint4(l0, l1, h0, h1);
+  if (p == 0) *reinterpret_cast<uint4*>(col + t * X16_ROW + QK) = make_uint4(0, 0, 0, 0);
+  // 32-means: the eight pieces of one (token, chunk) are eight consecutive
+  // lanes; quad sums, then row_shr:4 leaves all eight in lane j == 4
+  const half4 lv = __builtin_bit_cast(half4, lo), hv = __builtin_bit_cast(half4, hi);
+  float sl = ((float)lv[0] + (float)lv[1]) + ((float)lv[2] + (float)lv[3]);
+  float sh = ((float)hv[0] + (float)hv[1]) + ((float)hv[2] + (float)hv[3]);
+  sl += dpp_add_src<0xB1>(sl);
+  sh += dpp_add_src<0xB1>(sh);
+  sl += dpp_add_src<0x4E>(sl);
+  sh += dpp_add_src<0x4E>(sh);
+  sl += dpp_add_src<0x114>(sl);
+  sh += dpp_add_src<0x114>(sh);
+  if (j == 4) {
+    _Float16* m = col + X16_XPIECES * 8 + t * 8;
+    m[sb_slot(2 * c)] = (_Float16)(sl * 0.03125f);
+    m[sb_slot(2 * c + 1)] = (_Float16)(sh * 0.03125f);
+  }
 }
 
 // y[t][n] = fp16(sum_c P[c][n][t]) through a 64x64 LDS transpose.  Thread
@@ -105,7 +183,7 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const _Float16* __restr
 }
 
 struct Plan {
-  char cfg;      // 'A', 'B', 'C'
+  char cfg;      // 'A' .. 'D'
   int MT, ICMAX;
   int n_tiles, n_chunks;
   int Mpad;
@@ -116,20 +194,20 @@ int round_up(int a, int b) { return (a + b - 1) / b * b; }
 Plan make_plan(int M, int H, int I) {
   (void)H;
   Plan p;
-  p.cfg = (M <= 512) ? 'A' : 'B';
+  p.cfg = 'D';
   int chunks_wanted = 0;
-  // tuning override: ZINC_PREFILL_CFG="<A|B|C>[:<chunks>]"
+  // tuning override: ZINC_PREFILL_CFG="<A|B|C|D>[:<chunks>]"
   if (const char* e = std::getenv("ZINC_PREFILL_CFG")) {
-    if (e[0] == 'A' || e[0] == 'B' || e[0] == 'C') p.cfg = e[0];
+    if (e[0] >= 'A' && e[0] <= 'D') p.cfg = e[0];
     if (e[0] && e[1] == ':') chunks_wanted = std::atoi(e + 2);
   }
   p.MT = (p.cfg == 'A') ? 32 : 64;
-  p.ICMAX = (p.cfg == 'B') ? 640 : 384;
+  p.ICMAX = (p.cfg == 'B') ? 640 : (p.cfg == 'D') ? 192 : 384;
   const int npan = I / 64;
   const int min_chunks = (npan + p.ICMAX / 64 - 1) / (p.ICMAX / 64);
   p.n_tiles = (M + p.MT - 1) / p.MT;
   int chunks = min_chunks;
-  if (p.cfg == 'A') {
+  if (p.cfg == 'A' || p.cfg == 'D') {
     // enough units to cover the 256 CUs, up to one 64-row panel per chunk
     const int want = (256 + p.n_tiles - 1) / p.n_tiles;
     chunks = want > chunks ? want : chunks;
@@ -152,11 +230,28 @@ void launch_cfg(const Plan& p, const void* wg, const void* wu, const void* wd, i
                      inter_scale, out_scale, p.n_tiles, p.n_chunks);
 }
 
+template <int ICMAX>
+void launch_cfg16(const Plan& p, const void* wg, const void* wu, const void* wd, int H, int I, const void* x, int M,
+                  _Float16* P, _Float16* xg, float inter_scale, float out_scale, hipStream_t stream) {
+  (void)x;
+  const int n_groups = (p.n_chunks + 7) / 8;
+  hipLaunchKernelGGL((k_prefill_fused16<ICMAX>), dim3(n_groups * 8 * p.n_tiles), dim3(Fused16Cfg<ICMAX>::THREADS), 0,
+                     stream, static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
+                     static_cast<const uint8_t*>(wd), H, I, xg, M, P, p.Mpad, inter_scale, out_scale, p.n_tiles,
+                     p.n_chunks);
+}
+
+size_t partial_bytes(const Plan& p, int H) { return ((size_t)p.n_chunks * H * p.Mpad * sizeof(_Float16) + 255) & ~(size_t)255; }
+
+size_t staged_x_bytes(const Plan& p, int H) {
+  return (p.cfg == 'D') ? (size_t)p.n_tiles * (H / QK) * X16_COL * sizeof(_Float16) : 0;
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int M, int hidden, int inter) {
   const Plan p = make_plan(M > 0 ? M : 1, hidden, inter);
-  return (size_t)p.n_chunks * hidden * p.Mpad * sizeof(_Float16);
+  return partial_bytes(p, hidden) + staged_x_bytes(p, hidden);
 }
 
 hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
@@ -165,8 +260,13 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
   _Float16* P = static_cast<_Float16*>(ws);
   const float inter_scale = ldexpf(1.0f, -inter_shift);
   const float out_scale = ldexpf(1.0f, inter_shift - out_shift);
-  timing_begin(stream);
+  _Float16* xg = reinterpret_cast<_Float16*>(static_cast<char*>(ws) + partial_bytes(p, hidden));
+  if (p.cfg == 'D')
+    hipLaunchKernelGGL(k_stage_x16, dim3(8, hidden / QK, p.n_tiles), dim3(256), 0, stream,
+                       static_cast<const _Float16*>(x), hidden, M, xg);
+  timing_begin(stream);   // the timed region is the fused kernel alone
   switch (p.cfg) {
+    case 'D': launch_cfg16<192>(p, wg, wu, wd, hidden, inter, x, M, P, xg, inter_scale, out_scale, stream); break;
     case 'A': launch_cfg<1, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
     case 'B': launch_cfg<2, 1, 640>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
     default: launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
