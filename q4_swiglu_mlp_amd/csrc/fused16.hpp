@@ -178,16 +178,138 @@ __device__ __forceinline__ void fu16_store_col(const X16Copy<C::NCOPY>& xc, _Flo
   }
 }
 
+// Scales of chunk CH (0..3) of a W_down block: sub-blocks 2*CH (low nibbles)
+// and 2*CH+1 (high), packed as (s, -1024*s) and (s, -64*s).
+struct PanelS {
+  half2v lo, hi;
+};
+
+template <int CH>
+__device__ __forceinline__ PanelS panel_scales(uint4 hdr) {
+  const SixBit sb = unpack_sixbit(hdr.y, hdr.z, hdr.w);
+  const uint32_t w = ((CH < 2) ? sb.sc03 : sb.sc47) >> (16 * (CH & 1));   // bytes sc_2CH, sc_2CH+1
+  const uint32_t v = (w & 0xFFu) | ((w & 0xFF00u) << 8);
+  const half2v d2 = splat_lo(hdr.x);
+  const half2v sp = __builtin_elementwise_fma(bits_h2(v | 0x64006400u), d2,
+                                              d2 * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f});
+  PanelS r;
+  r.lo = half2v{sp[0], sp[0]} * half2v{(_Float16)1.0f, (_Float16)-1024.0f};
+  r.hi = half2v{sp[1], sp[1]} * half2v{(_Float16)1.0f, (_Float16)-64.0f};
+  return r;
+}
+
+// Phase 2 of the 64-token unit: the down projection of the chunk [r0, r1) for
+// all hidden output rows, from the strip in LDS.  The same contraction as
+// fu_phase2 (32x32x16 MFMAs, one decoded W_down operand for both 32-token
+// halves, the min correction against the strip's 32-row means), with the
+// strip as the A operand: a lane's sixteen accumulators of a token half are
+// then one output row n and the tokens 8q + 4(l/32) + {0..3}, so the fp16
+// partials leave in 8-byte stores from one base address per lane.
+// OFF = (r0 / 64) % 4.
+template <class C, int ICMAX, int OFF>
+__device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int H, int I, int chunk, int r0, int r1,
+                                            int row0, const OutPartial& out, const _Float16* __restrict__ hs,
+                                            const _Float16* __restrict__ hsum, const NibbleK& nk) {
+  constexpr int HS = C::HS, HSS = C::HSS;
+  constexpr int NB = C::NBMAX;
+  constexpr int NP = ICMAX / 64;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int npan = (r1 - r0) / 64;
+  const int b0 = r0 >> 8;
+  const int nblk = ((r1 - 1) >> 8) - b0 + 1;         // W_down blocks the chunk touches
+  const size_t row_bytes = (size_t)(I / QK) * BLOCK_BYTES;
+  const int NT = H / 32;                             // output row tiles
+  const uint8_t* blk_base = wd + (size_t)l32 * row_bytes + (size_t)b0 * BLOCK_BYTES;   // row l32 of tile 0
+  // lane's partials: row n = 32 nt + l32, tokens row0 + 32 tt + 8 q + 4 h + {0..3},
+  // in the token-quad layout P[chunk][t / 4][n][t % 4] (a store instruction
+  // writes two runs of 32 rows x 8 bytes)
+  const size_t quad_stride = (size_t)H * 4;   // halves per token quad
+  _Float16* const pout = out.P + ((size_t)chunk * (out.Mpad / 4) + row0 / 4 + h) * quad_stride + (size_t)l32 * 4;
+  const float scale = out.scale;
+
+  auto down_tile = [&](DownTileData<NP, NB>& dt, int nt, const uint8_t* nxt) {
+    const uint8_t* nq = nxt + 16 + 16 * h;
+    float16v acc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tt][e] = 0.0f;
+    auto panel = [&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      if (P < NP && P < npan) {
+        const PanelS ps = panel_scales<(P + OFF) & 3>(dt.hdr[(P + OFF) >> 2]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const half8 b = dequant_dword_sc(dword_of(dt.qs[P], s), ps.lo, ps.hi, nk);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const half8 a = *reinterpret_cast<const half8*>(hs + (tt * 32 + l32) * HS + P * 64 + (2 * s + h) * 8);
+            acc[tt] = mfma32(a, b, acc[tt]);
+          }
+        }
+        // panel used up: refill it with the next tile's bytes
+        dt.qs[P] = *reinterpret_cast<const uint4*>(nq + ((P + OFF) >> 2) * BLOCK_BYTES + 32 * ((P + OFF) & 3));
+      }
+    };
+    panel(std::integral_constant<int, 0>{});
+    if constexpr (NP > 1) panel(std::integral_constant<int, 1>{});
+    if constexpr (NP > 2) panel(std::integral_constant<int, 2>{});
+    static_assert(NP <= 3, "panels per chunk");
+    // min correction: lane half h covers block 2g + h (block-aligned strip means)
+#pragma unroll
+    for (int g = 0; g < (NB + 1) / 2; ++g) {
+      if (2 * g < nblk) {
+        uint4 hd = dt.hdr[2 * g];
+        if (2 * g + 1 < NB) {
+          if (h) hd = dt.hdr[2 * g + 1];   // zero header past the chunk's blocks -> zero operand
+        } else if (h) {
+          hd = make_uint4(0, 0, 0, 0);
+        }
+        const half8 b = block_neg_dm32(hd);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const half8 a = *reinterpret_cast<const half8*>(hsum + (tt * 32 + l32) * HSS + 16 * g + 8 * h);
+          acc[tt] = mfma32(a, b, acc[tt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+      if (k < nblk) dt.hdr[k] = *reinterpret_cast<const uint4*>(nxt + k * BLOCK_BYTES);
+    _Float16* po = pout + (size_t)nt * 32 * 4;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        half4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc[tt][4 * q + e] * scale);
+        *reinterpret_cast<half4*>(po + (size_t)(8 * tt + 2 * q) * quad_stride) = v;
+      }
+    }
+  };
+
+  // one rolling tile buffer: each panel's bytes and each header are refilled
+  // with the next tile's (nt + WAVES) as soon as they have been consumed
+  const size_t tile_step = (size_t)32 * row_bytes;
+  if (wave >= NT) return;   // wave-uniform: fewer output tiles than waves
+  DownTileData<NP, NB> d = load_down_tile<NP, NB, OFF>(blk_base + (size_t)wave * tile_step, nblk, npan, h);
+  for (int nt = wave; nt < NT; nt += C::WAVES) {
+    // refills read the next tile of this wave; after the last one, this tile
+    // again (in bounds, never used)
+    const int nn = (nt + C::WAVES < NT) ? nt + C::WAVES : nt;
+    down_tile(d, nt, blk_base + (size_t)nn * tile_step);
+  }
+}
+
 // One fused 64-token unit.  xcol = the tile's staged columns (k_stage_x16);
-// tok/wrow (LDS, 64 entries) map unit rows to tokens and output weights for
-// phase 2 and are visible to all threads before the call; row0 is the unit's
-// first output row handed to the output policy.
-template <int ICMAX, class Out>
+// row0 is the unit's first token row in the partial output.
+template <int ICMAX>
 __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
                                              const uint8_t* __restrict__ wd, int H, int I,
-                                             const _Float16* __restrict__ xcol, const int* __restrict__ tok,
-                                             const float* __restrict__ wrow, int chunk, int r0, int r1, int row0,
-                                             float inter_scale, const Out& out, Fused16Smem<ICMAX>& sm) {
+                                             const _Float16* __restrict__ xcol, int chunk, int r0, int r1, int row0,
+                                             float inter_scale, const OutPartial& out, Fused16Smem<ICMAX>& sm) {
   using C = Fused16Cfg<ICMAX>;
   constexpr int XS = C::XS, HS = C::HS, HSS = C::HSS, MT = C::MT;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -388,10 +510,10 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
 
   // ---------------- phase 2: down projection over this chunk ----------------
   switch (off) {
-    case 0: fu_phase2<C, 2, ICMAX, 0>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    case 1: fu_phase2<C, 2, ICMAX, 1>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    case 2: fu_phase2<C, 2, ICMAX, 2>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    default: fu_phase2<C, 2, ICMAX, 3>(wd, H, I, tok, wrow, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    case 0: fu16_phase2<C, ICMAX, 0>(wd, H, I, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    case 1: fu16_phase2<C, ICMAX, 1>(wd, H, I, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    case 2: fu16_phase2<C, ICMAX, 2>(wd, H, I, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    default: fu16_phase2<C, ICMAX, 3>(wd, H, I, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
   }
 }
 

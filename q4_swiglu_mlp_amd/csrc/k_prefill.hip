@@ -66,8 +66,6 @@ __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused
     const _Float16* __restrict__ xg, int M, _Float16* __restrict__ P, int Mpad, float inter_scale, float out_scale,
     int n_tiles, int n_chunks) {
   __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX> sm;
-  __shared__ int tok[64];
-  __shared__ float wrow[64];
   const int bid = blockIdx.x;
   const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
   const int tile = rem >> 3;
@@ -76,15 +74,10 @@ __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused
   const int npan = I / 64;
   const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
   const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
-  if (threadIdx.x < 64) {
-    const int t = tile * 64 + threadIdx.x;
-    tok[threadIdx.x] = (t < M) ? t : -1;
-    wrow[threadIdx.x] = 1.0f;
-  }
-  __syncthreads();
-  OutPartial out{P, Mpad, H, out_scale};
+  (void)M;   // padding tokens of the last tile are zero in the staged activation
+  const OutPartial out{P, Mpad, H, out_scale};
   const _Float16* xcol = xg + (size_t)tile * (H / QK) * X16_COL;
-  fused_unit16<ICMAX>(wg, wu, wd, H, I, xcol, tok, wrow, chunk, r0, r1, tile * 64, inter_scale, out, sm);
+  fused_unit16<ICMAX>(wg, wu, wd, H, I, xcol, chunk, r0, r1, tile * 64, inter_scale, out, sm);
 }
 
 template <int CTRL>
@@ -182,6 +175,45 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const _Float16* __restr
   }
 }
 
+// y[t][n] = fp16(sum_c P[c][t / 4][n][t % 4]) for the token-quad partial
+// layout of the 64-token unit.  Thread (np, tq) sums one 16-byte piece (rows
+// 2np, 2np+1 x tokens 4tq..4tq+3) over all chunks in fp32, four chunks' loads
+// in flight at a time, and writes four 4-byte pieces of y; consecutive threads
+// take consecutive row pairs, so loads and stores are contiguous runs.
+__global__ __launch_bounds__(256) void k_reduce_quads(const _Float16* __restrict__ P, int S, int H, int Mpad,
+                                                     _Float16* __restrict__ y, int M) {
+  const int np = blockIdx.x * 32 + (threadIdx.x & 31);   // row pair
+  const int tq = blockIdx.y * 8 + (threadIdx.x >> 5);    // token quad
+  const size_t plane = (size_t)(Mpad / 4) * H * 4;       // halves per chunk
+  const _Float16* base = P + ((size_t)tq * H + 2 * np) * 4;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  auto add = [&](const uint4& v) {
+    const half8 hv = __builtin_bit_cast(half8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (float)hv[e];
+  };
+  int c = 0;
+  for (; c + 4 <= S; c += 4) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(base + (c + u) * plane);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add(v[u]);
+  }
+  for (; c < S; ++c) add(*reinterpret_cast<const uint4*>(base + c * plane));
+  // acc[4j + e]: row 2np + j, token 4tq + e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = 4 * tq + e;
+    if (t < M) {
+      const half2v v = {(_Float16)acc[e], (_Float16)acc[4 + e]};
+      *reinterpret_cast<half2v*>(y + (size_t)t * H + 2 * np) = v;
+    }
+  }
+}
+
 struct Plan {
   char cfg;      // 'A' .. 'D'
   int MT, ICMAX;
@@ -272,8 +304,12 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
     default: launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
   }
   timing_end(stream);
-  hipLaunchKernelGGL(k_reduce_partials, dim3(hidden / 64, p.Mpad / 64), dim3(256), 0, stream, P, p.n_chunks, hidden,
-                     p.Mpad, static_cast<_Float16*>(y), M);
+  if (p.cfg == 'D')
+    hipLaunchKernelGGL(k_reduce_quads, dim3(hidden / 64, p.Mpad / 32), dim3(256), 0, stream, P, p.n_chunks, hidden,
+                       p.Mpad, static_cast<_Float16*>(y), M);
+  else
+    hipLaunchKernelGGL(k_reduce_partials, dim3(hidden / 64, p.Mpad / 64), dim3(256), 0, stream, P, p.n_chunks,
+                       hidden, p.Mpad, static_cast<_Float16*>(y), M);
   return hipGetLastError();
 }
 
