@@ -23,11 +23,12 @@
 // loads the 16-byte header and the quant runs [16o, +16) and [64+16o, +16);
 // MFMA i (0..7) takes dword i%4 of the first run (i < 4) or of the second, whose
 // eight slots are weights {0,2,1,3,32,34,33,35} + 64c + 16(o%2) + 4(i%4) of the
-// block (c = o/2, or 2 + o/2).  The activation is staged once per call by
-// k_stage_x16 in exactly that order, with the 32-element means the -dmin*m
-// term is contracted against (one MFMA per four blocks, lane octet o supplying
-// block 4g+o's eight -32*dmin*m values), so a unit copies its columns into LDS
-// with plain 16-byte moves.
+// block (c = o/2, or 2 + o/2).  The activation is staged once per call, per
+// token, by k_stage_x16 in exactly that order, with the 32-element means the
+// -dmin*m term is contracted against (one MFMA per four blocks, lane octet o
+// supplying block 4g+o's eight -32*dmin*m values), so a unit copies the rows
+// of its 64 tokens into LDS with plain 16-byte moves: a contiguous token range
+// for the dense prefill, the routed rows of one expert for the MoE.
 #pragma once
 
 #include <type_traits>
@@ -45,14 +46,15 @@ __device__ __forceinline__ f32x4_16 mfma16x16(half8 a, half8 b, f32x4_16 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Staged activation, per (64-token tile, block column): 64 token rows of
-// X16_ROW halves (32 operand pieces of eight fp16, then one piece of padding
-// that staggers the LDS banks of consecutive tokens), then 64 pieces of
-// 32-means (token t's eight sub-block means, sb_slot order).
-constexpr int X16_ROW = QK + 8;
-constexpr int X16_XPIECES = 64 * (X16_ROW / 8);   // 2112
-constexpr int X16_PIECES = X16_XPIECES + 64;      // 2176 = 34 waves of 16-byte pieces
-constexpr int X16_COL = X16_PIECES * 8;           // halves per column
+// Staged activation, per token and block column, X16_TP pieces of eight fp16:
+// the 32 operand pieces, one piece of padding (in LDS it staggers the banks
+// of consecutive tokens), then the token's eight 32-element means (sb_slot
+// order).  Layout [token][column][piece]; one extra all-zero token (index M)
+// stands in for the padding rows of a tile.
+constexpr int X16_ROW = QK + 8;           // halves per token row in LDS
+constexpr int X16_TP = X16_ROW / 8 + 1;   // pieces per token and column: 34
+constexpr int X16_PIECES = 64 * X16_TP;   // pieces per 64-token column: 2176
+constexpr int X16_TP_BYTES = X16_TP * 16; // bytes per token and column
 
 // Operand slot of the eight activations 64c + 4j + {0..3} and 64c + 32 + 4j +
 // {0..3} of a block: MFMA i = 4(c/2) + j%4, octet o = 2(c%2) + j/4.
@@ -139,44 +141,111 @@ __device__ __forceinline__ NibbleK nibble_consts_s() {
   return k;
 }
 
-// One staged column in flight: NCOPY 16-byte pieces per thread.  Waves past
-// the column's 34 waves of pieces re-read piece 0 (in bounds, never stored),
-// so no branch surrounds a load.
+// Copy plan of one thread: NCOPY 16-byte pieces per column, piece p = the
+// thread's slot = (token row t = p / 34, piece j = p % 34).  src = byte offset
+// of the piece in column 0 of the staged activation, dst = its offset (halves)
+// in the LDS row area (j < 33), in the means area (j = 33) or in the junk
+// area (slots past the column's pieces, which re-read token 0's piece 0).
+template <int N>
+struct X16Plan {
+  uint32_t src[N];
+  uint32_t dst[N];
+  uint32_t kind[N];   // 0: x row area, 1: means, 2: junk
+};
+
+template <class C>
+__device__ __forceinline__ X16Plan<C::NCOPY> fu16_plan(const int* __restrict__ tok, int nbH) {
+  X16Plan<C::NCOPY> pl;
+#pragma unroll
+  for (int it = 0; it < C::NCOPY; ++it) {
+    const int p = (int)threadIdx.x + C::THREADS * it;
+    const int t = p / X16_TP, j = p - t * X16_TP;
+    const bool in = p < X16_PIECES;
+    pl.src[it] = in ? ((uint32_t)tok[t] * nbH * X16_TP + j) * 16u : 0u;
+    pl.kind[it] = !in ? 2u : (j < X16_TP - 1) ? 0u : 1u;
+    pl.dst[it] = !in ? (uint32_t)(p - X16_PIECES) * 8u : (j < X16_TP - 1) ? (uint32_t)(t * X16_ROW + j * 8) : (uint32_t)(t * 8);
+  }
+  return pl;
+}
+
+// One staged column in flight.  No branch surrounds a load (a load whose only
+// use sits behind one is sunk to it by the compiler, with a full wait).
 template <int N>
 struct X16Copy {
   u32x4_16 v[N];
 };
 
 template <class C>
-__device__ __forceinline__ X16Copy<C::NCOPY> fu16_load_col(const _Float16* __restrict__ col) {
+__device__ __forceinline__ X16Copy<C::NCOPY> fu16_load_col(const uint8_t* __restrict__ xtok, int kb,
+                                                           const X16Plan<C::NCOPY>& pl) {
   X16Copy<C::NCOPY> r;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint8_t* col = xtok + (size_t)kb * X16_TP_BYTES;
 #pragma unroll
-  for (int it = 0; it < C::NCOPY; ++it) {
-    const bool wave_in = wv * 64 + C::THREADS * it < X16_PIECES;   // uniform
-    const int p = wave_in ? (int)threadIdx.x + C::THREADS * it : 0;
-    r.v[it] = *reinterpret_cast<const u32x4_16*>(col + 8 * p);
-  }
+  for (int it = 0; it < C::NCOPY; ++it) r.v[it] = *reinterpret_cast<const u32x4_16*>(col + pl.src[it]);
   return r;
 }
 
-// Every copy slot stores (no branch: a load whose only use sits behind one is
-// sunk to it by the compiler, with a full wait); slots past the column's
-// pieces land in a junk area.
 template <class C>
-__device__ __forceinline__ void fu16_store_col(const X16Copy<C::NCOPY>& xc, _Float16* __restrict__ xs,
-                                               _Float16* __restrict__ xm, _Float16* __restrict__ junk) {
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void fu16_store_col(const X16Copy<C::NCOPY>& xc, const X16Plan<C::NCOPY>& pl,
+                                               _Float16* __restrict__ xs, _Float16* __restrict__ xm,
+                                               _Float16* __restrict__ junk) {
 #pragma unroll
   for (int it = 0; it < C::NCOPY; ++it) {
-    const int p = (int)threadIdx.x + C::THREADS * it;
-    const int w0 = wv * 64 + C::THREADS * it;   // the wave's first piece: whole waves share a destination
-    _Float16* dst = (w0 < X16_XPIECES) ? xs + 8 * p
-                    : (w0 < X16_PIECES) ? xm + 8 * (p - X16_XPIECES)
-                                        : junk + 8 * (p - X16_PIECES);
-    *reinterpret_cast<u32x4_16*>(dst) = xc.v[it];
+    _Float16* base = (pl.kind[it] == 0u) ? xs : (pl.kind[it] == 1u) ? xm : junk;
+    *reinterpret_cast<u32x4_16*>(base + pl.dst[it]) = xc.v[it];
   }
 }
+
+namespace {
+
+template <int CTRL>
+__device__ __forceinline__ float x16_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// The staged activation: for tokens 0..M (token M all zero) and every block
+// column, the 34 pieces described at X16_TP.  Grid ((M + 8) / 8, H / 256),
+// 256 threads = 8 tokens x 32 pieces; piece (c, j) of a token is
+// x[64c + 4j + {0..3}] and x[64c + 32 + 4j + {0..3}] of the column.
+__global__ __launch_bounds__(256) void k_stage_x16(const _Float16* __restrict__ x, int H, int M,
+                                                   uint8_t* __restrict__ xtok) {
+  const int kb = blockIdx.y, nbH = H / QK;
+  const int token = blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (token > M) return;   // whole 32-lane groups (the DPP sums below stay within one)
+  const int p = threadIdx.x & 31, c = p >> 3, j = p & 7;
+  _Float16* col = reinterpret_cast<_Float16*>(xtok + ((size_t)token * nbH + kb) * X16_TP_BYTES);
+  uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
+  if (token < M) {
+    const _Float16* src = x + (size_t)token * H + (size_t)kb * QK + 64 * c + 4 * j;
+    lo = *reinterpret_cast<const uint2*>(src);
+    hi = *reinterpret_cast<const uint2*>(src + 32);
+  }
+  // slot order {0,2,1,3} within each group of four
+  const uint32_t l0 = (lo.x & 0xFFFFu) | (lo.y << 16), l1 = (lo.x >> 16) | (lo.y & 0xFFFF0000u);
+  const uint32_t h0 = (hi.x & 0xFFFFu) | (hi.y << 16), h1 = (hi.x >> 16) | (hi.y & 0xFFFF0000u);
+  *reinterpret_cast<uint4*>(col + 8 * x16_slot(c, j)) = make_uint4(l0, l1, h0, h1);
+  if (p == 0) *reinterpret_cast<uint4*>(col + QK) = make_uint4(0, 0, 0, 0);
+  // 32-means: the eight pieces of one (token, chunk) are eight consecutive
+  // lanes; quad sums, then row_shr:4 leaves all eight in lane j == 4
+  const half4 lv = __builtin_bit_cast(half4, lo), hv = __builtin_bit_cast(half4, hi);
+  float sl = ((float)lv[0] + (float)lv[1]) + ((float)lv[2] + (float)lv[3]);
+  float sh = ((float)hv[0] + (float)hv[1]) + ((float)hv[2] + (float)hv[3]);
+  sl += x16_dpp<0xB1>(sl);
+  sh += x16_dpp<0xB1>(sh);
+  sl += x16_dpp<0x4E>(sl);
+  sh += x16_dpp<0x4E>(sh);
+  sl += x16_dpp<0x114>(sl);
+  sh += x16_dpp<0x114>(sh);
+  if (j == 4) {
+    _Float16* m = col + X16_ROW;
+    m[sb_slot(2 * c)] = (_Float16)(sl * 0.03125f);
+    m[sb_slot(2 * c + 1)] = (_Float16)(sh * 0.03125f);
+  }
+}
+
+}  // namespace
+
+inline size_t x16_staged_bytes(int M, int H) { return (size_t)(M + 1) * (H / QK) * X16_TP_BYTES; }
 
 // Scales of chunk CH (0..3) of a W_down block: sub-blocks 2*CH (low nibbles)
 // and 2*CH+1 (high), packed as (s, -1024*s) and (s, -64*s).
@@ -198,17 +267,46 @@ __device__ __forceinline__ PanelS panel_scales(uint4 hdr) {
   return r;
 }
 
+// Output policies of phase 2.  store() receives the two 32-row accumulator
+// tiles of output rows n = 32 nt + (lane % 32): element 4q + e of tile tt
+// belongs to unit row 32 tt + 8 q + 4 (lane / 32) + e.
+//
+// Dense prefill: fp16 partials at the output scale in the token-quad layout
+// P[chunk][t / 4][n][t % 4], so each element group of four is one 8-byte store
+// and a store instruction writes two runs of 32 rows x 8 bytes.
+struct OutQuads {
+  _Float16* P;
+  int Mpad;
+  int H;
+  float scale;
+  int chunk;
+  int row0;   // the unit's first token
+  __device__ __forceinline__ void store(const float16v (&acc)[2], int nt, int l32, int h) const {
+    const size_t quad_stride = (size_t)H * 4;   // halves per token quad
+    _Float16* po = P + ((size_t)chunk * (Mpad / 4) + row0 / 4 + h) * quad_stride + (size_t)(nt * 32 + l32) * 4;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        half4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc[tt][4 * q + e] * scale);
+        *reinterpret_cast<half4*>(po + (size_t)(8 * tt + 2 * q) * quad_stride) = v;
+      }
+    }
+  }
+};
+
 // Phase 2 of the 64-token unit: the down projection of the chunk [r0, r1) for
 // all hidden output rows, from the strip in LDS.  The same contraction as
 // fu_phase2 (32x32x16 MFMAs, one decoded W_down operand for both 32-token
 // halves, the min correction against the strip's 32-row means), with the
 // strip as the A operand: a lane's sixteen accumulators of a token half are
-// then one output row n and the tokens 8q + 4(l/32) + {0..3}, so the fp16
-// partials leave in 8-byte stores from one base address per lane.
-// OFF = (r0 / 64) % 4.
-template <class C, int ICMAX, int OFF>
-__device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int H, int I, int chunk, int r0, int r1,
-                                            int row0, const OutPartial& out, const _Float16* __restrict__ hs,
+// then one output row n and the tokens 8q + 4(l/32) + {0..3}, which the
+// output policy stores.  OFF = (r0 / 64) % 4.
+template <class C, int ICMAX, int OFF, class Out>
+__device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int H, int I, int r0, int r1,
+                                            const Out& out, const _Float16* __restrict__ hs,
                                             const _Float16* __restrict__ hsum, const NibbleK& nk) {
   constexpr int HS = C::HS, HSS = C::HSS;
   constexpr int NB = C::NBMAX;
@@ -221,12 +319,6 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
   const size_t row_bytes = (size_t)(I / QK) * BLOCK_BYTES;
   const int NT = H / 32;                             // output row tiles
   const uint8_t* blk_base = wd + (size_t)l32 * row_bytes + (size_t)b0 * BLOCK_BYTES;   // row l32 of tile 0
-  // lane's partials: row n = 32 nt + l32, tokens row0 + 32 tt + 8 q + 4 h + {0..3},
-  // in the token-quad layout P[chunk][t / 4][n][t % 4] (a store instruction
-  // writes two runs of 32 rows x 8 bytes)
-  const size_t quad_stride = (size_t)H * 4;   // halves per token quad
-  _Float16* const pout = out.P + ((size_t)chunk * (out.Mpad / 4) + row0 / 4 + h) * quad_stride + (size_t)l32 * 4;
-  const float scale = out.scale;
 
   auto down_tile = [&](DownTileData<NP, NB>& dt, int nt, const uint8_t* nxt) {
     const uint8_t* nq = nxt + 16 + 16 * h;
@@ -277,17 +369,7 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
 #pragma unroll
     for (int k = 0; k < NB; ++k)
       if (k < nblk) dt.hdr[k] = *reinterpret_cast<const uint4*>(nxt + k * BLOCK_BYTES);
-    _Float16* po = pout + (size_t)nt * 32 * 4;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        half4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc[tt][4 * q + e] * scale);
-        *reinterpret_cast<half4*>(po + (size_t)(8 * tt + 2 * q) * quad_stride) = v;
-      }
-    }
+    out.store(acc, nt, l32, h);
   };
 
   // one rolling tile buffer: each panel's bytes and each header are refilled
@@ -303,13 +385,15 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
   }
 }
 
-// One fused 64-token unit.  xcol = the tile's staged columns (k_stage_x16);
-// row0 is the unit's first token row in the partial output.
-template <int ICMAX>
+// One fused 64-token unit.  xtok = the staged activation (k_stage_x16); tok =
+// the unit's 64 token indices (LDS, visible to all threads before the call;
+// the zero token M for padding rows); out = the phase-2 output policy.
+template <int ICMAX, class Out>
 __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
                                              const uint8_t* __restrict__ wd, int H, int I,
-                                             const _Float16* __restrict__ xcol, int chunk, int r0, int r1, int row0,
-                                             float inter_scale, const OutPartial& out, Fused16Smem<ICMAX>& sm) {
+                                             const uint8_t* __restrict__ xtok, const int* __restrict__ tok,
+                                             int r0, int r1, float inter_scale, const Out& out,
+                                             Fused16Smem<ICMAX>& sm) {
   using C = Fused16Cfg<ICMAX>;
   constexpr int XS = C::XS, HS = C::HS, HSS = C::HSS, MT = C::MT;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -338,13 +422,14 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
     for (int e = 0; e < 4; ++e) accg[g][e] = accu[g][e] = 0.0f;
 
   // prologue: columns 0 and 1 staged
+  const X16Plan<C::NCOPY> xplan = fu16_plan<C>(tok, nbH);
   {
-    const X16Copy<C::NCOPY> x0 = fu16_load_col<C>(xcol);
+    const X16Copy<C::NCOPY> x0 = fu16_load_col<C>(xtok, 0, xplan);
     const int c1 = nbH > 1 ? 1 : 0;
-    const X16Copy<C::NCOPY> x1 = fu16_load_col<C>(xcol + (size_t)c1 * X16_COL);
+    const X16Copy<C::NCOPY> x1 = fu16_load_col<C>(xtok, c1, xplan);
     lds_barrier();   // ring zeroed before the means land in it
-    fu16_store_col<C>(x0, sm.u.xs[0], sm.xm[0], sm.junk);
-    fu16_store_col<C>(x1, sm.u.xs[1], sm.xm[c1], sm.junk);
+    fu16_store_col<C>(x0, xplan, sm.u.xs[0], sm.xm[0], sm.junk);
+    fu16_store_col<C>(x1, xplan, sm.u.xs[1], sm.xm[c1], sm.junk);
   }
 
   // The column loop, once for waves with a row tile (ACT) and once for idle
@@ -378,7 +463,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
       const int kx = (kb + 2 < nbH) ? kb + 2 : nbH - 1;
       const uint32_t noff = wrow_off + (uint32_t)kn * BLOCK_BYTES;
       if ((kb & 1) == 0) lds_barrier();
-      const X16Copy<C::NCOPY> xc = fu16_load_col<C>(xcol + (size_t)kx * X16_COL);
+      const X16Copy<C::NCOPY> xc = fu16_load_col<C>(xtok, kx, xplan);
       _Float16* const xs_next = sm.u.xs[(kb + 2) & 3];
       _Float16* const xm_next = sm.xm[kx & (C::XRING - 1)];
       if constexpr (ACT) {
@@ -422,7 +507,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
             // released that slot, and the ring slot written is none of the
             // four the corrections of blocks up to kb+1 read (past the end a
             // rewrite of data nobody reads again, or of the same values)
-            fu16_store_col<C>(xc, xs_next, xm_next, sm.junk);
+            fu16_store_col<C>(xc, xplan, xs_next, xm_next, sm.junk);
             __builtin_amdgcn_sched_barrier(0);
           }
           if (i == 6) {   // and the second
@@ -466,7 +551,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
           cu = u32x4_16{0u, 0u, 0u, 0u};
         }
       } else {
-        fu16_store_col<C>(xc, xs_next, xm_next, sm.junk);
+        fu16_store_col<C>(xc, xplan, xs_next, xm_next, sm.junk);
       }
     }
   };
@@ -510,10 +595,10 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
 
   // ---------------- phase 2: down projection over this chunk ----------------
   switch (off) {
-    case 0: fu16_phase2<C, ICMAX, 0>(wd, H, I, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    case 1: fu16_phase2<C, ICMAX, 1>(wd, H, I, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    case 2: fu16_phase2<C, ICMAX, 2>(wd, H, I, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    default: fu16_phase2<C, ICMAX, 3>(wd, H, I, chunk, r0, r1, row0, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    case 0: fu16_phase2<C, ICMAX, 0>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    case 1: fu16_phase2<C, ICMAX, 1>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    case 2: fu16_phase2<C, ICMAX, 2>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    default: fu16_phase2<C, ICMAX, 3>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
   }
 }
 

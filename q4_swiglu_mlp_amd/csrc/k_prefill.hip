@@ -63,9 +63,10 @@ __global__ __launch_bounds__(64 * FuWaves<TT>::value) void k_prefill_fused(const
 template <int ICMAX>
 __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused16(
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, const uint8_t* __restrict__ wd, int H, int I,
-    const _Float16* __restrict__ xg, int M, _Float16* __restrict__ P, int Mpad, float inter_scale, float out_scale,
+    const uint8_t* __restrict__ xg, int M, _Float16* __restrict__ P, int Mpad, float inter_scale, float out_scale,
     int n_tiles, int n_chunks) {
   __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX> sm;
+  __shared__ int tok[64];
   const int bid = blockIdx.x;
   const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
   const int tile = rem >> 3;
@@ -74,55 +75,10 @@ __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused
   const int npan = I / 64;
   const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
   const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
-  (void)M;   // padding tokens of the last tile are zero in the staged activation
-  const OutPartial out{P, Mpad, H, out_scale};
-  const _Float16* xcol = xg + (size_t)tile * (H / QK) * X16_COL;
-  fused_unit16<ICMAX>(wg, wu, wd, H, I, xcol, chunk, r0, r1, tile * 64, inter_scale, out, sm);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_add_src(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-// The activation of every 64-token tile in the 64-token unit's operand order
-// (X16_* layout of fused16.hpp), with its 32-element means; tokens past M are
-// zero.  Grid (8, H/256, n_tiles), 256 threads = 8 tokens x 32 pieces: piece
-// (c, j) of a token is x[64c + 4j + {0..3}] and x[64c + 32 + 4j + {0..3}].
-__global__ __launch_bounds__(256) void k_stage_x16(const _Float16* __restrict__ x, int H, int M,
-                                                   _Float16* __restrict__ xg) {
-  const int kb = blockIdx.y, tile = blockIdx.z;
-  const int t = blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int p = threadIdx.x & 31, c = p >> 3, j = p & 7;
-  const int token = tile * 64 + t;
-  _Float16* col = xg + ((size_t)tile * (H / QK) + kb) * X16_COL;
-  uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
-  if (token < M) {
-    const _Float16* src = x + (size_t)token * H + (size_t)kb * QK + 64 * c + 4 * j;
-    lo = *reinterpret_cast<const uint2*>(src);
-    hi = *reinterpret_cast<const uint2*>(src + 32);
-  }
-  // slot order {0,2,1,3} within each group of four
-  const uint32_t l0 = (lo.x & 0xFFFFu) | (lo.y << 16), l1 = (lo.x >> 16) | (lo.y & 0xFFFF0000u);
-  const uint32_t h0 = (hi.x & 0xFFFFu) | (hi.y << 16), h1 = (hi.x >> 16) | (hi.y & 0xFFFF0000u);
-  *reinterpret_cast<uint4*>(col + t * X16_ROW + 8 * x16_slot(c, j)) = make_uint4(l0, l1, h0, h1);
-  if (p == 0) *reinterpret_cast<uint4*>(col + t * X16_ROW + QK) = make_uint4(0, 0, 0, 0);
-  // 32-means: the eight pieces of one (token, chunk) are eight consecutive
-  // lanes; quad sums, then row_shr:4 leaves all eight in lane j == 4
-  const half4 lv = __builtin_bit_cast(half4, lo), hv = __builtin_bit_cast(half4, hi);
-  float sl = ((float)lv[0] + (float)lv[1]) + ((float)lv[2] + (float)lv[3]);
-  float sh = ((float)hv[0] + (float)hv[1]) + ((float)hv[2] + (float)hv[3]);
-  sl += dpp_add_src<0xB1>(sl);
-  sh += dpp_add_src<0xB1>(sh);
-  sl += dpp_add_src<0x4E>(sl);
-  sh += dpp_add_src<0x4E>(sh);
-  sl += dpp_add_src<0x114>(sl);
-  sh += dpp_add_src<0x114>(sh);
-  if (j == 4) {
-    _Float16* m = col + X16_XPIECES * 8 + t * 8;
-    m[sb_slot(2 * c)] = (_Float16)(sl * 0.03125f);
-    m[sb_slot(2 * c + 1)] = (_Float16)(sh * 0.03125f);
-  }
+  if (threadIdx.x < 64) tok[threadIdx.x] = min(tile * 64 + (int)threadIdx.x, M);   // M: the zero token
+  __syncthreads();
+  const OutQuads out{P, Mpad, H, out_scale, chunk, tile * 64};
+  fused_unit16<ICMAX>(wg, wu, wd, H, I, xg, tok, r0, r1, inter_scale, out, sm);
 }
 
 // y[t][n] = fp16(sum_c P[c][n][t]) through a 64x64 LDS transpose.  Thread
@@ -264,7 +220,7 @@ void launch_cfg(const Plan& p, const void* wg, const void* wu, const void* wd, i
 
 template <int ICMAX>
 void launch_cfg16(const Plan& p, const void* wg, const void* wu, const void* wd, int H, int I, const void* x, int M,
-                  _Float16* P, _Float16* xg, float inter_scale, float out_scale, hipStream_t stream) {
+                  _Float16* P, uint8_t* xg, float inter_scale, float out_scale, hipStream_t stream) {
   (void)x;
   const int n_groups = (p.n_chunks + 7) / 8;
   hipLaunchKernelGGL((k_prefill_fused16<ICMAX>), dim3(n_groups * 8 * p.n_tiles), dim3(Fused16Cfg<ICMAX>::THREADS), 0,
@@ -276,7 +232,7 @@ void launch_cfg16(const Plan& p, const void* wg, const void* wu, const void* wd,
 size_t partial_bytes(const Plan& p, int H) { return ((size_t)p.n_chunks * H * p.Mpad * sizeof(_Float16) + 255) & ~(size_t)255; }
 
 size_t staged_x_bytes(const Plan& p, int H) {
-  return (p.cfg == 'D') ? (size_t)p.n_tiles * (H / QK) * X16_COL * sizeof(_Float16) : 0;
+  return (p.cfg == 'D') ? x16_staged_bytes(p.n_tiles * p.MT, H) : 0;
 }
 
 }  // namespace
@@ -292,9 +248,9 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
   _Float16* P = static_cast<_Float16*>(ws);
   const float inter_scale = ldexpf(1.0f, -inter_shift);
   const float out_scale = ldexpf(1.0f, inter_shift - out_shift);
-  _Float16* xg = reinterpret_cast<_Float16*>(static_cast<char*>(ws) + partial_bytes(p, hidden));
+  uint8_t* xg = static_cast<uint8_t*>(ws) + partial_bytes(p, hidden);
   if (p.cfg == 'D')
-    hipLaunchKernelGGL(k_stage_x16, dim3(8, hidden / QK, p.n_tiles), dim3(256), 0, stream,
+    hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream,
                        static_cast<const _Float16*>(x), hidden, M, xg);
   timing_begin(stream);   // the timed region is the fused kernel alone
   switch (p.cfg) {
