@@ -134,7 +134,8 @@ int zinc_mlp_q4k_decode(const void* w_gate, const void* w_up, const void* w_down
  * A slot whose id is outside [0, n_experts) contributes nothing; the kernel
  * then ORs 1 into *dev_error (a device int32, may be NULL) -- the flag is
  * sticky and the caller clears it.  Duplicate ids within a token each count.
- * 1 <= top_k <= n_experts <= 1024; M * top_k <= 2^24.
+ * 1 <= top_k <= n_experts <= 1024; M * top_k <= 2^24 and (M * top_k + 1) * hidden * 2 < 2^31
+ * (else ZINC_ERR_ARG, and the workspace size query returns 0).
  */
 size_t zinc_moe_q4k_experts_workspace_size(int32_t M, int32_t top_k, int32_t n_experts,
                                            int32_t hidden, int32_t inter);

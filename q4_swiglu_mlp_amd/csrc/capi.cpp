@@ -23,6 +23,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool dim_ok(int32_t v, int32_t max) { return v > 0 && v % 256 == 0 && v <= max; }
 
+// The MoE partial rows of one intermediate chunk, (M*top_k + 1) x hidden fp16,
+// are addressed with 32-bit byte offsets: they must stay below 2 GiB.
+bool moe_rows_ok(int32_t M, int32_t top_k, int32_t hidden) {
+  return ((long long)M * top_k + 1) * hidden * 2 <= 0x7FFFFFFFLL;
+}
+
 thread_local const char* t_last_hip_error = "no HIP error";
 
 int from_hip(hipError_t e) {
@@ -116,6 +122,7 @@ size_t zinc_moe_q4k_experts_workspace_size(int32_t M, int32_t top_k, int32_t n_e
   if (M < 0 || n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > n_experts) return 0;
   if ((long long)M * top_k > kMaxMoeSlots) return 0;
   if (!dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
+  if (!moe_rows_ok(M, top_k, hidden)) return 0;
   return zinc::moe_workspace_bytes(M, top_k, n_experts, hidden, inter);
 }
 
@@ -131,6 +138,7 @@ int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_dow
     return ZINC_ERR_ALIGN;
   if (n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > n_experts) return ZINC_ERR_ARG;
   if (M < 0 || (long long)M * top_k > kMaxMoeSlots) return ZINC_ERR_ARG;
+  if (!moe_rows_ok(M, top_k, hidden)) return ZINC_ERR_ARG;
   if (inter_shift < 0 || inter_shift > kMaxShift || out_shift < 0 || out_shift > kMaxShift) return ZINC_ERR_ARG;
   if (M == 0) return ZINC_OK;
   if (!workspace) return ZINC_ERR_NULL;

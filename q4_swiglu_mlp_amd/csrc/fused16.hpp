@@ -267,9 +267,9 @@ __device__ __forceinline__ PanelS panel_scales(uint4 hdr) {
   return r;
 }
 
-// Output policies of phase 2.  store() receives the two 32-row accumulator
-// tiles of output rows n = 32 nt + (lane % 32): element 4q + e of tile tt
-// belongs to unit row 32 tt + 8 q + 4 (lane / 32) + e.
+// Output policies of phase 2.  store<NTT>() receives the 32-row accumulator
+// tiles (NTT of them hold rows) of output rows n = 32 nt + (lane % 32):
+// element 4q + e of tile tt belongs to unit row 32 tt + 8 q + 4 (lane / 32) + e.
 //
 // Dense prefill: fp16 partials at the output scale in the token-quad layout
 // P[chunk][t / 4][n][t % 4], so each element group of four is one 8-byte store
@@ -281,11 +281,12 @@ struct OutQuads {
   float scale;
   int chunk;
   int row0;   // the unit's first token
+  template <int NTT>
   __device__ __forceinline__ void store(const float16v (&acc)[2], int nt, int l32, int h) const {
     const size_t quad_stride = (size_t)H * 4;   // halves per token quad
     _Float16* po = P + ((size_t)chunk * (Mpad / 4) + row0 / 4 + h) * quad_stride + (size_t)(nt * 32 + l32) * 4;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < NTT; ++tt) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         half4 v;
@@ -304,7 +305,7 @@ struct OutQuads {
 // strip as the A operand: a lane's sixteen accumulators of a token half are
 // then one output row n and the tokens 8q + 4(l/32) + {0..3}, which the
 // output policy stores.  OFF = (r0 / 64) % 4.
-template <class C, int ICMAX, int OFF, class Out>
+template <class C, int ICMAX, int OFF, int NTT, class Out>
 __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int H, int I, int r0, int r1,
                                             const Out& out, const _Float16* __restrict__ hs,
                                             const _Float16* __restrict__ hsum, const NibbleK& nk) {
@@ -335,7 +336,7 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
         for (int s = 0; s < 4; ++s) {
           const half8 b = dequant_dword_sc(dword_of(dt.qs[P], s), ps.lo, ps.hi, nk);
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
+          for (int tt = 0; tt < NTT; ++tt) {
             const half8 a = *reinterpret_cast<const half8*>(hs + (tt * 32 + l32) * HS + P * 64 + (2 * s + h) * 8);
             acc[tt] = mfma32(a, b, acc[tt]);
           }
@@ -360,7 +361,7 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
         }
         const half8 b = block_neg_dm32(hd);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < NTT; ++tt) {
           const half8 a = *reinterpret_cast<const half8*>(hsum + (tt * 32 + l32) * HSS + 16 * g + 8 * h);
           acc[tt] = mfma32(a, b, acc[tt]);
         }
@@ -369,30 +370,36 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
 #pragma unroll
     for (int k = 0; k < NB; ++k)
       if (k < nblk) dt.hdr[k] = *reinterpret_cast<const uint4*>(nxt + k * BLOCK_BYTES);
-    out.store(acc, nt, l32, h);
+    out.template store<NTT>(acc, nt, l32, h);
   };
 
-  // one rolling tile buffer: each panel's bytes and each header are refilled
-  // with the next tile's (nt + WAVES) as soon as they have been consumed
+  // two rolling tile buffers, so a wave's loads run two tiles ahead: each
+  // panel's bytes and each header are refilled with the tile after next
+  // (nt + 2 WAVES) as soon as they have been consumed
+  constexpr int W = C::WAVES;
   const size_t tile_step = (size_t)32 * row_bytes;
   if (wave >= NT) return;   // wave-uniform: fewer output tiles than waves
-  DownTileData<NP, NB> d = load_down_tile<NP, NB, OFF>(blk_base + (size_t)wave * tile_step, nblk, npan, h);
-  for (int nt = wave; nt < NT; nt += C::WAVES) {
-    // refills read the next tile of this wave; after the last one, this tile
-    // again (in bounds, never used)
-    const int nn = (nt + C::WAVES < NT) ? nt + C::WAVES : nt;
-    down_tile(d, nt, blk_base + (size_t)nn * tile_step);
+  // loads past the last tile re-read the last one (in bounds, never used)
+  auto clamp_tile = [&](int t) { return t < NT ? t : NT - 1; };
+  DownTileData<NP, NB> d0 = load_down_tile<NP, NB, OFF>(blk_base + (size_t)wave * tile_step, nblk, npan, h);
+  DownTileData<NP, NB> d1 =
+      load_down_tile<NP, NB, OFF>(blk_base + (size_t)clamp_tile(wave + W) * tile_step, nblk, npan, h);
+  for (int nt = wave; nt < NT; nt += 2 * W) {
+    down_tile(d0, nt, blk_base + (size_t)clamp_tile(nt + 2 * W) * tile_step);
+    if (nt + W < NT) down_tile(d1, nt + W, blk_base + (size_t)clamp_tile(nt + 3 * W) * tile_step);
   }
 }
 
 // One fused 64-token unit.  xtok = the staged activation (k_stage_x16); tok =
 // the unit's 64 token indices (LDS, visible to all threads before the call;
-// the zero token M for padding rows); out = the phase-2 output policy.
+// the zero token M for padding rows); rows = how many of them are real (1..64,
+// the rest are padding: 16-token groups and 32-token halves wholly past it
+// are skipped); out = the phase-2 output policy.
 template <int ICMAX, class Out>
 __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
                                              const uint8_t* __restrict__ wd, int H, int I,
                                              const uint8_t* __restrict__ xtok, const int* __restrict__ tok,
-                                             int r0, int r1, float inter_scale, const Out& out,
+                                             int rows, int r0, int r1, float inter_scale, const Out& out,
                                              Fused16Smem<ICMAX>& sm) {
   using C = Fused16Cfg<ICMAX>;
   constexpr int XS = C::XS, HS = C::HS, HSS = C::HSS, MT = C::MT;
@@ -442,8 +449,10 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   // Pipeline.  Within a block an active wave's MFMA steps are
   // software-pipelined: the B operands and the decoded A operands of step i+1
   // are fetched while step i's eight MFMAs run.
-  auto column_loop = [&](auto act_tag) {
+  auto column_loop = [&](auto act_tag, auto ng_tag) {
     constexpr bool ACT = decltype(act_tag)::value;
+    constexpr int NG = decltype(ng_tag)::value;   // 16-token groups holding rows
+    constexpr int VPM = (NG >= 3) ? 3 : (NG == 2) ? 5 : 9;   // decode VALU per MFMA slot
     u32x4_16 hg, hu, qg0, qu0, qg1, qu1;
     u32x4_16 cg = {0u, 0u, 0u, 0u}, cu = {0u, 0u, 0u, 0u};   // headers for the min correction
     if constexpr (ACT) {
@@ -480,7 +489,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
         const _Float16* xb = sm.u.xs[kb & 3] + xlane;
         auto load_b = [&](int i, half8 (&b)[4]) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const half8*>(xb + g * 16 * XS + i * 32);
+          for (int g = 0; g < NG; ++g) b[g] = *reinterpret_cast<const half8*>(xb + g * 16 * XS + i * 32);
         };
         auto decode = [&](int i, half8& ag, half8& au) {
           const uint32_t qg = (i < 4) ? qg0[i & 3] : qg1[i & 3];
@@ -516,23 +525,23 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
             __builtin_amdgcn_sched_barrier(0);
           }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
+          for (int g = 0; g < NG; ++g) {
             accg[g] = mfma16x16(agc, bc[g], accg[g]);
             accu[g] = mfma16x16(auc, bc[g], accu[g]);
           }
           if (i < 7) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) bc[g] = bn[g];
+            for (int g = 0; g < NG; ++g) bc[g] = bn[g];
             agc = agn;
             auc = aun;
           }
           // issue order of the step: the next B reads, then the MFMAs with
           // the next decode's VALU work threaded between them
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, NG, 0);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
+          for (int k = 0; k < 2 * NG; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
           }
         }
         // min correction once per four blocks (or at the last): octet o holds
@@ -542,7 +551,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
           const half8 dmg = block_neg_dm32(as_u4(cg)), dmu = block_neg_dm32(as_u4(cu));
           const _Float16* mb = sm.xm[((kb & ~3) + o) & (C::XRING - 1)] + r * 8;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
+          for (int g = 0; g < NG; ++g) {
             const half8 b = *reinterpret_cast<const half8*>(mb + g * 16 * 8);
             accg[g] = mfma16x16(dmg, b, accg[g]);
             accu[g] = mfma16x16(dmu, b, accu[g]);
@@ -555,10 +564,22 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
       }
     }
   };
-  if (act)
-    column_loop(std::true_type{});
+  // token groups past the unit's rows stay zero and are skipped
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  const int ng = (rows + 15) >> 4;   // uniform, 1..4
+  if (!act)
+    column_loop(std::false_type{}, I4{});
+  else if (ng >= 4)
+    column_loop(std::true_type{}, I4{});
+  else if (ng == 3)
+    column_loop(std::true_type{}, I3{});
+  else if (ng == 2)
+    column_loop(std::true_type{}, I2{});
   else
-    column_loop(std::false_type{});
+    column_loop(std::true_type{}, I1{});
   lds_barrier();   // the strip below overwrites the activation slots
 
   // SwiGLU in registers -> fp16 strip (panel order) and the 32-row sums.
@@ -594,12 +615,19 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   lds_barrier();
 
   // ---------------- phase 2: down projection over this chunk ----------------
-  switch (off) {
-    case 0: fu16_phase2<C, ICMAX, 0>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    case 1: fu16_phase2<C, ICMAX, 1>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    case 2: fu16_phase2<C, ICMAX, 2>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-    default: fu16_phase2<C, ICMAX, 3>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-  }
+  auto phase2 = [&](auto ntt_tag) {
+    constexpr int NTT = decltype(ntt_tag)::value;
+    switch (off) {
+      case 0: fu16_phase2<C, ICMAX, 0, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+      case 1: fu16_phase2<C, ICMAX, 1, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+      case 2: fu16_phase2<C, ICMAX, 2, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+      default: fu16_phase2<C, ICMAX, 3, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+    }
+  };
+  if (rows > 32)
+    phase2(I2{});
+  else
+    phase2(I1{});
 }
 
 }  // namespace zinc

@@ -9,14 +9,18 @@
 //   2. k_moe_plan     exclusive scan of the counts -> list offsets, and the tile
 //                     table (expert, first list entry, rows) of MT-slot tiles
 //   3. k_moe_scatter  slot indices grouped by expert, and each slot's position
-//   4. k_moe_fused    one fused unit per (tile, intermediate chunk); blocks past
-//                     the device-side tile count exit at once.  Each row's
-//                     expert output, times p[t,s], is stored (fp32) at the
-//                     row's list position: Q[chunk][position][hidden]
-//   5. k_moe_combine  y[t] = fp16(sum over chunks and the token's slots)
+//   4. k_stage_x16    the activation per token in the fused unit's operand
+//                     order (fused16.hpp), plus an all-zero token
+//   5. k_moe_fused16  one 64-token fused unit (fused16.hpp) per (tile of 64
+//                     routed rows of one expert, intermediate chunk); blocks
+//                     past the device-side tile count exit at once.  Each
+//                     row's expert output (fp16 at the output scale) is
+//                     stored at its slot: Q[chunk][slot][hidden]
+//   6. k_moe_combine  y[t] = fp16(sum over the token's slots of p[t,s] times
+//                     the sum over chunks), in fp32
 // No atomics: every partial has exactly one writer, and the combine order is
 // fixed, so the result is deterministic.
-#include "fused_core.hpp"
+#include "fused16.hpp"
 #include "launch.hpp"
 #include "util_kernels.hpp"
 
@@ -24,10 +28,9 @@ namespace zinc {
 
 namespace {
 
-constexpr int TT_MOE = 1;       // 32 (token, slot) rows per unit
-constexpr int RTW_MOE = 1;      // row tiles per wave per pass
-constexpr int ICMAX_MOE = 384;  // intermediate rows per chunk
-using MoeCfg = FusedCfg<TT_MOE, RTW_MOE, ICMAX_MOE>;
+constexpr int ICMAX_MOE = 192;  // intermediate rows per chunk (three 64-row panels)
+constexpr int MT_MOE = 64;      // routed rows per tile
+using MoeCfg = Fused16Cfg<ICMAX_MOE>;
 
 struct MoePlan {
   int* counts;       // [E]
@@ -39,14 +42,15 @@ struct MoePlan {
   int* n_tiles;      // [1]
   int* slots;        // [M * top_k] slot indices grouped by expert
   int* pos;          // [M * top_k] list position of each slot, -1 if its id is invalid
-  float* Q;          // [n_chunks][M * top_k][H]
+  _Float16* Q;       // [n_chunks][M * top_k + 1][H], fp16 at the output scale (last row: junk)
+  uint8_t* xtok;     // staged activation, x16_staged_bytes(M, H)
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 int max_tiles_for(int M, int top_k, int E) {
   const long long pairs = (long long)M * top_k;
-  return (int)((pairs + MoeCfg::MT - 1) / MoeCfg::MT + (pairs < E ? pairs : E));
+  return (int)((pairs + MT_MOE - 1) / MT_MOE + (pairs < E ? pairs : E));
 }
 
 int chunks_for(int I) {
@@ -70,7 +74,8 @@ MoePlan carve(void* ws, int M, int top_k, int E, int H, int I, size_t* total) {
   p.n_tiles = reinterpret_cast<int*>(take(sizeof(int)));
   p.slots = reinterpret_cast<int*>(take(sizeof(int) * pairs));
   p.pos = reinterpret_cast<int*>(take(sizeof(int) * pairs));
-  p.Q = reinterpret_cast<float*>(take(sizeof(float) * (size_t)chunks_for(I) * pairs * H));
+  p.Q = reinterpret_cast<_Float16*>(take(sizeof(_Float16) * (size_t)chunks_for(I) * (pairs + 1) * H));
+  p.xtok = reinterpret_cast<uint8_t*>(take(x16_staged_bytes(M, H)));
   if (total) *total = off;
   return p;
 }
@@ -87,38 +92,53 @@ __global__ __launch_bounds__(256) void k_moe_count(const int32_t* __restrict__ i
   }
 }
 
-// One block of 1024 threads; E <= 1024.
+// One block of 1024 threads; E <= 1024.  The tile table lists every expert's
+// full MT-row tiles first and the remainder tiles (fewer rows, cheaper units)
+// last, so the units launched first are the expensive ones and the cheap ones
+// fill in behind them.
 __global__ __launch_bounds__(1024) void k_moe_plan(const int* __restrict__ counts, int E, int* __restrict__ offsets,
                                                   int* __restrict__ tile_expert, int* __restrict__ tile_start,
                                                   int* __restrict__ tile_rows, int* __restrict__ n_tiles, int MT) {
   __shared__ int sc[1024];
-  __shared__ int st[1024];
+  __shared__ int sf[1024];
+  __shared__ int sr[1024];
   const int e = threadIdx.x;
   const int cnt = (e < E) ? counts[e] : 0;
-  const int nt = (cnt + MT - 1) / MT;
+  const int nf = cnt / MT;                 // full tiles
+  const int nr = (cnt % MT) ? 1 : 0;       // remainder tile
   sc[e] = cnt;
-  st[e] = nt;
+  sf[e] = nf;
+  sr[e] = nr;
   __syncthreads();
-  // inclusive Hillis-Steele scans of counts and tile counts
+  // inclusive Hillis-Steele scans of counts, full tiles and remainder tiles
   for (int d = 1; d < 1024; d <<= 1) {
     const int a = (e >= d) ? sc[e - d] : 0;
-    const int b = (e >= d) ? st[e - d] : 0;
+    const int b = (e >= d) ? sf[e - d] : 0;
+    const int c = (e >= d) ? sr[e - d] : 0;
     __syncthreads();
     sc[e] += a;
-    st[e] += b;
+    sf[e] += b;
+    sr[e] += c;
     __syncthreads();
   }
-  const int off = sc[e] - cnt;      // exclusive
-  const int tb = st[e] - nt;
+  const int off = sc[e] - cnt;   // exclusive
+  const int total_full = sf[1023];
   if (e < E) offsets[e] = off;
   if (e == E - 1) {
     offsets[E] = sc[e];
-    *n_tiles = st[e];
+    *n_tiles = total_full + sr[1023];
   }
-  for (int i = 0; i < nt; ++i) {
-    tile_expert[tb + i] = e;
-    tile_start[tb + i] = off + i * MT;
-    tile_rows[tb + i] = min(MT, cnt - i * MT);
+  const int tf = sf[e] - nf;
+  for (int i = 0; i < nf; ++i) {
+    tile_expert[tf + i] = e;
+    tile_start[tf + i] = off + i * MT;
+    tile_rows[tf + i] = MT;
+  }
+  if (nr) {
+    const int tr = total_full + sr[e] - 1;
+    tile_expert[tr] = e;
+    tile_start[tr] = off + nf * MT;
+    tile_rows[tr] = cnt - nf * MT;
   }
 }
 
@@ -137,48 +157,66 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__
   pos[i] = q;
 }
 
-// MoE output: row r of a unit is list position row0 + r; store w * v at Q[chunk][position][n].
-struct OutPairs {
-  float* Q;
+// MoE output of the 64-token unit: unit row r belongs to slot slot_of_row[r];
+// the fp16 partial, at the output scale, goes to Q[chunk][slot][n].  Padding
+// rows carry slot = pairs, a junk row after the chunk's pairs (no branch
+// around the stores).  Lanes run along n, so a store instruction writes two
+// runs of 32 rows x 2 bytes; its address is a 32-bit offset (row offsets read
+// once per unit) from the chunk's base.
+struct OutSlots {
+  _Float16* Q;
   size_t pairs;
   int H;
-  __device__ __forceinline__ void put(int chunk, int n, int position, int tok, float w, float v) const {
-    if (tok >= 0) Q[((size_t)chunk * pairs + position) * H + n] = w * v;
+  float scale;
+  int chunk;
+  const int* slot_of_row;   // LDS, 64 entries
+  template <int NTT>
+  __device__ __forceinline__ void store(const float16v (&acc)[2], int nt, int l32, int h) const {
+    const size_t rows_bytes = (pairs + 1) * (size_t)H * sizeof(_Float16);   // < 4 GiB (checked by the caller)
+    const __amdgpu_buffer_rsrc_t qc = __builtin_amdgcn_make_buffer_rsrc(Q + (size_t)chunk * (pairs + 1) * H, (short)0,
+                                                                       (int)rows_bytes, 0x00020000);
+    const uint32_t nb = (uint32_t)(nt * 32 + l32) * 2u;
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t row = (uint32_t)slot_of_row[32 * tt + 8 * q + 4 * h + e] * (uint32_t)H * 2u;
+          const _Float16 v = (_Float16)(acc[tt][4 * q + e] * scale);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, v), qc, row + nb, 0, 0);
+        }
+      }
+    }
   }
 };
 
-__global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
-                                                          const uint8_t* __restrict__ wd, int H, int I,
-                                                          const _Float16* __restrict__ x, const float* __restrict__ p,
-                                                          int top_k, const int* __restrict__ n_tiles,
-                                                          const int* __restrict__ tile_expert,
-                                                          const int* __restrict__ tile_start,
-                                                          const int* __restrict__ tile_rows,
-                                                          const int* __restrict__ slots, float* __restrict__ Q,
-                                                          int pairs, float inter_scale, int n_chunks) {
-  __shared__ __attribute__((aligned(16))) FusedSmem<TT_MOE, RTW_MOE, ICMAX_MOE> sm;
-  __shared__ int tok[MoeCfg::MT];
-  __shared__ float wrow[MoeCfg::MT];
+__global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
+    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, const uint8_t* __restrict__ wd, int H, int I,
+    int M, const uint8_t* __restrict__ xtok, int top_k, const int* __restrict__ n_tiles,
+    const int* __restrict__ tile_expert, const int* __restrict__ tile_start, const int* __restrict__ tile_rows,
+    const int* __restrict__ slots, _Float16* __restrict__ Q, int pairs, float inter_scale, float out_scale,
+    int n_chunks) {
+  __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX_MOE> sm;
+  __shared__ int tok[MT_MOE];
+  __shared__ int slot_of_row[MT_MOE];
 
-  // A tile's chunks have consecutive block ids and so spread over the XCDs
-  // (ids go round-robin over them); with n_chunks a multiple of 8, one chunk of
-  // every tile lands on the same XCD, whose L2 then serves that slice of an
-  // expert's weights to all of the expert's tiles.
+  // A tile's chunks have consecutive block ids and so go round-robin over the
+  // XCDs; the same chunk of an expert's consecutive tiles lands on the same
+  // pair of XCDs, whose L2s serve that slice of the expert's weights.
   const int ti = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x % n_chunks;
   if (ti >= *n_tiles) return;
   const int e = tile_expert[ti];
   const int start = tile_start[ti], rows = tile_rows[ti];
-  if (threadIdx.x < MoeCfg::MT) {
-    int t = -1;
-    float w = 0.0f;
+  if (threadIdx.x < MT_MOE) {
+    int t = M, sl = pairs;   // padding rows: the zero token, the junk row
     if ((int)threadIdx.x < rows) {
-      const int slot = slots[start + threadIdx.x];
-      t = slot / top_k;
-      w = p[slot];
+      sl = slots[start + threadIdx.x];
+      t = sl / top_k;
     }
     tok[threadIdx.x] = t;
-    wrow[threadIdx.x] = w;
+    slot_of_row[threadIdx.x] = sl;
   }
   __syncthreads();
   const int npan = I / 64;
@@ -186,31 +224,40 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused(const uint8_t* __
   const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
   const size_t gu_bytes = (size_t)I * (H / QK) * BLOCK_BYTES;   // one expert's gate (or up) matrix
   const size_t d_bytes = (size_t)H * (I / QK) * BLOCK_BYTES;    // one expert's down matrix
-  OutPairs out{Q, (size_t)pairs, H};
-  fused_unit<TT_MOE, RTW_MOE, ICMAX_MOE>(wg + e * gu_bytes, wu + e * gu_bytes, wd + e * d_bytes, H, I, x, tok, wrow,
-                                         chunk, r0, r1, start, inter_scale, out, sm);
+  const OutSlots out{Q, (size_t)pairs, H, out_scale, chunk, slot_of_row};
+  fused_unit16<ICMAX_MOE>(wg + e * gu_bytes, wu + e * gu_bytes, wd + e * d_bytes, H, I, xtok, tok, rows, r0, r1,
+                          inter_scale, out, sm);
 }
 
-// y[t][n] = fp16(scale * sum_c sum_s Q[c][pos[t*k+s]][n]); one block per token.
-__global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Q, const int* __restrict__ pos,
-                                                    int top_k, int n_chunks, int pairs, int H,
-                                                    _Float16* __restrict__ y, float scale) {
+// y[t][n] = fp16(sum_s p[t*k+s] * sum_c Q[c][t*k+s][n]) over the token's valid
+// slots; one block per token, eight outputs (one 16-byte load) per thread.
+__global__ __launch_bounds__(256) void k_moe_combine(const _Float16* __restrict__ Q, const int* __restrict__ pos,
+                                                    const float* __restrict__ p, int top_k, int n_chunks, int pairs,
+                                                    int H, _Float16* __restrict__ y) {
   const int t = blockIdx.x;
-  for (int n = threadIdx.x * 4; n < H; n += 256 * 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int n = threadIdx.x * 8; n < H; n += 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     for (int s = 0; s < top_k; ++s) {
-      const int q = pos[t * top_k + s];
-      if (q < 0) continue;
+      const int slot = t * top_k + s;
+      if (pos[slot] < 0) continue;   // invalid expert id: no contribution
+      float part[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[e] = 0.0f;
       for (int c = 0; c < n_chunks; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(Q + ((size_t)c * pairs + q) * H + n);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        const half8 v = *reinterpret_cast<const half8*>(Q + ((size_t)c * (pairs + 1) + slot) * H + n);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[e] += (float)v[e];
       }
+      const float w = p[slot];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w * part[e];
     }
-    _Float16* yr = y + (size_t)t * H + n;
-    yr[0] = (_Float16)(acc.x * scale);
-    yr[1] = (_Float16)(acc.y * scale);
-    yr[2] = (_Float16)(acc.z * scale);
-    yr[3] = (_Float16)(acc.w * scale);
+    half8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (_Float16)acc[e];
+    *reinterpret_cast<half8*>(y + (size_t)t * H + n) = o;
   }
 }
 
@@ -234,20 +281,22 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
   const int sblocks = (n_slots + 255) / 256;
   hipLaunchKernelGGL(k_moe_count, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, pl.counts, dev_error);
   hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, stream, pl.counts, E, pl.offsets, pl.tile_expert,
-                     pl.tile_start, pl.tile_rows, pl.n_tiles, MoeCfg::MT);
+                     pl.tile_start, pl.tile_rows, pl.n_tiles, MT_MOE);
   hipLaunchKernelGGL(k_moe_scatter, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, pl.offsets, pl.cursor,
                      pl.slots, pl.pos);
+  hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream, static_cast<const _Float16*>(x),
+                     hidden, M, pl.xtok);
   const int n_chunks = chunks_for(inter);
   const int max_tiles = max_tiles_for(M, top_k, E);
   timing_begin(stream);
-  hipLaunchKernelGGL(k_moe_fused, dim3(max_tiles * n_chunks), dim3(MoeCfg::THREADS), 0, stream,
+  hipLaunchKernelGGL(k_moe_fused16, dim3(max_tiles * n_chunks), dim3(MoeCfg::THREADS), 0, stream,
                      static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
-                     static_cast<const uint8_t*>(wd), hidden, inter, static_cast<const _Float16*>(x), p, top_k,
-                     pl.n_tiles, pl.tile_expert, pl.tile_start, pl.tile_rows, pl.slots, pl.Q, n_slots,
-                     ldexpf(1.0f, -inter_shift), n_chunks);
+                     static_cast<const uint8_t*>(wd), hidden, inter, M, pl.xtok, top_k, pl.n_tiles, pl.tile_expert,
+                     pl.tile_start, pl.tile_rows, pl.slots, pl.Q, n_slots, ldexpf(1.0f, -inter_shift),
+                     ldexpf(1.0f, inter_shift - out_shift), n_chunks);
   timing_end(stream);
-  hipLaunchKernelGGL(k_moe_combine, dim3(M), dim3(256), 0, stream, pl.Q, pl.pos, top_k, n_chunks, n_slots, hidden,
-                     static_cast<_Float16*>(y), ldexpf(1.0f, inter_shift - out_shift));
+  hipLaunchKernelGGL(k_moe_combine, dim3(M), dim3(256), 0, stream, pl.Q, pl.pos, p, top_k, n_chunks, n_slots, hidden,
+                     static_cast<_Float16*>(y));
   return hipGetLastError();
 }
 

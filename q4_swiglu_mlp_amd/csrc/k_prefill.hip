@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused
   if (threadIdx.x < 64) tok[threadIdx.x] = min(tile * 64 + (int)threadIdx.x, M);   // M: the zero token
   __syncthreads();
   const OutQuads out{P, Mpad, H, out_scale, chunk, tile * 64};
-  fused_unit16<ICMAX>(wg, wu, wd, H, I, xg, tok, r0, r1, inter_scale, out, sm);
+  fused_unit16<ICMAX>(wg, wu, wd, H, I, xg, tok, min(64, M - tile * 64), r0, r1, inter_scale, out, sm);
 }
 
 // y[t][n] = fp16(sum_c P[c][n][t]) through a 64x64 LDS transpose.  Thread
