@@ -1,5 +1,6 @@
-// Decode of one token (M = 1; larger M uses the MFMA kernels of
-// k_decode_mfma.hip): the SwiGLU block as two HBM-bound Q4_K passes.
+// Decode of one token (M = 1 and inter <= 16384; larger M or a longer
+// down-projection contraction use the MFMA kernels of k_decode_mfma.hip): the
+// SwiGLU block as two HBM-bound Q4_K passes.
 //
 //   k_decode_rows<GATEUP=true>  streams W_gate and W_up once: both projections
 //     share one staging of x (the same-input gate/up pair fusion of "Four
@@ -295,7 +296,11 @@ size_t decode_workspace_bytes(int M, int hidden, int inter) {
 
 hipError_t launch_decode(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x, void* y,
                          int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
-  if (M >= 2) return launch_decode_mfma(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream);
+  // The row kernels cover contractions up to DR_KMAX (four 64-chunk slots per
+  // lane); a longer down-projection contraction takes the MFMA path, which
+  // walks any K in passes.
+  if (M >= 2 || inter > DR_KMAX)
+    return launch_decode_mfma(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream);
   const float gu_scale = ldexpf(1.0f, -inter_shift), dn_scale = ldexpf(1.0f, inter_shift - out_shift);
   _Float16* hbuf = static_cast<_Float16*>(ws);
   timing_begin(stream);

@@ -194,6 +194,18 @@ def test_decode_tiny_workload(M):
     assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift), y_ref, f"decode tiny M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 4])
+def test_decode_long_down_contraction(M):
+    # inter = 16640 > 16384: longer than the M = 1 row kernels cover, so both M
+    # take the MFMA passes; the prefill kernel runs the same shape
+    H, I = 256, 16640
+    wg, wu, wd, x = _rand_mlp(777 + M, H, I, M)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
+    a, b = shifts_for(y_ref, h_ref)
+    assert_parity(decode(wg, wu, wd, H, I, x, a, b), y_ref, f"decode H={H} I={I} M={M}")
+    assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill H={H} I={I} M={M}")
+
+
 @pytest.mark.parametrize("name,layer", [("decode_m1", 0), ("decode_m4", 0), ("decode_m4", 17)])
 def test_decode_workloads(name, layer):
     w = S.WORKLOADS[name]
