@@ -96,7 +96,9 @@ int zinc_q4k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* 
  * rearranged into the MFMA operand order (written first, by a small kernel)
  * and the down-projection partial sums of the intermediate chunks, stored as
  * fp16 at the output scale and summed in fp32 by a reduce kernel.
- * Limits: hidden, inter multiples of 256, hidden <= 16384, inter <= 65536.
+ * Limits: hidden, inter multiples of 256, hidden <= 16384, inter <= 65536,
+ * M <= 2^20 and (M + 1) * (hidden / 256) * 544 < 2^32 (else ZINC_ERR_ARG, and
+ * the workspace size query returns 0).
  */
 size_t zinc_mlp_q4k_prefill_workspace_size(int32_t M, int32_t hidden, int32_t inter);
 int zinc_mlp_q4k_prefill(const void* w_gate, const void* w_up, const void* w_down,
@@ -134,8 +136,9 @@ int zinc_mlp_q4k_decode(const void* w_gate, const void* w_up, const void* w_down
  * A slot whose id is outside [0, n_experts) contributes nothing; the kernel
  * then ORs 1 into *dev_error (a device int32, may be NULL) -- the flag is
  * sticky and the caller clears it.  Duplicate ids within a token each count.
- * 1 <= top_k <= n_experts <= 1024; M * top_k <= 2^24 and (M * top_k + 1) * hidden * 2 < 2^31
- * (else ZINC_ERR_ARG, and the workspace size query returns 0).
+ * 1 <= top_k <= n_experts <= 1024; M * top_k <= 2^24, (M * top_k + 1) * hidden * 2 < 2^31
+ * and (M + 1) * (hidden / 256) * 544 < 2^32 (else ZINC_ERR_ARG, and the
+ * workspace size query returns 0).
  */
 size_t zinc_moe_q4k_experts_workspace_size(int32_t M, int32_t top_k, int32_t n_experts,
                                            int32_t hidden, int32_t inter);

@@ -23,6 +23,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool dim_ok(int32_t v, int32_t max) { return v > 0 && v % 256 == 0 && v <= max; }
 
+// The fused 64-token unit addresses its staged activation, (M + 1) tokens x
+// (hidden / 256) columns x 544 bytes, with 32-bit byte offsets.
+bool staged_ok(long long M, int32_t hidden) { return (M + 1) * (hidden / 256) * 544LL <= 0xFFFFFFFFLL; }
+
 // The MoE partial rows of one intermediate chunk, (M*top_k + 1) x hidden fp16,
 // are addressed with 32-bit byte offsets: they must stay below 2 GiB.
 bool moe_rows_ok(int32_t M, int32_t top_k, int32_t hidden) {
@@ -43,7 +47,7 @@ int check_dense(const void* wg, const void* wu, const void* wd, int32_t hidden, 
   if (!wg || !wu || !wd || !x || !y) return ZINC_ERR_NULL;
   if (!dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return ZINC_ERR_SHAPE;
   if (!aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(x) || !aligned16(y)) return ZINC_ERR_ALIGN;
-  if (M < 0 || M > max_m) return ZINC_ERR_ARG;
+  if (M < 0 || M > max_m || !staged_ok(M, hidden)) return ZINC_ERR_ARG;
   if (inter_shift < 0 || inter_shift > kMaxShift || out_shift < 0 || out_shift > kMaxShift) return ZINC_ERR_ARG;
   return ZINC_OK;
 }
@@ -80,7 +84,8 @@ int zinc_q4k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* 
 }
 
 size_t zinc_mlp_q4k_prefill_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
-  if (M < 0 || !dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
+  if (M < 0 || M > kMaxPrefillM || !dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
+  if (!staged_ok(M, hidden)) return 0;
   return zinc::prefill_workspace_bytes(M, hidden, inter);
 }
 
@@ -122,7 +127,7 @@ size_t zinc_moe_q4k_experts_workspace_size(int32_t M, int32_t top_k, int32_t n_e
   if (M < 0 || n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > n_experts) return 0;
   if ((long long)M * top_k > kMaxMoeSlots) return 0;
   if (!dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
-  if (!moe_rows_ok(M, top_k, hidden)) return 0;
+  if (!moe_rows_ok(M, top_k, hidden) || !staged_ok(M, hidden)) return 0;
   return zinc::moe_workspace_bytes(M, top_k, n_experts, hidden, inter);
 }
 
@@ -138,7 +143,7 @@ int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_dow
     return ZINC_ERR_ALIGN;
   if (n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > n_experts) return ZINC_ERR_ARG;
   if (M < 0 || (long long)M * top_k > kMaxMoeSlots) return ZINC_ERR_ARG;
-  if (!moe_rows_ok(M, top_k, hidden)) return ZINC_ERR_ARG;
+  if (!moe_rows_ok(M, top_k, hidden) || !staged_ok(M, hidden)) return ZINC_ERR_ARG;
   if (inter_shift < 0 || inter_shift > kMaxShift || out_shift < 0 || out_shift > kMaxShift) return ZINC_ERR_ARG;
   if (M == 0) return ZINC_OK;
   if (!workspace) return ZINC_ERR_NULL;

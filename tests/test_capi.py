@@ -68,6 +68,17 @@ def test_dense_argument_errors(fn):
     assert fn(M=0, ws=None, wsb=0) == 0
 
 
+def test_prefill_addressing_limits():
+    # the staged activation, (M+1) x hidden/256 x 544 B, is addressed with
+    # 32-bit offsets: at hidden 16384 M = 123360 fits, M = 123361 does not
+    assert (123360 + 1) * 64 * 544 <= 0xFFFFFFFF < (123361 + 1) * 64 * 544
+    assert prefill(hidden=16384, M=123361) == -5
+    assert Z.prefill_workspace_size(123361, 16384, 11008) == 0
+    assert Z.prefill_workspace_size(123360, 16384, 256) > 0
+    assert prefill(M=(1 << 20) + 1) == -5
+    assert Z.prefill_workspace_size((1 << 20) + 1, 256, 256) == 0
+
+
 def test_decode_token_limit():
     assert decode(M=9) == -5
     assert Z.decode_workspace_size(9, 4096, 11008) == 0
@@ -97,6 +108,9 @@ def test_moe_argument_errors():
     assert moe(ids=A + 2) == -3 and moe(err=A + 1) == -3 and moe(x=MIS) == -3
     assert moe(k=0) == -5 and moe(k=65) == -5 and moe(E=0) == -5 and moe(E=1025, k=8) == -5
     assert moe(M=-3) == -5 and moe(M=(1 << 24) // 8 + 1) == -5
+    # a chunk's partial rows, (M*k + 1) x hidden fp16, use 32-bit offsets
+    assert moe(M=65536, k=2, hidden=16384) == -5
+    assert Z.moe_workspace_size(65536, 2, 64, 16384, 768) == 0
     assert moe(ws=None) == -1 and moe(wsb=100) == -4
     assert moe(M=0, ws=None, wsb=0) == 0
 
