@@ -20,6 +20,9 @@
 //                     the sum over chunks), in fp32
 // No atomics: every partial has exactly one writer, and the combine order is
 // fixed, so the result is deterministic.
+#include <cstdlib>
+#include <cstring>
+
 #include "fused16.hpp"
 #include "launch.hpp"
 #include "util_kernels.hpp"
@@ -157,6 +160,83 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__
   pos[i] = q;
 }
 
+// Steps 1-3 in one workgroup of 1024 threads when the slot count is small
+// (the usual case): counts with LDS atomics, the scans and the tile table
+// (full tiles first, as k_moe_plan), then the scatter with LDS cursors.
+constexpr int kRouteOneBlockSlots = 1 << 16;
+
+__global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ ids, int n_slots, int E,
+                                                   int32_t* __restrict__ dev_error, int* __restrict__ offsets,
+                                                   int* __restrict__ tile_expert, int* __restrict__ tile_start,
+                                                   int* __restrict__ tile_rows, int* __restrict__ n_tiles,
+                                                   int* __restrict__ slots, int* __restrict__ pos, int MT) {
+  __shared__ int cnt[1024];
+  __shared__ int sc[1024];
+  __shared__ int sf[1024];
+  __shared__ int sr[1024];
+  const int e = threadIdx.x;
+  cnt[e] = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int i = threadIdx.x; i < n_slots; i += 1024) {
+    const int x = ids[i];
+    if (x >= 0 && x < E)
+      atomicAdd(&cnt[x], 1);
+    else
+      bad = true;
+  }
+  if (bad && dev_error) atomicOr(dev_error, 1);
+  __syncthreads();
+  const int c = (e < E) ? cnt[e] : 0;
+  const int nf = c / MT, nr = (c % MT) ? 1 : 0;
+  sc[e] = c;
+  sf[e] = nf;
+  sr[e] = nr;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int a = (e >= d) ? sc[e - d] : 0;
+    const int b = (e >= d) ? sf[e - d] : 0;
+    const int r = (e >= d) ? sr[e - d] : 0;
+    __syncthreads();
+    sc[e] += a;
+    sf[e] += b;
+    sr[e] += r;
+    __syncthreads();
+  }
+  const int off = sc[e] - c;
+  const int total_full = sf[1023];
+  if (e < E) offsets[e] = off;
+  if (e == E - 1) {
+    offsets[E] = sc[e];
+    *n_tiles = total_full + sr[1023];
+  }
+  const int tf = sf[e] - nf;
+  for (int i = 0; i < nf; ++i) {
+    tile_expert[tf + i] = e;
+    tile_start[tf + i] = off + i * MT;
+    tile_rows[tf + i] = MT;
+  }
+  if (nr) {
+    const int tr = total_full + sr[e] - 1;
+    tile_expert[tr] = e;
+    tile_start[tr] = off + nf * MT;
+    tile_rows[tr] = c - nf * MT;
+  }
+  __syncthreads();
+  cnt[e] = off;   // the expert's cursor
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_slots; i += 1024) {
+    const int x = ids[i];
+    if (x >= 0 && x < E) {
+      const int q = atomicAdd(&cnt[x], 1);
+      slots[q] = i;
+      pos[i] = q;
+    } else {
+      pos[i] = -1;
+    }
+  }
+}
+
 // MoE output of the 64-token unit: unit row r belongs to slot slot_of_row[r];
 // the fp16 partial, at the output scale, goes to Q[chunk][slot][n].  Padding
 // rows carry slot = pairs, a junk row after the chunk's pairs (no branch
@@ -275,15 +355,23 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
   const int E = n_experts;
   const int n_slots = M * top_k;
   MoePlan pl = carve(ws, M, top_k, E, hidden, inter, nullptr);
-  // counts and cursor are adjacent 256-byte-aligned arrays; zero both
-  launch_fill_zero(reinterpret_cast<float*>(pl.counts),
-                   (size_t)(reinterpret_cast<char*>(pl.offsets) - reinterpret_cast<char*>(pl.counts)) / 4, stream);
-  const int sblocks = (n_slots + 255) / 256;
-  hipLaunchKernelGGL(k_moe_count, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, pl.counts, dev_error);
-  hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, stream, pl.counts, E, pl.offsets, pl.tile_expert,
-                     pl.tile_start, pl.tile_rows, pl.n_tiles, MT_MOE);
-  hipLaunchKernelGGL(k_moe_scatter, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, pl.offsets, pl.cursor,
-                     pl.slots, pl.pos);
+  // ZINC_MOE_ROUTE=multi forces the multi-kernel routing (to test it at small sizes)
+  const char* route = std::getenv("ZINC_MOE_ROUTE");
+  const bool one_block = n_slots <= kRouteOneBlockSlots && !(route && std::strcmp(route, "multi") == 0);
+  if (one_block) {
+    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, stream, ids, n_slots, E, dev_error, pl.offsets,
+                       pl.tile_expert, pl.tile_start, pl.tile_rows, pl.n_tiles, pl.slots, pl.pos, MT_MOE);
+  } else {
+    // counts and cursor are adjacent 256-byte-aligned arrays; zero both
+    launch_fill_zero(reinterpret_cast<float*>(pl.counts),
+                     (size_t)(reinterpret_cast<char*>(pl.offsets) - reinterpret_cast<char*>(pl.counts)) / 4, stream);
+    const int sblocks = (n_slots + 255) / 256;
+    hipLaunchKernelGGL(k_moe_count, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, pl.counts, dev_error);
+    hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, stream, pl.counts, E, pl.offsets, pl.tile_expert,
+                       pl.tile_start, pl.tile_rows, pl.n_tiles, MT_MOE);
+    hipLaunchKernelGGL(k_moe_scatter, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, pl.offsets, pl.cursor,
+                       pl.slots, pl.pos);
+  }
   hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream, static_cast<const _Float16*>(x),
                      hidden, M, pl.xtok);
   const int n_chunks = chunks_for(inter);

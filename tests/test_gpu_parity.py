@@ -273,6 +273,24 @@ def test_moe_tiny():
     assert_parity(_moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, 8), y_ref, "moe E=4 top-2")
 
 
+def test_moe_both_routing_paths(monkeypatch):
+    # one-workgroup routing (the default at this size) and the multi-kernel
+    # routing used past 65536 slots: the same oracle result, bit-identical y
+    E, H, I, M, k = 16, 256, 512, 300, 4
+    wg, wu, wd, x, ids, p = _moe_inputs(E, H, I, M, k, 25)
+    ids = ids.copy()
+    ids[5, 1] = E + 3                                    # one invalid id: flagged, contributes nothing
+    y_ref, bad = O.moe(x, wg, wu, wd, ids, p, H, I)
+    assert bad == 1
+    b = max(0, int(np.ceil(np.log2(np.abs(y_ref).max() / 2 ** 13))))
+    y_one = _moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, b)
+    monkeypatch.setenv("ZINC_MOE_ROUTE", "multi")
+    y_multi = _moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, b)
+    assert_parity(y_one, y_ref, "moe one-workgroup routing")
+    assert_parity(y_multi, y_ref, "moe multi-kernel routing")
+    assert np.array_equal(y_one, y_multi)
+
+
 def test_moe_top1_weight1_matches_dense():
     E, H, I, M = 4, 512, 512, 70
     wg, wu, wd, x, _, _ = _moe_inputs(E, H, I, M, 1, 22)
