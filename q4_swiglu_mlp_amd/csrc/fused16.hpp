@@ -93,6 +93,7 @@ struct Fused16Smem {
   _Float16 xm[C::XRING][C::MT * 8];     // 32-means per block column, ring
   float hsum32[C::MT * C::HSS];         // the strip's 32-row sums while phase 1 runs
   _Float16 junk[(C::NJUNK > 0 ? C::NJUNK : 1) * 8];   // stores of the copy slots past a column
+  int p2_next;                          // phase 2: next unclaimed output tile
 };
 
 // Scales of the two chunks a lane decodes per block (chunk c0 = sel, c1 =
@@ -308,7 +309,8 @@ struct OutQuads {
 template <class C, int ICMAX, int OFF, int NTT, class Out>
 __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int H, int I, int r0, int r1,
                                             const Out& out, const _Float16* __restrict__ hs,
-                                            const _Float16* __restrict__ hsum, const NibbleK& nk) {
+                                            const _Float16* __restrict__ hsum, const NibbleK& nk,
+                                            int* __restrict__ next_tile) {
   constexpr int HS = C::HS, HSS = C::HSS;
   constexpr int NB = C::NBMAX;
   constexpr int NP = ICMAX / 64;
@@ -373,20 +375,35 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
     out.template store<NTT>(acc, nt, l32, h);
   };
 
-  // two rolling tile buffers, so a wave's loads run two tiles ahead: each
-  // panel's bytes and each header are refilled with the tile after next
-  // (nt + 2 WAVES) as soon as they have been consumed
+  // Two rolling tile buffers, so a wave's loads run two tiles ahead: each
+  // panel's bytes and each header are refilled with the wave's tile after
+  // next as soon as they have been consumed.  Wave w starts on tiles w and
+  // w + WAVES; every later tile is claimed from an LDS counter (starting at
+  // 2 WAVES) when the tile two before it starts, so waves that issue faster
+  // (the scheduler favours older waves) take more tiles and the unit's
+  // waves finish together.  Claims only grow, so a wave's tiles ascend and
+  // the first one past the last tile ends its loop.
   constexpr int W = C::WAVES;
   const size_t tile_step = (size_t)32 * row_bytes;
   if (wave >= NT) return;   // wave-uniform: fewer output tiles than waves
   // loads past the last tile re-read the last one (in bounds, never used)
   auto clamp_tile = [&](int t) { return t < NT ? t : NT - 1; };
-  DownTileData<NP, NB> d0 = load_down_tile<NP, NB, OFF>(blk_base + (size_t)wave * tile_step, nblk, npan, h);
-  DownTileData<NP, NB> d1 =
-      load_down_tile<NP, NB, OFF>(blk_base + (size_t)clamp_tile(wave + W) * tile_step, nblk, npan, h);
-  for (int nt = wave; nt < NT; nt += 2 * W) {
-    down_tile(d0, nt, blk_base + (size_t)clamp_tile(nt + 2 * W) * tile_step);
-    if (nt + W < NT) down_tile(d1, nt + W, blk_base + (size_t)clamp_tile(nt + 3 * W) * tile_step);
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(next_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int t0 = wave, t1 = wave + W;
+  DownTileData<NP, NB> d0 = load_down_tile<NP, NB, OFF>(blk_base + (size_t)t0 * tile_step, nblk, npan, h);
+  DownTileData<NP, NB> d1 = load_down_tile<NP, NB, OFF>(blk_base + (size_t)clamp_tile(t1) * tile_step, nblk, npan, h);
+  while (t0 < NT) {
+    const int t2 = claim();
+    down_tile(d0, t0, blk_base + (size_t)clamp_tile(t2) * tile_step);
+    if (t1 >= NT) break;
+    const int t3 = claim();
+    down_tile(d1, t1, blk_base + (size_t)clamp_tile(t3) * tile_step);
+    t0 = t2;
+    t1 = t3;
   }
 }
 
@@ -610,6 +627,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
       if (o == 0) atomicAdd(&sm.hsum32[t * HSS + slot], s4);
     }
   }
+  if (threadIdx.x == 0) sm.p2_next = 2 * C::WAVES;
   lds_barrier();   // strip and sums complete
   for (int i = threadIdx.x; i < MT * HSS; i += C::THREADS) sm.u.s.hsum[i] = (_Float16)(sm.hsum32[i] * 0.03125f);
   lds_barrier();
@@ -618,10 +636,10 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   auto phase2 = [&](auto ntt_tag) {
     constexpr int NTT = decltype(ntt_tag)::value;
     switch (off) {
-      case 0: fu16_phase2<C, ICMAX, 0, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-      case 1: fu16_phase2<C, ICMAX, 1, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-      case 2: fu16_phase2<C, ICMAX, 2, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
-      default: fu16_phase2<C, ICMAX, 3, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk); break;
+      case 0: fu16_phase2<C, ICMAX, 0, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
+      case 1: fu16_phase2<C, ICMAX, 1, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
+      case 2: fu16_phase2<C, ICMAX, 2, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
+      default: fu16_phase2<C, ICMAX, 3, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
     }
   };
   if (rows > 32)
