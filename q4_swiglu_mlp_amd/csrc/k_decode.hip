@@ -14,9 +14,10 @@
 // Shape.  Weight rows are independent dot products, so each wave owns whole
 // rows and walks them grid-stride (at any moment the grid reads one contiguous
 // window of the matrix): no tiles, no barriers inside the loop, no cross-wave
-// sums.  The workgroups are persistent (as many as are resident at once) and
+// sums.  The workgroups are persistent (a fixed number per CU, see DrCfg) and
 // stage the contraction vector once in LDS, under the latency of their first
-// rows' loads.
+// rows' loads; each wave keeps two rows in flight, computing one while the
+// next one's loads are outstanding.
 //
 // Lanes.  A row's super-blocks split into 64-weight chunks; lane l takes chunks
 // q = l, l+64, ... of the row, i.e. the block's 16-byte header and its 32 quant
@@ -34,15 +35,17 @@
 #include "launch.hpp"
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 
 namespace zinc {
 
 namespace {
 
 // waves per workgroup
-template <bool GATEUP>
+template <int W>
 struct DrShape {
-  static constexpr int WAVES = 8;
+  static constexpr int WAVES = W;
   static constexpr int THREADS = 64 * WAVES;
 };
 constexpr int DR_KMAX = 16384;               // longest contraction (the library's hidden limit)
@@ -111,13 +114,13 @@ __device__ __forceinline__ void chunk_dot(const Chunk& ch, int c, const _Float16
     acc[t] += slo * alo[t] - clo * X2[t * X2S] + shi * ahi[t] - chi * X2[t * X2S + 1];
 }
 
-template <int MM, bool GATEUP, int KQ>
-__global__ __launch_bounds__(DrShape<GATEUP>::THREADS) void k_decode_rows(const uint8_t* __restrict__ W0,
+template <int MM, bool GATEUP, int KQ, bool PF, int NW>
+__global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint8_t* __restrict__ W0,
                                                             const uint8_t* __restrict__ W1, int K, int N,
                                                             const _Float16* __restrict__ xin, int M,
                                                             _Float16* __restrict__ out, float scale) {
   constexpr int NMAT = GATEUP ? 2 : 1;
-  constexpr int DR_WAVES = DrShape<GATEUP>::WAVES, DR_THREADS = DrShape<GATEUP>::THREADS;
+  constexpr int DR_WAVES = DrShape<NW>::WAVES, DR_THREADS = DrShape<NW>::THREADS;
   extern __shared__ __attribute__((aligned(16))) unsigned char dr_smem[];
   const int nb = K / QK;
   const int Q = 4 * nb;                   // chunks per row
@@ -145,8 +148,10 @@ __global__ __launch_bounds__(DrShape<GATEUP>::THREADS) void k_decode_rows(const 
     qoff[k] = boff[k] + 16 + 32 * (qc & 3);
   }
   using Buf = Chunk[NMAT][KQ];
-  auto load_row = [&](int j, Buf& buf) __attribute__((always_inline)) {
-    const int jj = j < N ? j : 0;   // past the last row: re-read row 0 (never used)
+  // past the last row: re-read row fb (the wave's current row, cache-hot), or
+  // row 0 if that is past the end too (never used either way)
+  auto load_row = [&](int j, Buf& buf, int fb = 0) __attribute__((always_inline)) {
+    const int jj = j < N ? j : (fb < N ? fb : 0);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       const uint8_t* row = (m ? W1 : W0) + (size_t)jj * row_bytes;
@@ -201,10 +206,7 @@ __global__ __launch_bounds__(DrShape<GATEUP>::THREADS) void k_decode_rows(const 
     xv[u] = make_uint4(0, 0, 0, 0);
     if (g < ngroups && t < M) xv[u] = *reinterpret_cast<const uint4*>(xin + (size_t)t * K + 8 * a);
   }
-  // One row in flight per wave: with every wave of the grid streaming, more
-  // rows in flight only lengthened the queues (measured slower), so a wave
-  // loads row j, computes it, and moves on.
-  Buf buf;
+  Buf buf, buf2;
   int j = w0;
   load_row(j, buf);
   // stage x: groups of four with the middle two swapped; fp32 sums of every 32
@@ -228,9 +230,23 @@ __global__ __launch_bounds__(DrShape<GATEUP>::THREADS) void k_decode_rows(const 
   }
   __syncthreads();
 
-  for (; j < N; j += nwaves) {
-    if (j != w0) load_row(j, buf);
-    compute_row(j, buf);
+  if constexpr (PF) {
+    // two rows in flight per wave: the row after next is requested as soon
+    // as a buffer has been consumed, so the arithmetic of one row runs under
+    // the loads of the next
+    load_row(j + nwaves, buf2, j);
+    for (; j < N; j += 2 * nwaves) {
+      compute_row(j, buf);
+      load_row(j + 2 * nwaves, buf, j);
+      if (j + nwaves >= N) break;
+      compute_row(j + nwaves, buf2);
+      load_row(j + 3 * nwaves, buf2, j + nwaves);
+    }
+  } else {
+    for (; j < N; j += nwaves) {
+      if (j != w0) load_row(j, buf);
+      compute_row(j, buf);
+    }
   }
 }
 
@@ -248,13 +264,34 @@ int cu_count() {
 
 // Persistent grid: as many workgroups as are resident at once (occupancy of
 // this instantiation at this LDS size), so no workgroup waits for another to end.
-template <int MM, bool GATEUP, int KQ>
-hipError_t launch_rows(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
-                       float scale, hipStream_t stream) {
+// Launch shape of the row kernels: two rows in flight per wave or one,
+// waves per workgroup, workgroups per CU (0: as many as are resident).
+// Measured on the 4096/11008 layer sweep: two rows in flight on persistent
+// four-wave workgroups, two per CU for the gate/up pass (about 11 rows per
+// wave) and one for the down pass (4 rows per wave), beat the one-row,
+// full-occupancy shape by ~1.8 us per layer in kernel time.  ZINC_DR_GU /
+// ZINC_DR_DN = "pf,waves,wg_per_cu" override them.
+struct DrCfg {
+  bool pf;
+  int waves, wg_per_cu;
+};
+
+inline DrCfg dr_cfg(bool gateup) {
+  DrCfg c = gateup ? DrCfg{true, 4, 2} : DrCfg{true, 4, 1};
+  if (const char* e = std::getenv(gateup ? "ZINC_DR_GU" : "ZINC_DR_DN")) {
+    int pf = 0, w = 8, g = 0;
+    if (std::sscanf(e, "%d,%d,%d", &pf, &w, &g) == 3 && (w == 4 || w == 8) && g >= 0) c = DrCfg{pf != 0, w, g};
+  }
+  return c;
+}
+
+template <int MM, bool GATEUP, int KQ, bool PF, int NW>
+hipError_t launch_rows_cfg(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
+                           float scale, int wg_per_cu, hipStream_t stream) {
   const size_t smem = (size_t)MM * (K + 8) * 2 + (size_t)MM * 2 * (4 * (K / QK)) * 4;
   static size_t attr_set = 0;   // largest dynamic LDS size allowed so far
   if (smem > attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_rows<MM, GATEUP, KQ>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_rows<MM, GATEUP, KQ, PF, NW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = smem;
@@ -263,18 +300,30 @@ hipError_t launch_rows(const void* W0, const void* W1, int K, int N, const _Floa
   static int occ = 0;
   if (occ == 0 || occ_smem != smem) {
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_rows<MM, GATEUP, KQ>,
-                                                                DrShape<GATEUP>::THREADS, smem);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_rows<MM, GATEUP, KQ, PF, NW>,
+                                                                DrShape<NW>::THREADS, smem);
     if (e != hipSuccess) return e;
     occ = per_cu < 1 ? 1 : per_cu;
     occ_smem = smem;
   }
-  const int per_cu = occ;
-  constexpr int WAVES = DrShape<GATEUP>::WAVES;
-  const int grid = std::max(1, std::min(cu_count() * per_cu, (N + WAVES - 1) / WAVES));
-  hipLaunchKernelGGL((k_decode_rows<MM, GATEUP, KQ>), dim3(grid), dim3(DrShape<GATEUP>::THREADS), smem, stream,
+  const int per_cu = (wg_per_cu > 0 && wg_per_cu < occ) ? wg_per_cu : occ;
+  const int grid = std::max(1, std::min(cu_count() * per_cu, (N + NW - 1) / NW));
+  hipLaunchKernelGGL((k_decode_rows<MM, GATEUP, KQ, PF, NW>), dim3(grid), dim3(DrShape<NW>::THREADS), smem, stream,
                      static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), K, N, x, M, out, scale);
   return hipGetLastError();
+}
+
+template <int MM, bool GATEUP, int KQ>
+hipError_t launch_rows(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
+                       float scale, hipStream_t stream) {
+  const DrCfg c = dr_cfg(GATEUP);
+  if (c.pf && c.waves == 4)
+    return launch_rows_cfg<MM, GATEUP, KQ, true, 4>(W0, W1, K, N, x, M, out, scale, c.wg_per_cu, stream);
+  if (c.pf)
+    return launch_rows_cfg<MM, GATEUP, KQ, true, 8>(W0, W1, K, N, x, M, out, scale, c.wg_per_cu, stream);
+  if (c.waves == 4)
+    return launch_rows_cfg<MM, GATEUP, KQ, false, 4>(W0, W1, K, N, x, M, out, scale, c.wg_per_cu, stream);
+  return launch_rows_cfg<MM, GATEUP, KQ, false, 8>(W0, W1, K, N, x, M, out, scale, c.wg_per_cu, stream);
 }
 
 template <int MM, bool GATEUP>
