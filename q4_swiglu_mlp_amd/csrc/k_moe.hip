@@ -11,15 +11,20 @@
 //   3. k_moe_scatter  slot indices grouped by expert, and each slot's position
 //   4. k_stage_x16    the activation per token in the fused unit's operand
 //                     order (fused16.hpp), plus an all-zero token
-//   5. k_moe_fused16  one 64-token fused unit (fused16.hpp) per (tile of 64
-//                     routed rows of one expert, intermediate chunk); blocks
-//                     past the device-side tile count exit at once.  Each
-//                     row's expert output (fp16 at the output scale) is
-//                     stored at its slot: Q[chunk][slot][hidden]
+//   5. k_moe_fused16  one 64-token fused unit (fused16.hpp) per (tile of up
+//                     to 64 routed rows of one expert, intermediate chunk):
+//                     192-row chunks, or 128-row chunks for every tile of an
+//                     expert whose remainder tile is small; blocks past the
+//                     device-side unit count exit at once.  Each row's expert
+//                     output (fp16 at the output scale) is stored at its
+//                     slot: Q[chunk][slot][hidden]
 //   6. k_moe_combine  y[t] = fp16(sum over the token's slots of p[t,s] times
 //                     the sum over chunks), in fp32
-// No atomics: every partial has exactly one writer, and the combine order is
-// fixed, so the result is deterministic.
+// Every partial has exactly one writer, all tiles of an expert share one
+// chunking (so a row's arithmetic does not depend on which of its expert's
+// tiles the scatter put it in), and the combine order is fixed, so the result
+// is deterministic (the atomics only count and place).
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -42,9 +47,9 @@ struct MoePlan {
   int* tile_expert;  // [max_tiles]
   int* tile_start;   // [max_tiles]
   int* tile_rows;    // [max_tiles]
-  int* n_tiles;      // [1]
+  int* n_tiles;      // [2]: tiles, tiles of 192-row-chunk experts (listed first)
   int* slots;        // [M * top_k] slot indices grouped by expert
-  int* pos;          // [M * top_k] list position of each slot, -1 if its id is invalid
+  int* pos;          // [M * top_k] list position of each slot (| kPosSmall: 128-row chunks), -1 if its id is invalid
   _Float16* Q;       // [n_chunks][M * top_k + 1][H], fp16 at the output scale (last row: junk)
   uint8_t* xtok;     // staged activation, x16_staged_bytes(M, H)
 };
@@ -56,10 +61,33 @@ int max_tiles_for(int M, int top_k, int E) {
   return (int)((pairs + MT_MOE - 1) / MT_MOE + (pairs < E ? pairs : E));
 }
 
+// Chunks of the intermediate dimension: 192-row chunks (three 64-row panels),
+// or 128-row chunks (eight busy waves instead of twelve) for every tile of an
+// expert whose remainder tile has at most kSmallRows rows.  Such a remainder
+// tile costs most of a unit for a few rows (the weight decode dominates); cut
+// into more, shorter units, the expert's tiles fill the last round of units
+// more evenly.  A whole expert takes one chunking, so a row's partial sums do
+// not depend on which of the expert's tiles the scatter put it in.
+constexpr int kSmallRows = 16;
+
+__host__ __device__ inline bool small_expert(int count, int MT) {
+  const int rem = count % MT;
+  return rem > 0 && rem <= kSmallRows;
+}
+
 int chunks_for(int I) {
   const int npan = I / 64;
   return (npan + ICMAX_MOE / 64 - 1) / (ICMAX_MOE / 64);
 }
+
+int chunks_small_for(int I) {
+  const int npan = I / 64;
+  return std::max(chunks_for(I), (npan + 1) / 2);
+}
+
+// A slot's list position carries this bit when its expert takes 128-row
+// chunks (positions are below 2^24), so the combine knows its chunk count.
+constexpr int kPosSmall = 1 << 30;
 
 MoePlan carve(void* ws, int M, int top_k, int E, int H, int I, size_t* total) {
   MoePlan p;
@@ -74,13 +102,72 @@ MoePlan carve(void* ws, int M, int top_k, int E, int H, int I, size_t* total) {
   p.tile_expert = reinterpret_cast<int*>(take(sizeof(int) * mt));
   p.tile_start = reinterpret_cast<int*>(take(sizeof(int) * mt));
   p.tile_rows = reinterpret_cast<int*>(take(sizeof(int) * mt));
-  p.n_tiles = reinterpret_cast<int*>(take(sizeof(int)));
+  p.n_tiles = reinterpret_cast<int*>(take(sizeof(int) * 2));
   p.slots = reinterpret_cast<int*>(take(sizeof(int) * pairs));
   p.pos = reinterpret_cast<int*>(take(sizeof(int) * pairs));
-  p.Q = reinterpret_cast<_Float16*>(take(sizeof(_Float16) * (size_t)chunks_for(I) * (pairs + 1) * H));
+  p.Q = reinterpret_cast<_Float16*>(take(sizeof(_Float16) * (size_t)chunks_small_for(I) * (pairs + 1) * H));
   p.xtok = reinterpret_cast<uint8_t*>(take(x16_staged_bytes(M, H)));
   if (total) *total = off;
   return p;
+}
+
+// Tile table from per-expert counts, by thread e of a 1024-thread block (E <=
+// 1024): the tiles of 192-row-chunk experts first (full tiles, then
+// remainders), then those of 128-row-chunk experts (full, then remainders), so
+// the longest units start first.  Also the list offsets (exclusive scan of the
+// counts), n_tiles[0] = all tiles and n_tiles[1] = the tiles of 192-row-chunk
+// experts.  s0..s4: LDS scratch of 1024 ints each.  Returns the expert's list
+// offset.
+__device__ int build_tile_table(int e, int E, int c, int MT, int* s0, int* s1, int* s2, int* s3, int* s4,
+                                int* __restrict__ offsets, int* __restrict__ tile_expert,
+                                int* __restrict__ tile_start, int* __restrict__ tile_rows,
+                                int* __restrict__ n_tiles) {
+  const int nf = c / MT, rem = c - nf * MT;
+  const bool sm = small_expert(c, MT);
+  const int fa = sm ? 0 : nf, ra = (!sm && rem > 0) ? 1 : 0;   // 192-row-chunk expert
+  const int fb = sm ? nf : 0, rb = sm ? 1 : 0;                 // 128-row-chunk expert
+  s0[e] = c;
+  s1[e] = fa;
+  s2[e] = ra;
+  s3[e] = fb;
+  s4[e] = rb;
+  __syncthreads();
+  // inclusive Hillis-Steele scans
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int a0 = (e >= d) ? s0[e - d] : 0;
+    const int a1 = (e >= d) ? s1[e - d] : 0;
+    const int a2 = (e >= d) ? s2[e - d] : 0;
+    const int a3 = (e >= d) ? s3[e - d] : 0;
+    const int a4 = (e >= d) ? s4[e - d] : 0;
+    __syncthreads();
+    s0[e] += a0;
+    s1[e] += a1;
+    s2[e] += a2;
+    s3[e] += a3;
+    s4[e] += a4;
+    __syncthreads();
+  }
+  const int off = s0[e] - c;   // exclusive
+  const int tfa = s1[1023], tra = s2[1023], tfb = s3[1023], trb = s4[1023];
+  if (e < E) offsets[e] = off;
+  if (e == E - 1) {
+    offsets[E] = s0[e];
+    n_tiles[0] = tfa + tra + tfb + trb;
+    n_tiles[1] = tfa + tra;
+  }
+  const int t0 = sm ? tfa + tra + s3[e] - fb : s1[e] - fa;   // first full tile of this expert
+  for (int i = 0; i < nf; ++i) {
+    tile_expert[t0 + i] = e;
+    tile_start[t0 + i] = off + i * MT;
+    tile_rows[t0 + i] = MT;
+  }
+  if (rem > 0) {
+    const int t = sm ? tfa + tra + tfb + s4[e] - 1 : tfa + s2[e] - 1;
+    tile_expert[t] = e;
+    tile_start[t] = off + nf * MT;
+    tile_rows[t] = rem;
+  }
+  return off;
 }
 
 __global__ __launch_bounds__(256) void k_moe_count(const int32_t* __restrict__ ids, int n_slots, int E,
@@ -95,57 +182,17 @@ __global__ __launch_bounds__(256) void k_moe_count(const int32_t* __restrict__ i
   }
 }
 
-// One block of 1024 threads; E <= 1024.  The tile table lists every expert's
-// full MT-row tiles first and the remainder tiles (fewer rows, cheaper units)
-// last, so the units launched first are the expensive ones and the cheap ones
-// fill in behind them.
+// One block of 1024 threads: list offsets and the tile table (build_tile_table).
 __global__ __launch_bounds__(1024) void k_moe_plan(const int* __restrict__ counts, int E, int* __restrict__ offsets,
                                                   int* __restrict__ tile_expert, int* __restrict__ tile_start,
                                                   int* __restrict__ tile_rows, int* __restrict__ n_tiles, int MT) {
-  __shared__ int sc[1024];
-  __shared__ int sf[1024];
-  __shared__ int sr[1024];
+  __shared__ int s0[1024], s1[1024], s2[1024], s3[1024], s4[1024];
   const int e = threadIdx.x;
   const int cnt = (e < E) ? counts[e] : 0;
-  const int nf = cnt / MT;                 // full tiles
-  const int nr = (cnt % MT) ? 1 : 0;       // remainder tile
-  sc[e] = cnt;
-  sf[e] = nf;
-  sr[e] = nr;
-  __syncthreads();
-  // inclusive Hillis-Steele scans of counts, full tiles and remainder tiles
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int a = (e >= d) ? sc[e - d] : 0;
-    const int b = (e >= d) ? sf[e - d] : 0;
-    const int c = (e >= d) ? sr[e - d] : 0;
-    __syncthreads();
-    sc[e] += a;
-    sf[e] += b;
-    sr[e] += c;
-    __syncthreads();
-  }
-  const int off = sc[e] - cnt;   // exclusive
-  const int total_full = sf[1023];
-  if (e < E) offsets[e] = off;
-  if (e == E - 1) {
-    offsets[E] = sc[e];
-    *n_tiles = total_full + sr[1023];
-  }
-  const int tf = sf[e] - nf;
-  for (int i = 0; i < nf; ++i) {
-    tile_expert[tf + i] = e;
-    tile_start[tf + i] = off + i * MT;
-    tile_rows[tf + i] = MT;
-  }
-  if (nr) {
-    const int tr = total_full + sr[e] - 1;
-    tile_expert[tr] = e;
-    tile_start[tr] = off + nf * MT;
-    tile_rows[tr] = cnt - nf * MT;
-  }
+  build_tile_table(e, E, cnt, MT, s0, s1, s2, s3, s4, offsets, tile_expert, tile_start, tile_rows, n_tiles);
 }
 
-__global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__ ids, int n_slots, int E,
+__global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__ ids, int n_slots, int E, int MT,
                                                     const int* __restrict__ offsets, int* __restrict__ cursor,
                                                     int* __restrict__ slots, int* __restrict__ pos) {
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -155,14 +202,15 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__
     pos[i] = -1;
     return;
   }
-  const int q = offsets[e] + atomicAdd(cursor + e, 1);
+  const int o = offsets[e];
+  const int q = o + atomicAdd(cursor + e, 1);
   slots[q] = i;
-  pos[i] = q;
+  pos[i] = q | (small_expert(offsets[e + 1] - o, MT) ? kPosSmall : 0);
 }
 
 // Steps 1-3 in one workgroup of 1024 threads when the slot count is small
 // (the usual case): counts with LDS atomics, the scans and the tile table
-// (full tiles first, as k_moe_plan), then the scatter with LDS cursors.
+// (build_tile_table's order), then the scatter with LDS cursors.
 constexpr int kRouteOneBlockSlots = 1 << 16;
 
 __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ ids, int n_slots, int E,
@@ -171,9 +219,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
                                                    int* __restrict__ tile_rows, int* __restrict__ n_tiles,
                                                    int* __restrict__ slots, int* __restrict__ pos, int MT) {
   __shared__ int cnt[1024];
-  __shared__ int sc[1024];
-  __shared__ int sf[1024];
-  __shared__ int sr[1024];
+  __shared__ int s0[1024], s1[1024], s2[1024], s3[1024], s4[1024];
   const int e = threadIdx.x;
   cnt[e] = 0;
   __syncthreads();
@@ -188,40 +234,10 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
   if (bad && dev_error) atomicOr(dev_error, 1);
   __syncthreads();
   const int c = (e < E) ? cnt[e] : 0;
-  const int nf = c / MT, nr = (c % MT) ? 1 : 0;
-  sc[e] = c;
-  sf[e] = nf;
-  sr[e] = nr;
+  const int off = build_tile_table(e, E, c, MT, s0, s1, s2, s3, s4, offsets, tile_expert, tile_start, tile_rows,
+                                   n_tiles);
   __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int a = (e >= d) ? sc[e - d] : 0;
-    const int b = (e >= d) ? sf[e - d] : 0;
-    const int r = (e >= d) ? sr[e - d] : 0;
-    __syncthreads();
-    sc[e] += a;
-    sf[e] += b;
-    sr[e] += r;
-    __syncthreads();
-  }
-  const int off = sc[e] - c;
-  const int total_full = sf[1023];
-  if (e < E) offsets[e] = off;
-  if (e == E - 1) {
-    offsets[E] = sc[e];
-    *n_tiles = total_full + sr[1023];
-  }
-  const int tf = sf[e] - nf;
-  for (int i = 0; i < nf; ++i) {
-    tile_expert[tf + i] = e;
-    tile_start[tf + i] = off + i * MT;
-    tile_rows[tf + i] = MT;
-  }
-  if (nr) {
-    const int tr = total_full + sr[e] - 1;
-    tile_expert[tr] = e;
-    tile_start[tr] = off + nf * MT;
-    tile_rows[tr] = c - nf * MT;
-  }
+  s1[e] = small_expert(c, MT) ? kPosSmall : 0;   // the expert's position flag
   __syncthreads();
   cnt[e] = off;   // the expert's cursor
   __syncthreads();
@@ -230,7 +246,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
     if (x >= 0 && x < E) {
       const int q = atomicAdd(&cnt[x], 1);
       slots[q] = i;
-      pos[i] = q;
+      pos[i] = q | s1[x];
     } else {
       pos[i] = -1;
     }
@@ -276,17 +292,30 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
     int M, const uint8_t* __restrict__ xtok, int top_k, const int* __restrict__ n_tiles,
     const int* __restrict__ tile_expert, const int* __restrict__ tile_start, const int* __restrict__ tile_rows,
     const int* __restrict__ slots, _Float16* __restrict__ Q, int pairs, float inter_scale, float out_scale,
-    int n_chunks) {
+    int n_chunks, int n_chunks_small) {
   __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX_MOE> sm;
   __shared__ int tok[MT_MOE];
   __shared__ int slot_of_row[MT_MOE];
 
-  // A tile's chunks have consecutive block ids and so go round-robin over the
-  // XCDs; the same chunk of an expert's consecutive tiles lands on the same
-  // pair of XCDs, whose L2s serve that slice of the expert's weights.
-  const int ti = blockIdx.x / n_chunks;
-  const int chunk = blockIdx.x % n_chunks;
-  if (ti >= *n_tiles) return;
+  // Units: n_chunks per tile of a 192-row-chunk expert (listed first), then
+  // n_chunks_small per tile of the others.  A tile's chunks have consecutive
+  // block ids and so go round-robin over the XCDs; the same chunk of an
+  // expert's consecutive tiles lands on the same pair of XCDs, whose L2s serve
+  // that slice of the expert's weights.
+  const int nbig = n_tiles[1];
+  const int units_big = nbig * n_chunks;
+  int ti, chunk, nc;
+  if ((int)blockIdx.x < units_big) {
+    ti = blockIdx.x / n_chunks;
+    chunk = blockIdx.x % n_chunks;
+    nc = n_chunks;
+  } else {
+    const int u = blockIdx.x - units_big;
+    ti = nbig + u / n_chunks_small;
+    chunk = u % n_chunks_small;
+    nc = n_chunks_small;
+  }
+  if (ti >= n_tiles[0]) return;
   const int e = tile_expert[ti];
   const int start = tile_start[ti], rows = tile_rows[ti];
   if (threadIdx.x < MT_MOE) {
@@ -300,8 +329,8 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
   }
   __syncthreads();
   const int npan = I / 64;
-  const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
-  const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
+  const int r0 = (int)((long long)chunk * npan / nc) * 64;
+  const int r1 = (int)((long long)(chunk + 1) * npan / nc) * 64;
   const size_t gu_bytes = (size_t)I * (H / QK) * BLOCK_BYTES;   // one expert's gate (or up) matrix
   const size_t d_bytes = (size_t)H * (I / QK) * BLOCK_BYTES;    // one expert's down matrix
   const OutSlots out{Q, (size_t)pairs, H, out_scale, chunk, slot_of_row};
@@ -310,10 +339,12 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
 }
 
 // y[t][n] = fp16(sum_s p[t*k+s] * sum_c Q[c][t*k+s][n]) over the token's valid
-// slots; one block per token, eight outputs (one 16-byte load) per thread.
+// slots; one block per token, eight outputs (one 16-byte load) per thread.  A
+// slot's chunk count is n_chunks_small if its position carries kPosSmall.
 __global__ __launch_bounds__(256) void k_moe_combine(const _Float16* __restrict__ Q, const int* __restrict__ pos,
-                                                    const float* __restrict__ p, int top_k, int n_chunks, int pairs,
-                                                    int H, _Float16* __restrict__ y) {
+                                                    const float* __restrict__ p, int top_k, int n_chunks,
+                                                    int n_chunks_small, int pairs, int H,
+                                                    _Float16* __restrict__ y) {
   const int t = blockIdx.x;
   for (int n = threadIdx.x * 8; n < H; n += 256 * 8) {
     float acc[8];
@@ -321,11 +352,13 @@ __global__ __launch_bounds__(256) void k_moe_combine(const _Float16* __restrict_
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     for (int s = 0; s < top_k; ++s) {
       const int slot = t * top_k + s;
-      if (pos[slot] < 0) continue;   // invalid expert id: no contribution
+      const int q = pos[slot];
+      if (q < 0) continue;   // invalid expert id: no contribution
+      const int nc = (q & kPosSmall) ? n_chunks_small : n_chunks;
       float part[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) part[e] = 0.0f;
-      for (int c = 0; c < n_chunks; ++c) {
+      for (int c = 0; c < nc; ++c) {
         const half8 v = *reinterpret_cast<const half8*>(Q + ((size_t)c * (pairs + 1) + slot) * H + n);
 #pragma unroll
         for (int e = 0; e < 8; ++e) part[e] += (float)v[e];
@@ -369,22 +402,22 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
     hipLaunchKernelGGL(k_moe_count, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, pl.counts, dev_error);
     hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, stream, pl.counts, E, pl.offsets, pl.tile_expert,
                        pl.tile_start, pl.tile_rows, pl.n_tiles, MT_MOE);
-    hipLaunchKernelGGL(k_moe_scatter, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, pl.offsets, pl.cursor,
+    hipLaunchKernelGGL(k_moe_scatter, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, MT_MOE, pl.offsets, pl.cursor,
                        pl.slots, pl.pos);
   }
   hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream, static_cast<const _Float16*>(x),
                      hidden, M, pl.xtok);
-  const int n_chunks = chunks_for(inter);
+  const int n_chunks = chunks_for(inter), n_chunks_small = chunks_small_for(inter);
   const int max_tiles = max_tiles_for(M, top_k, E);
   timing_begin(stream);
-  hipLaunchKernelGGL(k_moe_fused16, dim3(max_tiles * n_chunks), dim3(MoeCfg::THREADS), 0, stream,
+  hipLaunchKernelGGL(k_moe_fused16, dim3(max_tiles * n_chunks_small), dim3(MoeCfg::THREADS), 0, stream,
                      static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
                      static_cast<const uint8_t*>(wd), hidden, inter, M, pl.xtok, top_k, pl.n_tiles, pl.tile_expert,
                      pl.tile_start, pl.tile_rows, pl.slots, pl.Q, n_slots, ldexpf(1.0f, -inter_shift),
-                     ldexpf(1.0f, inter_shift - out_shift), n_chunks);
+                     ldexpf(1.0f, inter_shift - out_shift), n_chunks, n_chunks_small);
   timing_end(stream);
-  hipLaunchKernelGGL(k_moe_combine, dim3(M), dim3(256), 0, stream, pl.Q, pl.pos, p, top_k, n_chunks, n_slots, hidden,
-                     static_cast<_Float16*>(y));
+  hipLaunchKernelGGL(k_moe_combine, dim3(M), dim3(256), 0, stream, pl.Q, pl.pos, p, top_k, n_chunks, n_chunks_small,
+                     n_slots, hidden, static_cast<_Float16*>(y));
   return hipGetLastError();
 }
 

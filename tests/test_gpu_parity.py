@@ -304,6 +304,22 @@ def test_moe_top1_weight1_matches_dense():
     assert_parity(ym, yd, "moe top-1 vs GPU dense")
 
 
+def test_moe_repeat_calls_bit_identical():
+    # experts of ~75 rows: a full tile plus a remainder of <= 16 rows, so these
+    # experts take 128-row chunks in all their tiles; the scatter places rows by
+    # atomics, yet a row's arithmetic must not depend on its tile: repeated
+    # calls give the same bits
+    E, H, I, M, k = 16, 256, 512, 300, 4
+    wg, wu, wd, x, ids, p = _moe_inputs(E, H, I, M, k, 26)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert any(0 < c % 64 <= 16 for c in counts) and any(c % 64 > 16 for c in counts)
+    y_ref, _ = O.moe(x, wg, wu, wd, ids, p, H, I)
+    b = max(0, int(np.ceil(np.log2(np.abs(y_ref).max() / 2 ** 13))))
+    ys = [_moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, b) for _ in range(3)]
+    assert_parity(ys[0], y_ref, "moe mixed chunkings")
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+
+
 def test_moe_permuted_slots_same_output():
     E, H, I, M, k = 8, 256, 512, 50, 3
     wg, wu, wd, x, ids, p = _moe_inputs(E, H, I, M, k, 23)
