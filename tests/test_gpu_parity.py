@@ -96,6 +96,19 @@ def test_prefill_other_shapes(H, I):
     assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill H={H} I={I}")
 
 
+@pytest.mark.parametrize("cfg", ["A", "B", "C", "D:32"])
+def test_prefill_alternative_units(cfg, monkeypatch):
+    # the alternative fused units behind ZINC_PREFILL_CFG (32x32x16 units on
+    # 32- or 64-token tiles, wider chunks; D with a forced chunk count), at a
+    # shape with several tiles, chunks and a ragged tail
+    monkeypatch.setenv("ZINC_PREFILL_CFG", cfg)
+    H, I, M = 512, 1280, 100
+    wg, wu, wd, x = _rand_mlp(77, H, I, M)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
+    a, b = shifts_for(y_ref, h_ref)
+    assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill config {cfg}")
+
+
 def test_prefill_m256_workload_full():
     w = S.WORKLOADS["prefill_m256"]
     wg, wu, wd = S.layer_weights(w.seed, 0, w.hidden, w.inter)
@@ -192,6 +205,19 @@ def test_decode_tiny_workload(M):
     x = S.workload_x(w)[:M]
     y_ref, _ = O.mlp(x, wg, wu, wd, w.hidden, w.inter)
     assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift), y_ref, f"decode tiny M={M}")
+
+
+@pytest.mark.parametrize("shape", ["0,8,0", "1,8,1", "0,4,3"])
+def test_decode_m1_launch_shapes(shape, monkeypatch):
+    # the M = 1 row kernels under the other launch shapes (rows in flight,
+    # waves per workgroup, workgroups per CU) that ZINC_DR_GU / ZINC_DR_DN select
+    monkeypatch.setenv("ZINC_DR_GU", shape)
+    monkeypatch.setenv("ZINC_DR_DN", shape)
+    H, I = 1024, 2816
+    wg, wu, wd, x = _rand_mlp(55, H, I, 1)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
+    a, b = shifts_for(y_ref, h_ref)
+    assert_parity(decode(wg, wu, wd, H, I, x, a, b), y_ref, f"decode M=1 shape {shape}")
 
 
 @pytest.mark.parametrize("M", [1, 4])
