@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,11 +37,18 @@ KERNEL_SOURCES = ("q4_swiglu_mlp_amd/csrc/fused16.hpp", "q4_swiglu_mlp_amd/csrc/
                   "q4_swiglu_mlp_amd/csrc/q4k_device.hpp", "q4_swiglu_mlp_amd/csrc/k_prefill.hip")
 
 
+_CODE_TOKENS = re.compile(r'("(?:\\.|[^"\\])*")|//[^\n]*|/\*.*?\*/', re.S)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the prefill kernel's sources with comments removed and
+    whitespace collapsed: the stored traffic counters stay valid across
+    comment edits and become stale on any change to the code."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = _CODE_TOKENS.sub(lambda m: m.group(1) or " ", f.read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -1,17 +1,18 @@
-// Fused Q4_K SwiGLU unit for 64-token tiles (the dense prefill).
+// Fused Q4_K SwiGLU unit for token tiles of MT = 64 (the dense prefill) or 80
+// (the MoE, where one tile then holds a whole expert of up to 80 rows).
 //
-// A unit is one (64-token tile, intermediate chunk of at most ICMAX rows)
+// A unit is one (MT-token tile, intermediate chunk of at most ICMAX rows)
 // pair, run by one workgroup of 12 waves:
 //
 //   phase 1  gate and up for the chunk: each wave owns a 16-row tile of the
 //            chunk and walks the whole hidden dimension one Q4_K super-block
 //            column at a time with 16x16x32 fp16 MFMAs (fp32 accumulation).  A
 //            lane decodes eight weights per MFMA step (its row r = l%16, octet
-//            o = l/16) and that operand meets all four 16-token groups of the
-//            tile, so each decoded weight serves 64 tokens.  SwiGLU is applied
-//            in registers and the fp16 strip [64 tokens x chunk] lands in LDS.
+//            o = l/16) and that operand meets every 16-token group of the
+//            tile, so each decoded weight serves MT tokens.  SwiGLU is applied
+//            in registers and the fp16 strip [MT tokens x chunk] lands in LDS.
 //   phase 2  the down projection of the strip (fu_phase2, 32x32x16 MFMAs, two
-//            32-token tiles per decoded W_down operand).
+//            or three 32-token tiles per decoded W_down operand).
 //
 // Weights are decoded in registers on the way into the multiply ("VGPR
 // pressure caps the fused RDNA4 prefill GEMM at nine waves", "What the fused
@@ -27,7 +28,7 @@
 // token, by k_stage_x16 in exactly that order, with the 32-element means the
 // -dmin*m term is contracted against (one MFMA per four blocks, lane octet o
 // supplying block 4g+o's eight -32*dmin*m values), so a unit copies the rows
-// of its 64 tokens into LDS with plain 16-byte moves: a contiguous token range
+// of its tokens into LDS with plain 16-byte moves: a contiguous token range
 // for the dense prefill, the routed rows of one expert for the MoE.
 #pragma once
 
@@ -60,9 +61,17 @@ constexpr int X16_TP_BYTES = X16_TP * 16; // bytes per token and column
 // {0..3} of a block: MFMA i = 4(c/2) + j%4, octet o = 2(c%2) + j/4.
 __host__ __device__ constexpr int x16_slot(int c, int j) { return (4 * (c >> 1) + (j & 3)) * 4 + 2 * (c & 1) + (j >> 2); }
 
-template <int ICMAX>
+template <int ICMAX, int MT_ = 64>
 struct Fused16Cfg {
-  static constexpr int MT = 64;                       // tokens per unit
+  static constexpr int MT = MT_;                      // tokens per unit: 64, or 80 (the MoE's)
+  static constexpr int NGMAX = MT / 16;               // 16-token groups
+  static constexpr int MTS = (MT + 31) / 32 * 32;     // strip rows: whole 32-token halves of phase 2
+  // activation columns in LDS: four (copy two ahead, a barrier every two
+  // blocks) for 64 tokens; three (copy one ahead, a barrier every block) for
+  // 80, which is what fits beside the unit's other LDS
+  static constexpr int SLOTS = (MT <= 64) ? 4 : 3;
+  static constexpr int AHEAD = SLOTS - 2;
+  static constexpr int PIECES = MT * X16_TP;          // 16-byte pieces of one staged column
   static constexpr int WAVES = 12;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int XS = X16_ROW;
@@ -70,24 +79,25 @@ struct Fused16Cfg {
   static constexpr int NBMAX = (ICMAX - 64) / 256 + 2;  // W_down blocks a chunk can touch
   static constexpr int HSS = ((8 * NBMAX + 15) / 16) * 16;
   static constexpr int XRING = 8;                     // block columns of means kept (two correction groups)
-  static constexpr int NCOPY = (X16_PIECES + THREADS - 1) / THREADS;
-  static constexpr int NJUNK = NCOPY * THREADS - X16_PIECES;   // copy slots past the column
+  static constexpr int NCOPY = (PIECES + THREADS - 1) / THREADS;
+  static constexpr int NJUNK = NCOPY * THREADS - PIECES;   // copy slots past the column
+  static_assert(MT % 16 == 0 && MT >= 64 && MT <= 80, "64 or 80 tokens per unit");
   static_assert(ICMAX % 64 == 0, "chunks are whole 64-row panels");
   static_assert(ICMAX / 16 <= WAVES, "one 16-row tile per wave");
 };
 
-template <int ICMAX>
+template <int ICMAX, int MT_ = 64>
 struct Fused16Smem {
-  using C = Fused16Cfg<ICMAX>;
+  using C = Fused16Cfg<ICMAX, MT_>;
   union {
-    // phase 1: activation columns in operand order, slot = column % 4 (the
-    // column being read, the next one, and the two being staged)
-    _Float16 xs[4][C::MT * C::XS];
+    // phase 1: activation columns in operand order, slot = column % SLOTS
+    // (the column being read and the ones being staged)
+    _Float16 xs[C::SLOTS][C::MT * C::XS];
     // after phase 1 (the same memory): the intermediate strip in panel order
-    // and its 32-row means (block-aligned, zero-padded)
+    // and its 32-row means (block-aligned, zero-padded), MTS token rows
     struct {
-      _Float16 hs[C::MT * C::HS];
-      _Float16 hsum[C::MT * C::HSS];
+      _Float16 hs[C::MTS * C::HS];
+      _Float16 hsum[C::MTS * C::HSS];
     } s;
   } u;
   _Float16 xm[C::XRING][C::MT * 8];     // 32-means per block column, ring
@@ -161,10 +171,10 @@ __device__ __forceinline__ X16Plan<C::NCOPY> fu16_plan(const int* __restrict__ t
   for (int it = 0; it < C::NCOPY; ++it) {
     const int p = (int)threadIdx.x + C::THREADS * it;
     const int t = p / X16_TP, j = p - t * X16_TP;
-    const bool in = p < X16_PIECES;
+    const bool in = p < C::PIECES;
     pl.src[it] = in ? ((uint32_t)tok[t] * nbH * X16_TP + j) * 16u : 0u;
     pl.kind[it] = !in ? 2u : (j < X16_TP - 1) ? 0u : 1u;
-    pl.dst[it] = !in ? (uint32_t)(p - X16_PIECES) * 8u : (j < X16_TP - 1) ? (uint32_t)(t * X16_ROW + j * 8) : (uint32_t)(t * 8);
+    pl.dst[it] = !in ? (uint32_t)(p - C::PIECES) * 8u : (j < X16_TP - 1) ? (uint32_t)(t * X16_ROW + j * 8) : (uint32_t)(t * 8);
   }
   return pl;
 }
@@ -176,22 +186,29 @@ struct X16Copy {
   u32x4_16 v[N];
 };
 
+// Pieces [A, B) of a thread's share of column kb (the whole share by default).
+template <class C, int A = 0, int B = C::NCOPY>
+__device__ __forceinline__ void fu16_load_part(const uint8_t* __restrict__ xtok, int kb,
+                                               const X16Plan<C::NCOPY>& pl, X16Copy<C::NCOPY>& r) {
+  const uint8_t* col = xtok + (size_t)kb * X16_TP_BYTES;
+#pragma unroll
+  for (int it = A; it < B; ++it) r.v[it] = *reinterpret_cast<const u32x4_16*>(col + pl.src[it]);
+}
+
 template <class C>
 __device__ __forceinline__ X16Copy<C::NCOPY> fu16_load_col(const uint8_t* __restrict__ xtok, int kb,
                                                            const X16Plan<C::NCOPY>& pl) {
   X16Copy<C::NCOPY> r;
-  const uint8_t* col = xtok + (size_t)kb * X16_TP_BYTES;
-#pragma unroll
-  for (int it = 0; it < C::NCOPY; ++it) r.v[it] = *reinterpret_cast<const u32x4_16*>(col + pl.src[it]);
+  fu16_load_part<C>(xtok, kb, pl, r);
   return r;
 }
 
-template <class C>
+template <class C, int A = 0, int B = C::NCOPY>
 __device__ __forceinline__ void fu16_store_col(const X16Copy<C::NCOPY>& xc, const X16Plan<C::NCOPY>& pl,
                                                _Float16* __restrict__ xs, _Float16* __restrict__ xm,
                                                _Float16* __restrict__ junk) {
 #pragma unroll
-  for (int it = 0; it < C::NCOPY; ++it) {
+  for (int it = A; it < B; ++it) {
     _Float16* base = (pl.kind[it] == 0u) ? xs : (pl.kind[it] == 1u) ? xm : junk;
     *reinterpret_cast<u32x4_16*>(base + pl.dst[it]) = xc.v[it];
   }
@@ -282,8 +299,8 @@ struct OutQuads {
   float scale;
   int chunk;
   int row0;   // the unit's first token
-  template <int NTT>
-  __device__ __forceinline__ void store(const float16v (&acc)[2], int nt, int l32, int h) const {
+  template <int NTT, int NA>
+  __device__ __forceinline__ void store(const float16v (&acc)[NA], int nt, int l32, int h) const {
     const size_t quad_stride = (size_t)H * 4;   // halves per token quad
     _Float16* po = P + ((size_t)chunk * (Mpad / 4) + row0 / 4 + h) * quad_stride + (size_t)(nt * 32 + l32) * 4;
 #pragma unroll
@@ -299,7 +316,7 @@ struct OutQuads {
   }
 };
 
-// Phase 2 of the 64-token unit: the down projection of the chunk [r0, r1) for
+// Phase 2 of the unit: the down projection of the chunk [r0, r1) for
 // all hidden output rows, from the strip in LDS.  The same contraction as
 // fu_phase2 (32x32x16 MFMAs, one decoded W_down operand for both 32-token
 // halves, the min correction against the strip's 32-row means), with the
@@ -325,9 +342,9 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
 
   auto down_tile = [&](DownTileData<NP, NB>& dt, int nt, const uint8_t* nxt) {
     const uint8_t* nq = nxt + 16 + 16 * h;
-    float16v acc[2];
+    float16v acc[C::MTS / 32];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < C::MTS / 32; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[tt][e] = 0.0f;
     auto panel = [&](auto pc) {
@@ -407,18 +424,19 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
   }
 }
 
-// One fused 64-token unit.  xtok = the staged activation (k_stage_x16); tok =
-// the unit's 64 token indices (LDS, visible to all threads before the call;
-// the zero token M for padding rows); rows = how many of them are real (1..64,
+// One fused MT-token unit.  xtok = the staged activation (k_stage_x16); tok =
+// the unit's MT token indices (LDS, visible to all threads before the call;
+// the zero token M for padding rows); rows = how many of them are real (1..MT,
 // the rest are padding: 16-token groups and 32-token halves wholly past it
 // are skipped); out = the phase-2 output policy.
-template <int ICMAX, class Out>
+template <int ICMAX, class Out, int MT_>
 __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
                                              const uint8_t* __restrict__ wd, int H, int I,
                                              const uint8_t* __restrict__ xtok, const int* __restrict__ tok,
                                              int rows, int r0, int r1, float inter_scale, const Out& out,
-                                             Fused16Smem<ICMAX>& sm) {
-  using C = Fused16Cfg<ICMAX>;
+                                             Fused16Smem<ICMAX, MT_>& sm) {
+  using C = Fused16Cfg<ICMAX, MT_>;
+  constexpr int NGMAX = C::NGMAX, SLOTS = C::SLOTS, AHEAD = C::AHEAD, MTS = C::MTS;
   constexpr int XS = C::XS, HS = C::HS, HSS = C::HSS, MT = C::MT;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, o = lane >> 4, sel = (o >> 1) & 1;
@@ -439,29 +457,36 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   // slots never written in this unit; zero operands need finite partners
   for (int i = threadIdx.x; i < C::XRING * MT * 8; i += C::THREADS) (&sm.xm[0][0])[i] = (_Float16)0.0f;
 
-  f32x4_16 accg[4], accu[4];
+  f32x4_16 accg[NGMAX], accu[NGMAX];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < NGMAX; ++g)
 #pragma unroll
     for (int e = 0; e < 4; ++e) accg[g][e] = accu[g][e] = 0.0f;
 
-  // prologue: columns 0 and 1 staged
+  // prologue: columns 0 .. AHEAD-1 staged
   const X16Plan<C::NCOPY> xplan = fu16_plan<C>(tok, nbH);
   {
     const X16Copy<C::NCOPY> x0 = fu16_load_col<C>(xtok, 0, xplan);
     const int c1 = nbH > 1 ? 1 : 0;
-    const X16Copy<C::NCOPY> x1 = fu16_load_col<C>(xtok, c1, xplan);
-    lds_barrier();   // ring zeroed before the means land in it
-    fu16_store_col<C>(x0, xplan, sm.u.xs[0], sm.xm[0], sm.junk);
-    fu16_store_col<C>(x1, xplan, sm.u.xs[1], sm.xm[c1], sm.junk);
+    if constexpr (AHEAD == 2) {
+      const X16Copy<C::NCOPY> x1 = fu16_load_col<C>(xtok, c1, xplan);
+      lds_barrier();   // ring zeroed before the means land in it
+      fu16_store_col<C>(x0, xplan, sm.u.xs[0], sm.xm[0], sm.junk);
+      fu16_store_col<C>(x1, xplan, sm.u.xs[1], sm.xm[c1], sm.junk);
+    } else {
+      lds_barrier();
+      fu16_store_col<C>(x0, xplan, sm.u.xs[0], sm.xm[0], sm.junk);
+    }
   }
 
   // The column loop, once for waves with a row tile (ACT) and once for idle
   // waves, which only help stage the activation; both meet the same barriers.
   //
-  // Staging.  Column c is copied into slot c % 4 during block c-2 (MFMA step
-  // 4); a barrier at the top of every even block publishes the two columns
-  // copied in the two blocks before and releases the two slots read there.
+  // Staging.  Column c is copied into slot c % SLOTS during block c - AHEAD
+  // (MFMA step 4), SLOTS = AHEAD + 2.  A barrier at the top of every AHEAD-th
+  // block publishes the columns copied before it; the slot written in block
+  // kb held column kb - 2, which every wave finished reading before the last
+  // barrier.
   //
   // Pipeline.  Within a block an active wave's MFMA steps are
   // software-pipelined: the B operands and the decoded A operands of step i+1
@@ -486,11 +511,16 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
       // end they re-read the last column (never used), so no branch ever
       // surrounds a load
       const int kn = (kb + 1 < nbH) ? kb + 1 : kb;
-      const int kx = (kb + 2 < nbH) ? kb + 2 : nbH - 1;
+      const int kx = (kb + AHEAD < nbH) ? kb + AHEAD : nbH - 1;
       const uint32_t noff = wrow_off + (uint32_t)kn * BLOCK_BYTES;
-      if ((kb & 1) == 0) lds_barrier();
-      const X16Copy<C::NCOPY> xc = fu16_load_col<C>(xtok, kx, xplan);
-      _Float16* const xs_next = sm.u.xs[(kb + 2) & 3];
+      if (kb % AHEAD == 0) lds_barrier();
+      // an 80-token column is copied in two halves (the second loaded once
+      // the first is stored), which keeps half the copy registers live
+      constexpr bool SPLIT = C::NCOPY >= 4;
+      constexpr int HALF = SPLIT ? (C::NCOPY + 1) / 2 : C::NCOPY;
+      X16Copy<C::NCOPY> xc;
+      fu16_load_part<C, 0, HALF>(xtok, kx, xplan, xc);
+      _Float16* const xs_next = sm.u.xs[(kb + AHEAD) % SLOTS];
       _Float16* const xm_next = sm.xm[kx & (C::XRING - 1)];
       if constexpr (ACT) {
         const Lane16S sg = lane16_scales(as_u4(hg), sel), su = lane16_scales(as_u4(hu), sel);
@@ -503,8 +533,8 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
         // keep the column's loads here, a whole block step ahead of their use
         // (left alone, the scheduler sinks them below the MFMAs)
         __builtin_amdgcn_sched_barrier(0);
-        const _Float16* xb = sm.u.xs[kb & 3] + xlane;
-        auto load_b = [&](int i, half8 (&b)[4]) {
+        const _Float16* xb = sm.u.xs[kb % SLOTS] + xlane;
+        auto load_b = [&](int i, half8 (&b)[NGMAX]) {
 #pragma unroll
           for (int g = 0; g < NG; ++g) b[g] = *reinterpret_cast<const half8*>(xb + g * 16 * XS + i * 32);
         };
@@ -514,13 +544,17 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
           ag = (i < 4) ? dequant_dword_sc(qg, sg.lo0, sg.hi0, nk) : dequant_dword_sc(qg, sg.lo1, sg.hi1, nk);
           au = (i < 4) ? dequant_dword_sc(qu, su.lo0, su.hi0, nk) : dequant_dword_sc(qu, su.lo1, su.hi1, nk);
         };
-        half8 bc[4], bn[4], agc, auc, agn, aun;
+        // Five token groups leave no room for a second set of B operands:
+        // there each group's B is refilled in place right after its two
+        // MFMAs, a whole step ahead of its next use.
+        constexpr bool INPLACE = NG > 4;
+        half8 bc[NGMAX], bn[INPLACE ? 1 : NGMAX], agc, auc, agn, aun;
         load_b(0, bc);
         decode(0, agc, auc);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           if (i < 7) {
-            load_b(i + 1, bn);
+            if constexpr (!INPLACE) load_b(i + 1, bn);
             decode(i + 1, agn, aun);
           }
           if (i == 3) {   // the first quant run is decoded: refill it in place
@@ -528,13 +562,20 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
             qu0 = *reinterpret_cast<const u32x4_16*>(wu + (noff + 16 + 16 * o));
             __builtin_amdgcn_sched_barrier(0);
           }
+          // column kx into its slot and the means ring: the last barrier
+          // released that slot, and the ring slot written is none of the
+          // four the corrections of blocks up to kb+1 read (past the end a
+          // rewrite of data nobody reads again, or of the same values)
           if (i == 4) {
-            // column kx into its slot and the means ring: the last barrier
-            // released that slot, and the ring slot written is none of the
-            // four the corrections of blocks up to kb+1 read (past the end a
-            // rewrite of data nobody reads again, or of the same values)
-            fu16_store_col<C>(xc, xplan, xs_next, xm_next, sm.junk);
+            fu16_store_col<C, 0, HALF>(xc, xplan, xs_next, xm_next, sm.junk);
+            if constexpr (SPLIT) fu16_load_part<C, HALF, C::NCOPY>(xtok, kx, xplan, xc);
             __builtin_amdgcn_sched_barrier(0);
+          }
+          if constexpr (SPLIT) {
+            if (i == 7) {
+              fu16_store_col<C, HALF, C::NCOPY>(xc, xplan, xs_next, xm_next, sm.junk);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
           if (i == 6) {   // and the second
             qg1 = *reinterpret_cast<const u32x4_16*>(wg + (noff + 80 + 16 * o));
@@ -545,20 +586,38 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
           for (int g = 0; g < NG; ++g) {
             accg[g] = mfma16x16(agc, bc[g], accg[g]);
             accu[g] = mfma16x16(auc, bc[g], accu[g]);
+            if constexpr (INPLACE) {
+              if (i < 7) bc[g] = *reinterpret_cast<const half8*>(xb + g * 16 * XS + (i + 1) * 32);
+            }
           }
           if (i < 7) {
+            if constexpr (!INPLACE) {
 #pragma unroll
-            for (int g = 0; g < NG; ++g) bc[g] = bn[g];
+              for (int g = 0; g < NG; ++g) bc[g] = bn[g];
+            }
             agc = agn;
             auc = aun;
           }
-          // issue order of the step: the next B reads, then the MFMAs with
-          // the next decode's VALU work threaded between them
-          __builtin_amdgcn_sched_group_barrier(0x100, NG, 0);
+          if constexpr (INPLACE) {
+            // issue order: per group its two MFMAs with decode VALU work
+            // between them, then that group's B refill
 #pragma unroll
-          for (int k = 0; k < 2 * NG; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+            for (int g = 0; g < NG; ++g) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+          } else {
+            // issue order of the step: the next B reads, then the MFMAs with
+            // the next decode's VALU work threaded between them
+            __builtin_amdgcn_sched_group_barrier(0x100, NG, 0);
+#pragma unroll
+            for (int k = 0; k < 2 * NG; ++k) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+            }
           }
         }
         // min correction once per four blocks (or at the last): octet o holds
@@ -577,6 +636,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
           cu = u32x4_16{0u, 0u, 0u, 0u};
         }
       } else {
+        if constexpr (SPLIT) fu16_load_part<C, HALF, C::NCOPY>(xtok, kx, xplan, xc);
         fu16_store_col<C>(xc, xplan, xs_next, xm_next, sm.junk);
       }
     }
@@ -586,10 +646,13 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   using I4 = std::integral_constant<int, 4>;
-  const int ng = (rows + 15) >> 4;   // uniform, 1..4
+  using IG = std::integral_constant<int, NGMAX>;
+  const int ng = (rows + 15) >> 4;   // uniform, 1..NGMAX
   if (!act)
-    column_loop(std::false_type{}, I4{});
-  else if (ng >= 4)
+    column_loop(std::false_type{}, IG{});
+  else if (ng >= NGMAX)
+    column_loop(std::true_type{}, IG{});
+  else if (NGMAX > 4 && ng == 4)
     column_loop(std::true_type{}, I4{});
   else if (ng == 3)
     column_loop(std::true_type{}, I3{});
@@ -598,6 +661,9 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   else
     column_loop(std::true_type{}, I1{});
   lds_barrier();   // the strip below overwrites the activation slots
+  if constexpr (MTS > MT) {   // token rows past the unit's MT: a zero strip (phase 2 reads whole 32-token halves)
+    for (int i = threadIdx.x; i < (MTS - MT) * HS; i += C::THREADS) sm.u.s.hs[MT * HS + i] = (_Float16)0.0f;
+  }
 
   // SwiGLU in registers -> fp16 strip (panel order) and the 32-row sums.
   // Accumulator e of lane (r, o) in group g: row 4o + e of the tile, token 16g + r.
@@ -606,7 +672,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
     const int jg = off * 64 + rt * 16;                  // row from the start of the chunk's first W_down block
     const int slot = 8 * (jg >> 8) + sb_slot((jg >> 5) & 7);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < NGMAX; ++g) {
       _Float16 hv[4];
       float s4 = 0.0f;
 #pragma unroll
@@ -629,7 +695,8 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   }
   if (threadIdx.x == 0) sm.p2_next = 2 * C::WAVES;
   lds_barrier();   // strip and sums complete
-  for (int i = threadIdx.x; i < MT * HSS; i += C::THREADS) sm.u.s.hsum[i] = (_Float16)(sm.hsum32[i] * 0.03125f);
+  for (int i = threadIdx.x; i < MTS * HSS; i += C::THREADS)
+    sm.u.s.hsum[i] = (i < MT * HSS) ? (_Float16)(sm.hsum32[i] * 0.03125f) : (_Float16)0.0f;
   lds_barrier();
 
   // ---------------- phase 2: down projection over this chunk ----------------
@@ -642,6 +709,12 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
       default: fu16_phase2<C, ICMAX, 3, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
     }
   };
+  if constexpr (MTS > 64) {
+    if (rows > 64) {
+      phase2(std::integral_constant<int, 3>{});
+      return;
+    }
+  }
   if (rows > 32)
     phase2(I2{});
   else

@@ -11,8 +11,8 @@
 //   3. k_moe_scatter  slot indices grouped by expert, and each slot's position
 //   4. k_stage_x16    the activation per token in the fused unit's operand
 //                     order (fused16.hpp), plus an all-zero token
-//   5. k_moe_fused16  one 64-token fused unit (fused16.hpp) per (tile of up
-//                     to 64 routed rows of one expert, intermediate chunk):
+//   5. k_moe_fused16  one 80-token fused unit (fused16.hpp) per (tile of up
+//                     to 80 routed rows of one expert, intermediate chunk):
 //                     192-row chunks, or 128-row chunks for every tile of an
 //                     expert whose remainder tile is small; blocks past the
 //                     device-side unit count exit at once.  Each row's expert
@@ -37,8 +37,8 @@ namespace zinc {
 namespace {
 
 constexpr int ICMAX_MOE = 192;  // intermediate rows per chunk (three 64-row panels)
-constexpr int MT_MOE = 64;      // routed rows per tile
-using MoeCfg = Fused16Cfg<ICMAX_MOE>;
+constexpr int MT_MOE = 80;      // routed rows per tile: an expert of up to 80 rows is one tile
+using MoeCfg = Fused16Cfg<ICMAX_MOE, MT_MOE>;
 
 struct MoePlan {
   int* counts;       // [E]
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
   }
 }
 
-// MoE output of the 64-token unit: unit row r belongs to slot slot_of_row[r];
+// MoE output of the 80-token unit: unit row r belongs to slot slot_of_row[r];
 // the fp16 partial, at the output scale, goes to Q[chunk][slot][n].  Padding
 // rows carry slot = pairs, a junk row after the chunk's pairs (no branch
 // around the stores).  Lanes run along n, so a store instruction writes two
@@ -265,9 +265,9 @@ struct OutSlots {
   int H;
   float scale;
   int chunk;
-  const int* slot_of_row;   // LDS, 64 entries
-  template <int NTT>
-  __device__ __forceinline__ void store(const float16v (&acc)[2], int nt, int l32, int h) const {
+  const int* slot_of_row;   // LDS, one entry per strip row (96)
+  template <int NTT, int NA>
+  __device__ __forceinline__ void store(const float16v (&acc)[NA], int nt, int l32, int h) const {
     const size_t rows_bytes = (pairs + 1) * (size_t)H * sizeof(_Float16);   // < 4 GiB (checked by the caller)
     const __amdgpu_buffer_rsrc_t qc = __builtin_amdgcn_make_buffer_rsrc(Q + (size_t)chunk * (pairs + 1) * H, (short)0,
                                                                        (int)rows_bytes, 0x00020000);
@@ -293,9 +293,9 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
     const int* __restrict__ tile_expert, const int* __restrict__ tile_start, const int* __restrict__ tile_rows,
     const int* __restrict__ slots, _Float16* __restrict__ Q, int pairs, float inter_scale, float out_scale,
     int n_chunks, int n_chunks_small) {
-  __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX_MOE> sm;
+  __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX_MOE, MT_MOE> sm;
   __shared__ int tok[MT_MOE];
-  __shared__ int slot_of_row[MT_MOE];
+  __shared__ int slot_of_row[MoeCfg::MTS];   // rows past MT_MOE (phase 2's last 32-token half): the junk row
 
   // Units: n_chunks per tile of a 192-row-chunk expert (listed first), then
   // n_chunks_small per tile of the others.  A tile's chunks have consecutive
@@ -318,13 +318,13 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
   if (ti >= n_tiles[0]) return;
   const int e = tile_expert[ti];
   const int start = tile_start[ti], rows = tile_rows[ti];
-  if (threadIdx.x < MT_MOE) {
+  if (threadIdx.x < MoeCfg::MTS) {
     int t = M, sl = pairs;   // padding rows: the zero token, the junk row
     if ((int)threadIdx.x < rows) {
       sl = slots[start + threadIdx.x];
       t = sl / top_k;
     }
-    tok[threadIdx.x] = t;
+    if (threadIdx.x < MT_MOE) tok[threadIdx.x] = t;
     slot_of_row[threadIdx.x] = sl;
   }
   __syncthreads();
