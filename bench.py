@@ -284,6 +284,32 @@ def moe_lines(args, torch, np, Z, S, dev, t):
         "mfma_frac_fused_kernel": round(flops / (kern * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
     })
     log(f"[bench] {out[-1]}")
+
+    # the router on the GPU (top-8 of 64 logits per token), alone and feeding
+    # the expert call: the MoE block with no host read-back between the two
+    glog = t(S.workload_router_logits(w))
+    rids = torch.empty((w.M, w.top_k), dtype=torch.int32, device=dev)
+    rp = torch.empty((w.M, w.top_k), dtype=torch.float32, device=dev)
+
+    def rcall(_i):
+        Z.zinc_moe_route_topk(glog, w.top_k, expert_ids=rids, expert_weights=rp)
+
+    def lcall(i):
+        rcall(i)
+        eg, eu, ed = sets[i % 2]
+        Z.zinc_moe_q4k_experts(eg, eu, ed, w.n_experts, w.hidden, w.inter, gx, rids, rp, w.inter_shift, w.out_shift,
+                               y=y, workspace=ws)
+
+    rwall, rms = time_calls(rcall, steps, 10, torch)
+    lwall, _ = time_calls(lcall, steps, 10, torch)
+    out.append({
+        "workload": "MoE router, top-8 of 64 fp32 logits, M=512; then router + experts as one block",
+        "router_us_per_call": round(rwall / steps * 1e6, 3),
+        "router_kernel_us": round(sum(rms) / len(rms) * 1e3, 3),
+        "router_plus_experts_us": round(lwall / steps * 1e6, 3),
+        "router_plus_experts_tokens_per_s": round(w.M / (lwall / steps), 1),
+    })
+    log(f"[bench] {out[-1]}")
     return out
 
 

@@ -151,6 +151,32 @@ int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_dow
                          void* stream);
 
 /*
+ * MoE router: for every token t, the top_k experts with the largest router
+ * logits and their mixing weights, written to the device buffers that
+ * zinc_moe_q4k_experts reads, so no host read-back separates the router from
+ * the experts ("Four bottlenecks, one CUDA backend", "Bottleneck 2": every MoE
+ * layer computes router logits and picks the top-k experts; "What's next, and
+ * what it's worth": the router's remaining per-layer sync).
+ *   logits          fp32 [M x n_experts] row-major, device
+ *   expert_ids      int32 [M x top_k], device, written: slot s holds the expert
+ *                   of the s-th largest logit; equal logits go to the lower
+ *                   expert index first; a NaN logit ranks below every number
+ *   expert_weights  fp32 [M x top_k], device, written: the softmax of the chosen
+ *                   logits, exp(l_s - l_0) / sum_j exp(l_j - l_0) (one NaN among
+ *                   them makes the token's weights NaN)
+ * This is the reading taken of the pages' "top-k experts" plus mixing weights:
+ * the softmax is over the k chosen logits (the full softmax renormalised over
+ * the chosen experts, which is the same value).
+ * Limits: 1 <= top_k <= min(64, n_experts), n_experts <= 1024, M >= 0,
+ * M * top_k <= 2^24 (else ZINC_ERR_ARG); M == 0 then returns ZINC_OK without
+ * reading the pointers (an empty buffer may be NULL); otherwise pointers must
+ * be non-NULL (ZINC_ERR_NULL) and 4-byte aligned (ZINC_ERR_ALIGN).
+ * One kernel, enqueued on `stream`; no workspace.
+ */
+int zinc_moe_route_topk(const float* logits, int32_t M, int32_t n_experts, int32_t top_k,
+                        int32_t* expert_ids, float* expert_weights, void* stream);
+
+/*
  * Kernel timing for benchmarks and profiles (off by default; not needed for
  * correct use).  After zinc_timing_enable(capacity), every prefill, decode and
  * MoE call records a HIP event pair on its stream immediately around its main

@@ -21,12 +21,16 @@ Plain, slow, obviously-correct float64 numpy:
 * ``moe``: the batched-expert form of "Four bottlenecks, one CUDA backend",
   "Bottleneck 2": each token's output is the mixing-weighted sum of its chosen
   experts' MLP outputs; expert ids are inputs.
+* ``route_topk``: the router step before it -- per token the top-k experts by
+  router logit and the softmax of the chosen logits.
 
 Every function is pinned in ``tests/test_oracle.py`` against things other than
 itself: hand-built blocks with closed-form weights, a bit-level brute-force
 field reader, silu identities and a library sigmoid, brute-force loops on tiny
 shapes, one-hot / zero / unit-weight probes, exact scaling and permutation
-invariants, and MoE reductions to the dense MLP.
+invariants, and MoE reductions to the dense MLP; the router against a
+brute-force search over expert subsets, tie and NaN rules written out, a
+library softmax, and the renormalised full softmax.
 """
 from __future__ import annotations
 
@@ -152,6 +156,42 @@ def moe(x, wg_blobs, wu_blobs, wd_blobs, ids, p, hidden: int, inter: int):
         ye, _ = mlp(x64[rows], wg_blobs[e], wu_blobs[e], wd_blobs[e], hidden, inter)
         np.add.at(y, rows, p64[rows, slots][:, None] * ye)
     return y, bad
+
+
+# ----------------------------------------------------------------------------
+# MoE router: top-k experts and mixing weights
+# ----------------------------------------------------------------------------
+def route_topk(logits, top_k: int):
+    """The router step of "Four bottlenecks, one CUDA backend", "Bottleneck 2"
+    (every MoE layer computes router logits and picks the top-k experts).
+
+    Per token: the ``top_k`` experts with the largest logits, largest first;
+    equal logits in increasing expert index; a NaN logit ranks below every
+    number.  Mixing weights: the softmax of the chosen logits (the reading
+    taken: the full softmax renormalised over the chosen experts, the same
+    value), computed in float64 as exp(l_s - l_0) / sum_j exp(l_j - l_0) with
+    l_0 the first (largest) chosen logit.
+
+    ``logits`` float32 ``[M, E]``.  Returns ``(ids int32 [M, k], p float64 [M, k])``."""
+    L = np.asarray(logits, dtype=np.float32)
+    M, E = L.shape
+    ids = np.empty((M, top_k), dtype=np.int32)
+    p = np.empty((M, top_k), dtype=np.float64)
+    for t in range(M):
+        row = [float(v) for v in L[t]]
+
+        def rank(j):
+            v = row[j]
+            is_number = not np.isnan(v)
+            return (is_number, v if is_number else 0.0, -j)
+
+        chosen = sorted(range(E), key=rank, reverse=True)[:top_k]
+        v = np.array([row[j] for j in chosen], dtype=np.float64)
+        with np.errstate(invalid="ignore"):
+            e = np.exp(v - v[0])
+            p[t] = e / e.sum()
+        ids[t] = chosen
+    return ids, p
 
 
 # ----------------------------------------------------------------------------

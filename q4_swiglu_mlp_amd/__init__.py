@@ -11,6 +11,7 @@ Functions carry the C entry points' names and take torch tensors:
 * ``zinc_mlp_q4k_prefill(w_gate, w_up, w_down, hidden, inter, x, ...)`` -> fp16 y
 * ``zinc_mlp_q4k_decode(...)`` (1 <= M <= 8) -> fp16 y
 * ``zinc_moe_q4k_experts(w_gate, w_up, w_down, n_experts, hidden, inter, x, ids, p, ...)`` -> fp16 y
+* ``zinc_moe_route_topk(logits, top_k)`` -> (int32 ids, fp32 weights), both on the GPU
 
 Q4_K weights are uint8 tensors holding the raw 144-byte blocks ([rows,
 cols/256, 144] or flat); x is fp16 ``[M, hidden]``.
@@ -39,6 +40,7 @@ EXPORTS = (
     "zinc_mlp_q4k_decode",
     "zinc_moe_q4k_experts_workspace_size",
     "zinc_moe_q4k_experts",
+    "zinc_moe_route_topk",
     "zinc_timing_enable",
     "zinc_timing_collect",
     "zinc_timing_disable",
@@ -63,7 +65,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
-            "(python -c 'import __graft_entry__ as g; g.build()' or python q4_swiglu_mlp_amd/build.py)")
+            "(python q4_swiglu_mlp_amd/build.py, or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.zinc_strerror.restype = ctypes.c_char_p
@@ -84,6 +86,8 @@ def _load() -> ctypes.CDLL:
     lib.zinc_moe_q4k_experts_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.zinc_moe_q4k_experts.restype = ctypes.c_int
     lib.zinc_moe_q4k_experts.argtypes = [P, P, P, I32, I32, I32, P, I32, P, P, I32, P, I32, I32, P, SZ, P, P]
+    lib.zinc_moe_route_topk.restype = ctypes.c_int
+    lib.zinc_moe_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
     lib.zinc_timing_enable.restype = ctypes.c_int
     lib.zinc_timing_enable.argtypes = [I32]
     lib.zinc_timing_collect.restype = ctypes.c_int
@@ -220,3 +224,22 @@ def zinc_moe_q4k_experts(w_gate, w_up, w_down, n_experts: int, hidden: int, inte
                                   _ptr(dev_error), _stream(stream))
     _check(st, "zinc_moe_q4k_experts")
     return y
+
+
+def zinc_moe_route_topk(logits, top_k: int, expert_ids=None, expert_weights=None, stream=None):
+    """Per token the top_k experts by router logit and their softmax weights,
+    computed on the GPU.  ``logits`` fp32 ``[M, n_experts]``; returns
+    ``(expert_ids int32 [M, top_k], expert_weights fp32 [M, top_k])``."""
+    torch = _torch()
+    _require_cuda(logits, expert_ids, expert_weights)
+    if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous float32 [M, n_experts] tensor")
+    M, E = int(logits.shape[0]), int(logits.shape[1])
+    if expert_ids is None:
+        expert_ids = torch.empty((M, top_k), dtype=torch.int32, device=logits.device)
+    if expert_weights is None:
+        expert_weights = torch.empty((M, top_k), dtype=torch.float32, device=logits.device)
+    st = lib.zinc_moe_route_topk(_ptr(logits), M, E, top_k, _ptr(expert_ids), _ptr(expert_weights),
+                                 _stream(stream))
+    _check(st, "zinc_moe_route_topk")
+    return expert_ids, expert_weights

@@ -18,6 +18,7 @@ constexpr int kMaxDecodeM = 8;
 constexpr int kMaxExperts = 1024;
 constexpr long long kMaxPrefillM = 1 << 20;
 constexpr long long kMaxMoeSlots = 1 << 24;
+constexpr int kMaxRouterTopK = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -153,6 +154,19 @@ int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_dow
   return from_hip(zinc::launch_moe(w_gate, w_up, w_down, n_experts, hidden, inter, x_f16, M, expert_ids,
                                    expert_weights, top_k, y_f16, inter_shift, out_shift, workspace, dev_error,
                                    static_cast<hipStream_t>(stream)));
+}
+
+int zinc_moe_route_topk(const float* logits, int32_t M, int32_t n_experts, int32_t top_k, int32_t* expert_ids,
+                        float* expert_weights, void* stream) {
+  if (n_experts < 1 || n_experts > kMaxExperts || top_k < 1 || top_k > n_experts || top_k > kMaxRouterTopK)
+    return ZINC_ERR_ARG;
+  if (M < 0 || (long long)M * top_k > kMaxMoeSlots) return ZINC_ERR_ARG;
+  if (M == 0) return ZINC_OK;   // nothing is read or written (empty buffers may be NULL)
+  if (!logits || !expert_ids || !expert_weights) return ZINC_ERR_NULL;
+  if (!aligned4(logits) || !aligned4(expert_ids) || !aligned4(expert_weights)) return ZINC_ERR_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(zinc::launch_route_topk(logits, M, n_experts, top_k, expert_ids, expert_weights,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -38,4 +38,9 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
                       const void* x, int M, const int32_t* ids, const float* p, int top_k, void* y,
                       int inter_shift, int out_shift, void* ws, int32_t* dev_error, hipStream_t stream);
 
+// MoE router: per token the top_k largest logits' experts and their softmax
+// weights (k_router.hip).  1 <= top_k <= min(64, n_experts), n_experts <= 1024.
+hipError_t launch_route_topk(const float* logits, int M, int n_experts, int top_k, int32_t* ids, float* p,
+                             hipStream_t stream);
+
 }  // namespace zinc

@@ -136,3 +136,13 @@ def gen_routing(rng: np.random.Generator, M: int, n_experts: int, top_k: int):
 def workload_routing(w: Workload, M: int | None = None):
     rng = np.random.default_rng([w.seed, 1000])
     return gen_routing(rng, w.M if M is None else M, w.n_experts, w.top_k)
+
+
+def gen_router_logits(rng: np.random.Generator, M: int, n_experts: int, scale: float = 1.0):
+    """Router logits ``float32 [M, n_experts]``: ``scale`` times standard normals."""
+    return (rng.standard_normal((M, n_experts)) * scale).astype(np.float32)
+
+
+def workload_router_logits(w: Workload, M: int | None = None):
+    rng = np.random.default_rng([w.seed, 2000])
+    return gen_router_logits(rng, w.M if M is None else M, w.n_experts)

@@ -123,3 +123,20 @@ def test_dequant_argument_errors():
     assert f(MIS, 4, 256, A, None) == -3
     assert f(A, 1 << 20, 1 << 12, A, None) == -2     # rows*cols beyond int32
     assert f(A, 0, 256, A, None) == 0
+
+
+def route(**kw):
+    args = dict(logits=A, M=16, E=64, k=8, ids=A, p=A)
+    args.update(kw)
+    return Z.lib.zinc_moe_route_topk(args["logits"], args["M"], args["E"], args["k"], args["ids"], args["p"], None)
+
+
+def test_router_argument_errors():
+    assert route(logits=None) == -1 and route(ids=None) == -1 and route(p=None) == -1
+    assert route(logits=A + 2) == -3 and route(ids=A + 1) == -3 and route(p=A + 3) == -3
+    assert route(k=0) == -5 and route(k=65) == -5 and route(E=8, k=9) == -5
+    assert route(E=0, k=1) == -5 and route(E=1025, k=8) == -5
+    assert route(M=-1) == -5 and route(M=(1 << 24) // 8 + 1) == -5
+    # no tokens: nothing is read, so empty (NULL) buffers are accepted
+    assert route(M=0) == 0 and route(M=0, logits=None, ids=None, p=None) == 0
+    assert route(M=0, k=0) == -5

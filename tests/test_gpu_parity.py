@@ -331,14 +331,15 @@ def test_moe_top1_weight1_matches_dense():
 
 
 def test_moe_repeat_calls_bit_identical():
-    # experts of ~75 rows: a full tile plus a remainder of <= 16 rows, so these
-    # experts take 128-row chunks in all their tiles; the scatter places rows by
-    # atomics, yet a row's arithmetic must not depend on its tile: repeated
-    # calls give the same bits
+    # tiles hold up to 80 rows; experts of 81-83 rows here are a full tile plus
+    # a remainder of <= 16 rows, so they take 128-row chunks in both their
+    # tiles, and the scatter places their rows in one tile or the other by
+    # atomics; a row's arithmetic must not depend on its tile: repeated calls
+    # give the same bits (the other experts are one tile of 192-row chunks)
     E, H, I, M, k = 16, 256, 512, 300, 4
     wg, wu, wd, x, ids, p = _moe_inputs(E, H, I, M, k, 26)
     counts = np.bincount(ids.ravel(), minlength=E)
-    assert any(0 < c % 64 <= 16 for c in counts) and any(c % 64 > 16 for c in counts)
+    assert any(c > 80 and c % 80 <= 16 for c in counts) and any(c % 80 > 16 for c in counts)
     y_ref, _ = O.moe(x, wg, wu, wd, ids, p, H, I)
     b = max(0, int(np.ceil(np.log2(np.abs(y_ref).max() / 2 ** 13))))
     ys = [_moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, b) for _ in range(3)]

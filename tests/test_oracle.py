@@ -393,6 +393,83 @@ def test_moe_out_of_range_ids_contribute_nothing():
 
 
 # ---------------------------------------------------------------------------
+# Router: top-k selection and the softmax of the chosen logits
+# ---------------------------------------------------------------------------
+def test_router_matches_brute_force_subset_search():
+    """For distinct logits the chosen set is the k-subset with the largest sum
+    (found by enumerating every subset), listed in decreasing logit order."""
+    import itertools
+    rng = np.random.default_rng(71)
+    for _ in range(60):
+        E = int(rng.integers(1, 8))
+        k = int(rng.integers(1, E + 1))
+        row = rng.permutation(E).astype(np.float32) + rng.standard_normal(E).astype(np.float32) * 0.1
+        ids, p = O.route_topk(row[None, :], k)
+        best = max(itertools.combinations(range(E), k), key=lambda c: sum(float(row[j]) for j in c))
+        assert sorted(ids[0].tolist()) == sorted(best)
+        vals = [float(row[j]) for j in ids[0]]
+        assert all(a > b for a, b in zip(vals, vals[1:]))
+        assert abs(p[0].sum() - 1.0) < 1e-12
+
+
+def test_router_ties_go_to_the_lower_index():
+    ids, p = O.route_topk(np.zeros((2, 10), dtype=np.float32), 4)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 2
+    assert np.all(p == 0.25)
+    row = np.array([[1.0, 3.0, 2.0, 3.0, 1.0, 3.0]], dtype=np.float32)
+    ids, _ = O.route_topk(row, 5)
+    assert ids[0].tolist() == [1, 3, 5, 2, 0]
+
+
+def test_router_top1_is_first_argmax_with_weight_one():
+    rng = np.random.default_rng(72)
+    L = rng.integers(-3, 4, size=(50, 12)).astype(np.float32)   # many ties
+    ids, p = O.route_topk(L, 1)
+    assert np.array_equal(ids[:, 0], np.argmax(L, axis=1))
+    assert np.all(p == 1.0)
+
+
+def test_router_weights_match_library_softmax():
+    from scipy.special import softmax
+    rng = np.random.default_rng(73)
+    L = (rng.standard_normal((40, 64)) * 3).astype(np.float32)
+    ids, p = O.route_topk(L, 8)
+    for t in range(40):
+        chosen = L[t, ids[t]].astype(np.float64)
+        assert np.allclose(p[t], softmax(chosen), rtol=1e-13, atol=0)
+        # the full softmax over all experts, renormalised over the chosen ones
+        full = softmax(L[t].astype(np.float64))[ids[t]]
+        assert np.allclose(p[t], full / full.sum(), rtol=1e-12, atol=0)
+
+
+def test_router_shift_invariance_and_ratio():
+    rng = np.random.default_rng(74)
+    # logits on a 2^-10 grid below 8 in magnitude, so adding 16 is exact in fp32
+    L = (np.round(np.clip(rng.standard_normal((20, 32)), -7, 7) * 1024) / 1024).astype(np.float32)
+    ids, p = O.route_topk(L, 6)
+    ids2, p2 = O.route_topk(L + np.float32(16.0), 6)
+    assert np.array_equal((L + np.float32(16.0)).astype(np.float64) - 16.0, L.astype(np.float64))
+    assert np.array_equal(ids, ids2)
+    assert np.allclose(p, p2, rtol=1e-12, atol=0)
+    # p_a / p_b = exp(l_a - l_b)
+    t = 3
+    a, b = ids[t, 0], ids[t, 1]
+    assert math.isclose(p[t, 0] / p[t, 1], math.exp(float(L[t, a]) - float(L[t, b])), rel_tol=1e-12)
+
+
+def test_router_nan_ranks_below_every_number():
+    row = np.array([[np.nan, -np.inf, 2.0, np.nan, -5.0]], dtype=np.float32)
+    ids, p = O.route_topk(row, 3)
+    assert ids[0].tolist() == [2, 4, 1]
+    assert p[0, 2] == 0.0 and p[0, 0] > p[0, 1] > 0
+    ids, p = O.route_topk(row, 5)
+    assert ids[0].tolist() == [2, 4, 1, 0, 3]
+    assert np.all(np.isnan(p[0]))
+    ids, p = O.route_topk(np.full((1, 6), np.nan, dtype=np.float32), 2)
+    assert ids[0].tolist() == [0, 1] and np.all(np.isnan(p[0]))
+
+
+# ---------------------------------------------------------------------------
 # Workload shift exponents keep the fp16 intermediate and output in range
 # ---------------------------------------------------------------------------
 def test_tiny_workload_shifts_have_headroom():
