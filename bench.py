@@ -4,15 +4,17 @@
 Headline: one 4096 -> 11008 -> 4096 Q4_K SwiGLU MLP layer on a 256-token
 prefill tile (seed 1), timed over K repeats after W warmup calls, inputs
 already resident in HBM.  A step is one call of zinc_mlp_q4k_prefill: the
-fused kernel (per-chunk fp32 partial outputs) and the reduce kernel that sums
-them into fp16 y.
+fused kernel (per-chunk fp16 partial outputs at y's scale) and the reduce
+kernel that sums them in fp32 into fp16 y.
 
 Printed as ONE JSON line: tokens/s, the fused kernel's MFMA roofline fraction
 (its duration measured with HIP events recorded on its own stream by the
 library's timing hook), the HBM traffic from the committed rocprofv3 counter
 summary when it matches the current kernel source, and the CPU oracle timed
 on the host.  Secondary lines (decode M=1/M=4 over 32 independent layers,
-the 64-expert MoE over two rotated expert sets) ride in "secondary".
+the 64-expert MoE over two rotated expert sets, the router) ride in
+"secondary".  ``--only staged`` instead times the fused prefill against its
+staged baseline (the intermediate in device memory) at M=256 and M=2048.
 
 usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-secondary] [--no-cpu-baseline]
 """
@@ -188,6 +190,47 @@ def secondary(args, torch):
         out += decode_lines(args, torch, np, Z, S, dev, t)
     if args.only in (None, "moe"):
         out += moe_lines(args, torch, np, Z, S, dev, t)
+    if args.only == "staged":   # its own run: its fused calls at M=2048 would mix into the headline kernel's trace
+        out += staged_lines(args, torch, np, Z, S, dev, t)
+    return out
+
+
+def staged_lines(args, torch, np, Z, S, dev, t):
+    """The fused prefill against its staged comparison baseline (the same
+    units with G, U and the intermediate in device memory), whole calls."""
+    out = []
+    for name, steps in (("prefill_m256", 50), ("prefill_m2048", 10)):
+        w = S.WORKLOADS[name]
+        wg, wu, wd = (t(a) for a in S.layer_weights(w.seed, 0, w.hidden, w.inter))
+        gx = t(S.workload_x(w))
+        y = torch.empty((w.M, w.hidden), dtype=torch.float16, device=dev)
+        wsf = torch.empty(Z.prefill_workspace_size(w.M, w.hidden, w.inter), dtype=torch.uint8, device=dev)
+        wss = torch.empty(Z.prefill_staged_workspace_size(w.M, w.hidden, w.inter), dtype=torch.uint8, device=dev)
+
+        def fused(_i):
+            Z.zinc_mlp_q4k_prefill(wg, wu, wd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=wsf)
+
+        def staged(_i):
+            Z.zinc_mlp_q4k_prefill_staged(wg, wu, wd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y,
+                                          workspace=wss)
+
+        # alternate the two a few times (same thermal state), keep each one's best round
+        best_f, best_s = float("inf"), float("inf")
+        for _ in range(3):
+            best_f = min(best_f, time_calls(fused, steps, 3, torch)[0] / steps)
+            best_s = min(best_s, time_calls(staged, steps, 3, torch)[0] / steps)
+        crossing = 6 * w.M * w.inter * 2
+        out.append({
+            "workload": f"fused vs staged prefill 4096/11008 M={w.M} (seed {w.seed}, layer 0)",
+            "fused_us": round(best_f * 1e6, 2),
+            "staged_us": round(best_s * 1e6, 2),
+            "staged_over_fused": round(best_s / best_f, 3),
+            "fused_tokens_per_s": round(w.M / best_f, 1),
+            "staged_tokens_per_s": round(w.M / best_s, 1),
+            "intermediate_crossings_MB": round(crossing / 1e6, 2),
+        })
+        log(f"[bench] {out[-1]}")
+        del wsf, wss
     return out
 
 
@@ -320,7 +363,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "moe"], default=None,
+    ap.add_argument("--only", choices=["decode", "moe", "staged"], default=None,
                     help="development runs: skip the headline and the CPU baseline, run one secondary part")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3x), the reference kernel that "

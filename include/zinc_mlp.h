@@ -108,6 +108,28 @@ int zinc_mlp_q4k_prefill(const void* w_gate, const void* w_up, const void* w_dow
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The staged comparison baseline of the prefill -- measurement only, not a
+ * product path.  The same y as zinc_mlp_q4k_prefill, computed with the
+ * intermediate in device memory, as the unfused dataflow the fusion replaces
+ * ("Fused SwiGLU MLP: ZINC RDNA4 Down-Projection Bandwidth", "The MLP is two
+ * trips up to a wider width" and "Counting the bytes"): the gate/up pass stores
+ * fp16 G and U [M x inter], a SwiGLU kernel reads them and stores the fp16
+ * intermediate, and the down pass reads it back -- six crossings of
+ * M x inter x 2 bytes that the fused call keeps on chip.  The units, their
+ * decode and the split-K reduction are the fused call's, so the difference
+ * between the two calls is what the fusion saves.  G and U are rounded to fp16
+ * unscaled (they must stay below 65504 in magnitude); the shifts apply as in
+ * the fused call.  Arguments, limits and errors as zinc_mlp_q4k_prefill, with
+ * its own workspace size.
+ */
+size_t zinc_mlp_q4k_prefill_staged_workspace_size(int32_t M, int32_t hidden, int32_t inter);
+int zinc_mlp_q4k_prefill_staged(const void* w_gate, const void* w_up, const void* w_down,
+                                int32_t hidden, int32_t inter,
+                                const void* x_f16, void* y_f16, int32_t M,
+                                int32_t inter_shift, int32_t out_shift,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode, 1 <= M <= 8 tokens: the same block as a pair of HBM-bound matvecs.
  * The first streams W_gate and W_up once, computing both projections from one
  * read of x and applying SwiGLU (the same-input gate/up pair fusion of "Four

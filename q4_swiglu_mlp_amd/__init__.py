@@ -9,6 +9,7 @@ Functions carry the C entry points' names and take torch tensors:
 
 * ``zinc_q4k_dequant_f32(blocks, rows, cols)`` -> fp32 ``[rows, cols]``
 * ``zinc_mlp_q4k_prefill(w_gate, w_up, w_down, hidden, inter, x, ...)`` -> fp16 y
+* ``zinc_mlp_q4k_prefill_staged(...)`` -> fp16 y (comparison baseline, intermediate in device memory)
 * ``zinc_mlp_q4k_decode(...)`` (1 <= M <= 8) -> fp16 y
 * ``zinc_moe_q4k_experts(w_gate, w_up, w_down, n_experts, hidden, inter, x, ids, p, ...)`` -> fp16 y
 * ``zinc_moe_route_topk(logits, top_k)`` -> (int32 ids, fp32 weights), both on the GPU
@@ -36,6 +37,8 @@ EXPORTS = (
     "zinc_q4k_dequant_f32",
     "zinc_mlp_q4k_prefill_workspace_size",
     "zinc_mlp_q4k_prefill",
+    "zinc_mlp_q4k_prefill_staged_workspace_size",
+    "zinc_mlp_q4k_prefill_staged",
     "zinc_mlp_q4k_decode_workspace_size",
     "zinc_mlp_q4k_decode",
     "zinc_moe_q4k_experts_workspace_size",
@@ -74,11 +77,12 @@ def _load() -> ctypes.CDLL:
     lib.zinc_hip_error_string.argtypes = []
     lib.zinc_q4k_dequant_f32.restype = ctypes.c_int
     lib.zinc_q4k_dequant_f32.argtypes = [P, I32, I32, P, P]
-    for name in ("zinc_mlp_q4k_prefill_workspace_size", "zinc_mlp_q4k_decode_workspace_size"):
+    for name in ("zinc_mlp_q4k_prefill_workspace_size", "zinc_mlp_q4k_prefill_staged_workspace_size",
+                 "zinc_mlp_q4k_decode_workspace_size"):
         fn = getattr(lib, name)
         fn.restype = SZ
         fn.argtypes = [I32, I32, I32]
-    for name in ("zinc_mlp_q4k_prefill", "zinc_mlp_q4k_decode"):
+    for name in ("zinc_mlp_q4k_prefill", "zinc_mlp_q4k_prefill_staged", "zinc_mlp_q4k_decode"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, P, P, I32, I32, P, P, I32, I32, I32, P, SZ, P]
@@ -166,6 +170,10 @@ def prefill_workspace_size(M: int, hidden: int, inter: int) -> int:
     return int(lib.zinc_mlp_q4k_prefill_workspace_size(M, hidden, inter))
 
 
+def prefill_staged_workspace_size(M: int, hidden: int, inter: int) -> int:
+    return int(lib.zinc_mlp_q4k_prefill_staged_workspace_size(M, hidden, inter))
+
+
 def decode_workspace_size(M: int, hidden: int, inter: int) -> int:
     return int(lib.zinc_mlp_q4k_decode_workspace_size(M, hidden, inter))
 
@@ -196,6 +204,13 @@ def zinc_mlp_q4k_prefill(w_gate, w_up, w_down, hidden: int, inter: int, x, inter
     """y = fp16(MLP(x) * 2^-out_shift) for fp16 x [M, hidden]; fused prefill kernel."""
     return _dense("zinc_mlp_q4k_prefill", prefill_workspace_size, w_gate, w_up, w_down, hidden, inter, x,
                   inter_shift, out_shift, y, workspace, stream)
+
+
+def zinc_mlp_q4k_prefill_staged(w_gate, w_up, w_down, hidden: int, inter: int, x, inter_shift: int = 0,
+                                out_shift: int = 0, y=None, workspace=None, stream=None):
+    """The prefill's staged comparison baseline (intermediate in device memory); same y."""
+    return _dense("zinc_mlp_q4k_prefill_staged", prefill_staged_workspace_size, w_gate, w_up, w_down, hidden, inter,
+                  x, inter_shift, out_shift, y, workspace, stream)
 
 
 def zinc_mlp_q4k_decode(w_gate, w_up, w_down, hidden: int, inter: int, x, inter_shift: int = 0, out_shift: int = 0,

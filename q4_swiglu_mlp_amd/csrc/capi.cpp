@@ -104,6 +104,26 @@ int zinc_mlp_q4k_prefill(const void* w_gate, const void* w_up, const void* w_dow
                                        workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t zinc_mlp_q4k_prefill_staged_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
+  if (M < 0 || M > kMaxPrefillM || !dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter) || !staged_ok(M, hidden))
+    return 0;
+  return zinc::prefill_staged_workspace_bytes(M, hidden, inter);
+}
+
+int zinc_mlp_q4k_prefill_staged(const void* w_gate, const void* w_up, const void* w_down, int32_t hidden,
+                                int32_t inter, const void* x_f16, void* y_f16, int32_t M, int32_t inter_shift,
+                                int32_t out_shift, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift, kMaxPrefillM);
+  if (st != ZINC_OK) return st;
+  if (M == 0) return ZINC_OK;
+  if (!workspace) return ZINC_ERR_NULL;
+  if (!aligned16(workspace)) return ZINC_ERR_ALIGN;
+  if (workspace_bytes < zinc::prefill_staged_workspace_bytes(M, hidden, inter)) return ZINC_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return from_hip(zinc::launch_prefill_staged(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift,
+                                              out_shift, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t zinc_mlp_q4k_decode_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
   if (M < 0 || M > kMaxDecodeM || !dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
   return zinc::decode_workspace_bytes(M, hidden, inter);

@@ -424,17 +424,33 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
   }
 }
 
+// What a unit runs: the fused form, or one half of the staged comparison
+// baseline, in which the intermediate crosses device memory as the unfused
+// dataflow of "The MLP is two trips up to a wider width" has it (gate and up
+// written and read back, the intermediate written and read back):
+//   kUnitGateUp  phase 1 only; G and U stored as fp16 [M x I] (token-major)
+//   kUnitDown    no phase 1; the strip is read from the fp16 intermediate
+//                [M x I], then phase 2 as in the fused form
+enum : int { kUnitFused = 0, kUnitGateUp = 1, kUnitDown = 2 };
+
+struct StagedIO {
+  _Float16* g = nullptr;          // kUnitGateUp outputs
+  _Float16* u = nullptr;
+  const _Float16* h = nullptr;    // kUnitDown input
+  int t0 = 0;                     // the unit's first token
+};
+
 // One fused MT-token unit.  xtok = the staged activation (k_stage_x16); tok =
 // the unit's MT token indices (LDS, visible to all threads before the call;
 // the zero token M for padding rows); rows = how many of them are real (1..MT,
 // the rest are padding: 16-token groups and 32-token halves wholly past it
 // are skipped); out = the phase-2 output policy.
-template <int ICMAX, class Out, int MT_>
+template <int ICMAX, class Out, int MT_, int MODE = kUnitFused>
 __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
                                              const uint8_t* __restrict__ wd, int H, int I,
                                              const uint8_t* __restrict__ xtok, const int* __restrict__ tok,
                                              int rows, int r0, int r1, float inter_scale, const Out& out,
-                                             Fused16Smem<ICMAX, MT_>& sm) {
+                                             Fused16Smem<ICMAX, MT_>& sm, StagedIO sio = StagedIO{}) {
   using C = Fused16Cfg<ICMAX, MT_>;
   constexpr int NGMAX = C::NGMAX, SLOTS = C::SLOTS, AHEAD = C::AHEAD, MTS = C::MTS;
   constexpr int XS = C::XS, HS = C::HS, HSS = C::HSS, MT = C::MT;
@@ -463,6 +479,13 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
 #pragma unroll
     for (int e = 0; e < 4; ++e) accg[g][e] = accu[g][e] = 0.0f;
 
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using IG = std::integral_constant<int, NGMAX>;
+
+  if constexpr (MODE != kUnitDown) {
   // prologue: columns 0 .. AHEAD-1 staged
   const X16Plan<C::NCOPY> xplan = fu16_plan<C>(tok, nbH);
   {
@@ -642,11 +665,6 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
     }
   };
   // token groups past the unit's rows stay zero and are skipped
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
-  using IG = std::integral_constant<int, NGMAX>;
   const int ng = (rows + 15) >> 4;   // uniform, 1..NGMAX
   if (!act)
     column_loop(std::false_type{}, IG{});
@@ -660,14 +678,54 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
     column_loop(std::true_type{}, I2{});
   else
     column_loop(std::true_type{}, I1{});
+  }   // MODE != kUnitDown
+  if constexpr (MODE == kUnitGateUp) {
+    // staged baseline: G and U to device memory; accumulator e of lane (r, o)
+    // in group g is row 4o + e of the wave's tile, token 16g + r
+    if (act) {
+      const int n = r0 + rt * 16 + 4 * o;
+#pragma unroll
+      for (int g = 0; g < NGMAX; ++g) {
+        const int t = g * 16 + r;
+        if (t < rows) {
+          half4 gv, uv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            gv[e] = (_Float16)accg[g][e];
+            uv[e] = (_Float16)accu[g][e];
+          }
+          *reinterpret_cast<half4*>(sio.g + (size_t)(sio.t0 + t) * I + n) = gv;
+          *reinterpret_cast<half4*>(sio.u + (size_t)(sio.t0 + t) * I + n) = uv;
+        }
+      }
+    }
+    return;
+  }
   lds_barrier();   // the strip below overwrites the activation slots
   if constexpr (MTS > MT) {   // token rows past the unit's MT: a zero strip (phase 2 reads whole 32-token halves)
     for (int i = threadIdx.x; i < (MTS - MT) * HS; i += C::THREADS) sm.u.s.hs[MT * HS + i] = (_Float16)0.0f;
   }
 
+  if constexpr (MODE == kUnitDown) {
+    // staged baseline: the strip and its 32-row sums from the intermediate in
+    // device memory (zero rows past the unit's tokens)
+    const int nq = (r1 - r0) >> 2;
+    for (int idx = threadIdx.x; idx < MT * nq; idx += C::THREADS) {
+      const int t = idx / nq, jl = (idx - t * nq) * 4;
+      uint2 v = make_uint2(0u, 0u);
+      if (t < rows) v = *reinterpret_cast<const uint2*>(sio.h + (size_t)(sio.t0 + t) * I + r0 + jl);
+      const half4 hv = __builtin_bit_cast(half4, v);
+      const uint32_t w0 = (v.x & 0xFFFFu) | (v.y << 16);
+      const uint32_t w1 = (v.x >> 16) | (v.y & 0xFFFF0000u);
+      *reinterpret_cast<uint2*>(sm.u.s.hs + t * HS + (jl & ~63) + panel_pos(jl & 63)) = make_uint2(w0, w1);
+      const int jg = off * 64 + jl;
+      const int slot = 8 * (jg >> 8) + sb_slot((jg >> 5) & 7);
+      atomicAdd(&sm.hsum32[t * HSS + slot], ((float)hv[0] + (float)hv[1]) + ((float)hv[2] + (float)hv[3]));
+    }
+  }
   // SwiGLU in registers -> fp16 strip (panel order) and the 32-row sums.
   // Accumulator e of lane (r, o) in group g: row 4o + e of the tile, token 16g + r.
-  if (act) {
+  if (MODE == kUnitFused && act) {
     const int jl = rt * 16 + 4 * o;                     // chunk-local row, multiple of 4
     const int jg = off * 64 + rt * 16;                  // row from the start of the chunk's first W_down block
     const int slot = 8 * (jg >> 8) + sb_slot((jg >> 5) & 7);

@@ -81,6 +81,50 @@ __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused
   fused_unit16<ICMAX>(wg, wu, wd, H, I, xg, tok, min(64, M - tile * 64), r0, r1, inter_scale, out, sm);
 }
 
+// The staged comparison baseline: the same units in two launches, phase 1
+// storing G and U (kUnitGateUp), phase 2 reading the strip from the
+// intermediate in device memory (kUnitDown).
+template <int ICMAX, int MODE>
+__global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_staged16(
+    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, const uint8_t* __restrict__ wd, int H, int I,
+    const uint8_t* __restrict__ xg, int M, _Float16* __restrict__ P, int Mpad, float out_scale, int n_tiles,
+    int n_chunks, _Float16* __restrict__ G, _Float16* __restrict__ U, const _Float16* __restrict__ Hm) {
+  __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX> sm;
+  __shared__ int tok[64];
+  const int bid = blockIdx.x;
+  const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
+  const int tile = rem >> 3;
+  const int chunk = grp * 8 + (rem & 7);
+  if (chunk >= n_chunks) return;
+  const int npan = I / 64;
+  const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
+  const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
+  if (threadIdx.x < 64) tok[threadIdx.x] = min(tile * 64 + (int)threadIdx.x, M);
+  __syncthreads();
+  const OutQuads out{P, Mpad, H, out_scale, chunk, tile * 64};
+  StagedIO sio;
+  sio.g = G;
+  sio.u = U;
+  sio.h = Hm;
+  sio.t0 = tile * 64;
+  fused_unit16<ICMAX, OutQuads, 64, MODE>(wg, wu, wd, H, I, xg, tok, min(64, M - tile * 64), r0, r1, 1.0f, out, sm,
+                                          sio);
+}
+
+// Staged baseline, between the two launches: h = fp16(silu(g) * u * scale),
+// eight elements per thread.
+__global__ __launch_bounds__(256) void k_swiglu_f16(const _Float16* __restrict__ g, const _Float16* __restrict__ u,
+                                                    _Float16* __restrict__ h, size_t n8, float scale) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const half8 gv = *reinterpret_cast<const half8*>(g + 8 * i);
+  const half8 uv = *reinterpret_cast<const half8*>(u + 8 * i);
+  half8 hv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hv[e] = (_Float16)(silu_f32((float)gv[e]) * (float)uv[e] * scale);
+  *reinterpret_cast<half8*>(h + 8 * i) = hv;
+}
+
 // y[t][n] = fp16(sum_c P[c][n][t]) through a 64x64 LDS transpose.  Thread
 // (tx, ty) sums tokens 8tx..8tx+7 (one 16-byte load) of hidden rows ty and
 // ty + 32 over all chunks in fp32, four chunks' loads in flight at a time.
@@ -179,14 +223,16 @@ struct Plan {
 
 int round_up(int a, int b) { return (a + b - 1) / b * b; }
 
-Plan make_plan(int M, int H, int I) {
+// force_d: configuration D whatever the override names (its chunk count
+// still applies); the staged baseline runs that unit.
+Plan make_plan(int M, int H, int I, bool force_d = false) {
   (void)H;
   Plan p;
   p.cfg = 'D';
   int chunks_wanted = 0;
   // tuning override: ZINC_PREFILL_CFG="<A|B|C|D>[:<chunks>]"
   if (const char* e = std::getenv("ZINC_PREFILL_CFG")) {
-    if (e[0] >= 'A' && e[0] <= 'D') p.cfg = e[0];
+    if (e[0] >= 'A' && e[0] <= 'D' && !force_d) p.cfg = e[0];
     if (e[0] && e[1] == ':') chunks_wanted = std::atoi(e + 2);
   }
   p.MT = (p.cfg == 'A') ? 32 : 64;
@@ -240,6 +286,45 @@ size_t staged_x_bytes(const Plan& p, int H) {
 size_t prefill_workspace_bytes(int M, int hidden, int inter) {
   const Plan p = make_plan(M > 0 ? M : 1, hidden, inter);
   return partial_bytes(p, hidden) + staged_x_bytes(p, hidden);
+}
+
+// Staged baseline workspace: the fused path's (configuration D) plus fp16
+// G, U and the intermediate, [M x inter] each.
+size_t prefill_staged_workspace_bytes(int M, int hidden, int inter) {
+  const Plan p = make_plan(M > 0 ? M : 1, hidden, inter, true);
+  const size_t mi = (((size_t)(M > 0 ? M : 1) * inter * sizeof(_Float16)) + 255) & ~(size_t)255;
+  return partial_bytes(p, hidden) + (x16_staged_bytes(p.n_tiles * p.MT, hidden) + 255) / 256 * 256 + 3 * mi;
+}
+
+hipError_t launch_prefill_staged(const void* wg, const void* wu, const void* wd, int hidden, int inter,
+                                 const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
+                                 hipStream_t stream) {
+  const Plan p = make_plan(M, hidden, inter, true);
+  _Float16* P = static_cast<_Float16*>(ws);
+  uint8_t* xg = static_cast<uint8_t*>(ws) + partial_bytes(p, hidden);
+  const size_t mi = (((size_t)M * inter * sizeof(_Float16)) + 255) & ~(size_t)255;
+  _Float16* G = reinterpret_cast<_Float16*>(xg + (x16_staged_bytes(p.n_tiles * p.MT, hidden) + 255) / 256 * 256);
+  _Float16* U = reinterpret_cast<_Float16*>(reinterpret_cast<uint8_t*>(G) + mi);
+  _Float16* Hm = reinterpret_cast<_Float16*>(reinterpret_cast<uint8_t*>(U) + mi);
+  const float inter_scale = ldexpf(1.0f, -inter_shift);
+  const float out_scale = ldexpf(1.0f, inter_shift - out_shift);
+  const int n_groups = (p.n_chunks + 7) / 8;
+  const dim3 grid(n_groups * 8 * p.n_tiles), block(Fused16Cfg<192>::THREADS);
+  const auto* bg = static_cast<const uint8_t*>(wg);
+  const auto* bu = static_cast<const uint8_t*>(wu);
+  const auto* bd = static_cast<const uint8_t*>(wd);
+  hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream,
+                     static_cast<const _Float16*>(x), hidden, M, xg);
+  hipLaunchKernelGGL((k_prefill_staged16<192, kUnitGateUp>), grid, block, 0, stream, bg, bu, bd, hidden, inter, xg, M,
+                     P, p.Mpad, out_scale, p.n_tiles, p.n_chunks, G, U, (const _Float16*)nullptr);
+  const size_t n8 = (size_t)M * inter / 8;
+  hipLaunchKernelGGL(k_swiglu_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, G, U, Hm, n8,
+                     inter_scale);
+  hipLaunchKernelGGL((k_prefill_staged16<192, kUnitDown>), grid, block, 0, stream, bg, bu, bd, hidden, inter, xg, M,
+                     P, p.Mpad, out_scale, p.n_tiles, p.n_chunks, (_Float16*)nullptr, (_Float16*)nullptr, Hm);
+  hipLaunchKernelGGL(k_reduce_quads, dim3(hidden / 64, p.Mpad / 32), dim3(256), 0, stream, P, p.n_chunks, hidden,
+                     p.Mpad, static_cast<_Float16*>(y), M);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,

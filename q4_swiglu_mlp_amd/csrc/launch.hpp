@@ -21,6 +21,13 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
                           const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
                           hipStream_t stream);
 
+// The staged comparison baseline of the prefill: the same units with the
+// gate/up outputs and the intermediate in device memory (four main launches).
+size_t prefill_staged_workspace_bytes(int M, int hidden, int inter);
+hipError_t launch_prefill_staged(const void* wg, const void* wu, const void* wd, int hidden, int inter,
+                                 const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
+                                 hipStream_t stream);
+
 // Decode, 1 <= M <= 8: row-streaming dot products for M = 1 (k_decode.hip),
 // 16x16x32 MFMA tiles for M >= 2 (k_decode_mfma.hip); both write the fp16
 // intermediate [M x inter] into the workspace between their two kernels.

@@ -53,7 +53,15 @@ def decode(**kw):
                                      args["y"], args["M"], args["a"], args["b"], args["ws"], args["wsb"], None)
 
 
-@pytest.mark.parametrize("fn", [prefill, decode])
+def prefill_staged(**kw):
+    args = dict(wg=A, wu=A, wd=A, hidden=4096, inter=11008, x=A, y=A, M=256, a=0, b=0, ws=A, wsb=1 << 31)
+    args.update(kw)
+    return Z.lib.zinc_mlp_q4k_prefill_staged(args["wg"], args["wu"], args["wd"], args["hidden"], args["inter"],
+                                             args["x"], args["y"], args["M"], args["a"], args["b"], args["ws"],
+                                             args["wsb"], None)
+
+
+@pytest.mark.parametrize("fn", [prefill, prefill_staged, decode])
 def test_dense_argument_errors(fn):
     assert fn(wg=None) == -1 and fn(wd=None) == -1 and fn(x=None) == -1 and fn(y=None) == -1
     assert fn(hidden=0) == -2 and fn(hidden=300) == -2 and fn(inter=-256) == -2 and fn(inter=1000) == -2
@@ -88,6 +96,10 @@ def test_workspace_sizes():
     assert Z.prefill_workspace_size(256, 4096, 11008) >= 256 * 4096 * 4
     assert Z.prefill_workspace_size(257, 4096, 11008) > Z.prefill_workspace_size(256, 4096, 11008)
     assert Z.prefill_workspace_size(256, 4000, 11008) == 0
+    # the staged baseline adds G, U and the intermediate, M x inter fp16 each
+    assert (Z.prefill_staged_workspace_size(256, 4096, 11008)
+            >= Z.prefill_workspace_size(256, 4096, 11008) + 3 * 256 * 11008 * 2)
+    assert Z.prefill_staged_workspace_size(256, 4000, 11008) == 0
     assert Z.decode_workspace_size(4, 4096, 11008) >= 4 * 11008 * 2
     assert Z.moe_workspace_size(512, 8, 64, 2048, 768) >= 512 * 2048 * 4 + 512 * 8 * 4
     assert Z.moe_workspace_size(512, 65, 64, 2048, 768) == 0

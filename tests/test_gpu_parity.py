@@ -118,6 +118,22 @@ def test_prefill_m256_workload_full():
     assert_parity(y, y_ref, "prefill 4096/11008 M=256")
 
 
+@pytest.mark.parametrize("M", [1, 65, 256])
+def test_prefill_staged_baseline_matches(M):
+    # the comparison baseline (intermediate in device memory) computes the
+    # same y: against the oracle, and close to the fused call (it rounds G
+    # and U to fp16 on the way, the fused call does not)
+    w = S.WORKLOADS["prefill_m256"]
+    wg, wu, wd = S.layer_weights(w.seed, 0, w.hidden, w.inter)
+    x = S.workload_x(w, M=M)
+    ys = unscale(Z.zinc_mlp_q4k_prefill_staged(dev(wg), dev(wu), dev(wd), w.hidden, w.inter, dev(x), w.inter_shift,
+                                               w.out_shift), w.out_shift)
+    yf = prefill(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift)
+    y_ref, _ = O.mlp(x, wg, wu, wd, w.hidden, w.inter)
+    assert_parity(ys, y_ref, f"staged baseline M={M}")
+    assert_parity(ys, yf, f"staged baseline vs fused M={M}")
+
+
 @pytest.mark.parametrize("layer", [0, 31])
 def test_prefill_m2048_workload_sampled_tokens(layer):
     w = S.WORKLOADS["prefill_m2048"]
