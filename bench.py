@@ -12,8 +12,8 @@ Printed as ONE JSON line: tokens/s, the fused kernel's MFMA roofline fraction
 library's timing hook), the HBM traffic from the committed rocprofv3 counter
 summary when it matches the current kernel source, and the CPU oracle timed
 on the host.  Secondary lines (decode M=1/M=4 over 32 independent layers,
-the 64-expert MoE over two rotated expert sets, the router) ride in
-"secondary".  ``--only staged`` instead times the fused prefill against its
+the 64-expert MoE over two rotated expert sets, the router, the MLP block
+with its RMS norm and residual) ride in "secondary".  ``--only staged`` instead times the fused prefill against its
 staged baseline (the intermediate in device memory) at M=256 and M=2048.
 
 usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-secondary] [--no-cpu-baseline]
@@ -190,8 +190,41 @@ def secondary(args, torch):
         out += decode_lines(args, torch, np, Z, S, dev, t)
     if args.only in (None, "moe"):
         out += moe_lines(args, torch, np, Z, S, dev, t)
+    if args.only in (None, "block"):
+        out += block_lines(args, torch, np, Z, S, dev, t)
     if args.only == "staged":   # its own run: its fused calls at M=2048 would mix into the headline kernel's trace
         out += staged_lines(args, torch, np, Z, S, dev, t)
+    return out
+
+
+def block_lines(args, torch, np, Z, S, dev, t):
+    """The MLP block entry points (pre-MLP RMS norm + MLP + residual) against
+    the plain MLP call: prefill M=256 and decode M=1, whole calls."""
+    out = []
+    for name, fblock, fplain, steps in (("prefill_m256", Z.zinc_mlp_q4k_prefill_block, Z.zinc_mlp_q4k_prefill, 100),
+                                        ("decode_m1", Z.zinc_mlp_q4k_decode_block, Z.zinc_mlp_q4k_decode, 200)):
+        w = S.WORKLOADS[name]
+        wg, wu, wd = (t(a) for a in S.layer_weights(w.seed, 0, w.hidden, w.inter))
+        gx = t(S.workload_x(w))
+        gamma = t(np.random.default_rng(w.seed).uniform(0.5, 1.5, w.hidden).astype(np.float16))
+        y = torch.empty((w.M, w.hidden), dtype=torch.float16, device=dev)
+        wsb = torch.empty(4 << 20 if w.M == 1 else 160 << 20, dtype=torch.uint8, device=dev)
+
+        def blk(_i):
+            fblock(wg, wu, wd, w.hidden, w.inter, gx, gamma, 1e-5, 1.0, w.inter_shift, w.out_shift, y=y, workspace=wsb)
+
+        def plain(_i):
+            fplain(wg, wu, wd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=wsb)
+
+        tb = min(time_calls(blk, steps, 5, torch)[0] for _ in range(2)) / steps
+        tp = min(time_calls(plain, steps, 5, torch)[0] for _ in range(2)) / steps
+        out.append({
+            "workload": f"MLP block (RMS norm + MLP + residual) vs plain MLP call, {name} (4096/11008, M={w.M})",
+            "block_us": round(tb * 1e6, 2),
+            "plain_us": round(tp * 1e6, 2),
+            "block_tokens_per_s": round(w.M / tb, 1),
+        })
+        log(f"[bench] {out[-1]}")
     return out
 
 
@@ -363,7 +396,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "moe", "staged"], default=None,
+    ap.add_argument("--only", choices=["decode", "moe", "block", "staged"], default=None,
                     help="development runs: skip the headline and the CPU baseline, run one secondary part")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3x), the reference kernel that "

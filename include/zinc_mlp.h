@@ -108,6 +108,39 @@ int zinc_mlp_q4k_prefill(const void* w_gate, const void* w_up, const void* w_dow
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The MLP block with its neighbours folded in: the pre-MLP RMS norm and the
+ * post-MLP residual ("Four bottlenecks, one CUDA backend", "Bottleneck 3":
+ * norm and residual steps fused into fewer launches, with the per-layer output
+ * scale folded into the norm + residual step):
+ *   r_t     = 1 / sqrt(mean_k x[t][k]^2 + norm_eps)           (fp32)
+ *   xn[t]   = fp16(x[t] * r_t * norm_weight)                   (the MLP's input)
+ *   y[t]    = fp16((x[t] + mlp_scale * MLP(xn[t])) * 2^-out_shift)
+ * with MLP and the shifts as in zinc_mlp_q4k_prefill / _decode (inter_shift
+ * scales the intermediate).  x is the residual stream; y may be x itself (an
+ * in-place residual update).  norm_weight_f16: fp16 [hidden], 16-byte aligned.
+ * norm_eps >= 0 and mlp_scale finite, else ZINC_ERR_ARG (with norm_eps == 0 an
+ * all-zero row gives NaN).  The norm runs as one small kernel writing xn to the
+ * workspace; the residual and the scale are applied where y is written (the
+ * reduce kernel, or the decode down-projection kernel), so neither costs a
+ * launch of its own.  Other arguments, limits and errors as the plain entry
+ * points (_decode_block: 1 <= M <= 8), with their own workspace sizes.
+ */
+size_t zinc_mlp_q4k_prefill_block_workspace_size(int32_t M, int32_t hidden, int32_t inter);
+int zinc_mlp_q4k_prefill_block(const void* w_gate, const void* w_up, const void* w_down,
+                               int32_t hidden, int32_t inter,
+                               const void* x_f16, const void* norm_weight_f16, float norm_eps,
+                               float mlp_scale, void* y_f16, int32_t M,
+                               int32_t inter_shift, int32_t out_shift,
+                               void* workspace, size_t workspace_bytes, void* stream);
+size_t zinc_mlp_q4k_decode_block_workspace_size(int32_t M, int32_t hidden, int32_t inter);
+int zinc_mlp_q4k_decode_block(const void* w_gate, const void* w_up, const void* w_down,
+                              int32_t hidden, int32_t inter,
+                              const void* x_f16, const void* norm_weight_f16, float norm_eps,
+                              float mlp_scale, void* y_f16, int32_t M,
+                              int32_t inter_shift, int32_t out_shift,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The staged comparison baseline of the prefill -- measurement only, not a
  * product path.  The same y as zinc_mlp_q4k_prefill, computed with the
  * intermediate in device memory, as the unfused dataflow the fusion replaces

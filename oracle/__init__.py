@@ -21,6 +21,8 @@ Plain, slow, obviously-correct float64 numpy:
 * ``moe``: the batched-expert form of "Four bottlenecks, one CUDA backend",
   "Bottleneck 2": each token's output is the mixing-weighted sum of its chosen
   experts' MLP outputs; expert ids are inputs.
+* ``rms_norm`` / ``mlp_block``: the block with its neighbours -- the pre-MLP
+  RMS norm and the residual add (with a per-layer scale on the MLP output).
 * ``route_topk``: the router step before it -- per token the top-k experts by
   router logit and the softmax of the chosen logits.
 
@@ -30,7 +32,9 @@ field reader, silu identities and a library sigmoid, brute-force loops on tiny
 shapes, one-hot / zero / unit-weight probes, exact scaling and permutation
 invariants, and MoE reductions to the dense MLP; the router against a
 brute-force search over expert subsets, tie and NaN rules written out, a
-library softmax, and the renormalised full softmax.
+library softmax, and the renormalised full softmax; the RMS norm against
+torch's rms_norm, closed forms and its scale invariance, the block against its
+zero-weight and zero-scale reductions.
 """
 from __future__ import annotations
 
@@ -133,6 +137,27 @@ def mlp(x, wg_blob, wu_blob, wd_blob, hidden: int, inter: int):
     Wu = q4k_dequant(wu_blob, inter, hidden)
     Wd = q4k_dequant(wd_blob, hidden, inter)
     return mlp_from_weights(x, Wg, Wu, Wd)
+
+
+def rms_norm(x, gamma, eps: float):
+    """RMS norm of each row: x * gamma / sqrt(mean(x^2) + eps), in float64."""
+    x64 = np.asarray(x, dtype=np.float64)
+    g64 = np.asarray(gamma, dtype=np.float64)
+    ms = np.mean(x64 * x64, axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return x64 / np.sqrt(ms + eps) * g64
+
+
+def mlp_block(x, gamma, eps: float, mlp_scale: float, wg_blob, wu_blob, wd_blob, hidden: int, inter: int):
+    """The MLP with its neighbours of "Four bottlenecks, one CUDA backend",
+    "Bottleneck 3" (norm and residual steps folded into the MLP's launches,
+    the per-layer output scale with them): the pre-MLP RMS norm feeds the MLP
+    and the residual stream x is added back,
+        y = x + mlp_scale * MLP(rms_norm(x) * gamma).
+    Returns ``(y [M x hidden], xn [M x hidden])`` in float64."""
+    xn = rms_norm(x, gamma, eps)
+    ym, _ = mlp(xn, wg_blob, wu_blob, wd_blob, hidden, inter)
+    return np.asarray(x, dtype=np.float64) + float(mlp_scale) * ym, xn
 
 
 def moe(x, wg_blobs, wu_blobs, wd_blobs, ids, p, hidden: int, inter: int):

@@ -9,6 +9,8 @@ Functions carry the C entry points' names and take torch tensors:
 
 * ``zinc_q4k_dequant_f32(blocks, rows, cols)`` -> fp32 ``[rows, cols]``
 * ``zinc_mlp_q4k_prefill(w_gate, w_up, w_down, hidden, inter, x, ...)`` -> fp16 y
+* ``zinc_mlp_q4k_prefill_block`` / ``zinc_mlp_q4k_decode_block(..., x, norm_weight, eps, mlp_scale, ...)``
+  -> fp16 y = x + mlp_scale * MLP(rms_norm(x)) (pre-MLP norm and residual folded in)
 * ``zinc_mlp_q4k_prefill_staged(...)`` -> fp16 y (comparison baseline, intermediate in device memory)
 * ``zinc_mlp_q4k_decode(...)`` (1 <= M <= 8) -> fp16 y
 * ``zinc_moe_q4k_experts(w_gate, w_up, w_down, n_experts, hidden, inter, x, ids, p, ...)`` -> fp16 y
@@ -37,6 +39,10 @@ EXPORTS = (
     "zinc_q4k_dequant_f32",
     "zinc_mlp_q4k_prefill_workspace_size",
     "zinc_mlp_q4k_prefill",
+    "zinc_mlp_q4k_prefill_block_workspace_size",
+    "zinc_mlp_q4k_prefill_block",
+    "zinc_mlp_q4k_decode_block_workspace_size",
+    "zinc_mlp_q4k_decode_block",
     "zinc_mlp_q4k_prefill_staged_workspace_size",
     "zinc_mlp_q4k_prefill_staged",
     "zinc_mlp_q4k_decode_workspace_size",
@@ -78,7 +84,8 @@ def _load() -> ctypes.CDLL:
     lib.zinc_q4k_dequant_f32.restype = ctypes.c_int
     lib.zinc_q4k_dequant_f32.argtypes = [P, I32, I32, P, P]
     for name in ("zinc_mlp_q4k_prefill_workspace_size", "zinc_mlp_q4k_prefill_staged_workspace_size",
-                 "zinc_mlp_q4k_decode_workspace_size"):
+                 "zinc_mlp_q4k_decode_workspace_size", "zinc_mlp_q4k_prefill_block_workspace_size",
+                 "zinc_mlp_q4k_decode_block_workspace_size"):
         fn = getattr(lib, name)
         fn.restype = SZ
         fn.argtypes = [I32, I32, I32]
@@ -86,6 +93,11 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, P, P, I32, I32, P, P, I32, I32, I32, P, SZ, P]
+    F32 = ctypes.c_float
+    for name in ("zinc_mlp_q4k_prefill_block", "zinc_mlp_q4k_decode_block"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P, P, P, I32, I32, P, P, F32, F32, P, I32, I32, I32, P, SZ, P]
     lib.zinc_moe_q4k_experts_workspace_size.restype = SZ
     lib.zinc_moe_q4k_experts_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.zinc_moe_q4k_experts.restype = ctypes.c_int
@@ -189,9 +201,8 @@ def _dense(fn_name: str, ws_fn, w_gate, w_up, w_down, hidden, inter, x, inter_sh
     M = int(x.shape[0])
     if y is None:
         y = torch.empty((M, hidden), dtype=torch.float16, device=x.device)
-    need = ws_fn(M, hidden, inter)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(max(ws_fn(M, hidden, inter), 16), dtype=torch.uint8, device=x.device)
     st = getattr(lib, fn_name)(_ptr(w_gate), _ptr(w_up), _ptr(w_down), hidden, inter, _ptr(x), _ptr(y), M,
                                inter_shift, out_shift, _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                _stream(stream))
@@ -204,6 +215,39 @@ def zinc_mlp_q4k_prefill(w_gate, w_up, w_down, hidden: int, inter: int, x, inter
     """y = fp16(MLP(x) * 2^-out_shift) for fp16 x [M, hidden]; fused prefill kernel."""
     return _dense("zinc_mlp_q4k_prefill", prefill_workspace_size, w_gate, w_up, w_down, hidden, inter, x,
                   inter_shift, out_shift, y, workspace, stream)
+
+
+def _block(fn_name: str, ws_name: str, w_gate, w_up, w_down, hidden, inter, x, norm_weight, norm_eps, mlp_scale,
+           inter_shift, out_shift, y, workspace, stream):
+    torch = _torch()
+    _require_cuda(w_gate, w_up, w_down, x, norm_weight, y, workspace)
+    M = int(x.shape[0])
+    if y is None:
+        y = torch.empty((M, hidden), dtype=torch.float16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(int(getattr(lib, ws_name)(M, hidden, inter)), 16), dtype=torch.uint8,
+                                device=x.device)
+    st = getattr(lib, fn_name)(_ptr(w_gate), _ptr(w_up), _ptr(w_down), hidden, inter, _ptr(x), _ptr(norm_weight),
+                               float(norm_eps), float(mlp_scale), _ptr(y), M, inter_shift, out_shift, _ptr(workspace),
+                               int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(st, fn_name)
+    return y
+
+
+def zinc_mlp_q4k_prefill_block(w_gate, w_up, w_down, hidden: int, inter: int, x, norm_weight, norm_eps: float,
+                               mlp_scale: float = 1.0, inter_shift: int = 0, out_shift: int = 0, y=None,
+                               workspace=None, stream=None):
+    """y = fp16((x + mlp_scale * MLP(rms_norm(x) * norm_weight)) * 2^-out_shift); ``y`` may be ``x``."""
+    return _block("zinc_mlp_q4k_prefill_block", "zinc_mlp_q4k_prefill_block_workspace_size", w_gate, w_up, w_down,
+                  hidden, inter, x, norm_weight, norm_eps, mlp_scale, inter_shift, out_shift, y, workspace, stream)
+
+
+def zinc_mlp_q4k_decode_block(w_gate, w_up, w_down, hidden: int, inter: int, x, norm_weight, norm_eps: float,
+                              mlp_scale: float = 1.0, inter_shift: int = 0, out_shift: int = 0, y=None,
+                              workspace=None, stream=None):
+    """The decode form (1 <= M <= 8) of zinc_mlp_q4k_prefill_block."""
+    return _block("zinc_mlp_q4k_decode_block", "zinc_mlp_q4k_decode_block_workspace_size", w_gate, w_up, w_down,
+                  hidden, inter, x, norm_weight, norm_eps, mlp_scale, inter_shift, out_shift, y, workspace, stream)
 
 
 def zinc_mlp_q4k_prefill_staged(w_gate, w_up, w_down, hidden: int, inter: int, x, inter_shift: int = 0,
@@ -230,9 +274,9 @@ def zinc_moe_q4k_experts(w_gate, w_up, w_down, n_experts: int, hidden: int, inte
     top_k = int(expert_ids.shape[1]) if expert_ids.dim() == 2 else 1
     if y is None:
         y = torch.empty((M, hidden), dtype=torch.float16, device=x.device)
-    need = moe_workspace_size(M, top_k, n_experts, hidden, inter)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(max(moe_workspace_size(M, top_k, n_experts, hidden, inter), 16), dtype=torch.uint8,
+                                device=x.device)
     st = lib.zinc_moe_q4k_experts(_ptr(w_gate), _ptr(w_up), _ptr(w_down), n_experts, hidden, inter, _ptr(x), M,
                                   _ptr(expert_ids), _ptr(expert_weights), top_k, _ptr(y), inter_shift, out_shift,
                                   _ptr(workspace), int(workspace.numel() * workspace.element_size()),

@@ -7,7 +7,10 @@
 
 #include <cstdint>
 
+#include <cmath>
+
 #include "launch.hpp"
+#include "util_kernels.hpp"
 
 namespace {
 
@@ -50,6 +53,19 @@ int check_dense(const void* wg, const void* wu, const void* wd, int32_t hidden, 
   if (!aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(x) || !aligned16(y)) return ZINC_ERR_ALIGN;
   if (M < 0 || M > max_m || !staged_ok(M, hidden)) return ZINC_ERR_ARG;
   if (inter_shift < 0 || inter_shift > kMaxShift || out_shift < 0 || out_shift > kMaxShift) return ZINC_ERR_ARG;
+  return ZINC_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// The block entry points: the normalised activation sits after the wrapped
+// call's own workspace.
+size_t xn_bytes(int32_t M, int32_t hidden) { return align256((size_t)(M > 0 ? M : 1) * hidden * 2); }
+
+int check_block(const void* norm_weight, float eps, float mlp_scale) {
+  if (!norm_weight) return ZINC_ERR_NULL;
+  if (!aligned16(norm_weight)) return ZINC_ERR_ALIGN;
+  if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(mlp_scale)) return ZINC_ERR_ARG;
   return ZINC_OK;
 }
 
@@ -102,6 +118,33 @@ int zinc_mlp_q4k_prefill(const void* w_gate, const void* w_up, const void* w_dow
   (void)hipGetLastError();
   return from_hip(zinc::launch_prefill(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift,
                                        workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t zinc_mlp_q4k_prefill_block_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
+  const size_t base = zinc_mlp_q4k_prefill_workspace_size(M, hidden, inter);
+  return base ? align256(base) + xn_bytes(M, hidden) : 0;
+}
+
+int zinc_mlp_q4k_prefill_block(const void* w_gate, const void* w_up, const void* w_down, int32_t hidden,
+                               int32_t inter, const void* x_f16, const void* norm_weight_f16, float norm_eps,
+                               float mlp_scale, void* y_f16, int32_t M, int32_t inter_shift, int32_t out_shift,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift, kMaxPrefillM);
+  if (st != ZINC_OK) return st;
+  st = check_block(norm_weight_f16, norm_eps, mlp_scale);
+  if (st != ZINC_OK) return st;
+  if (M == 0) return ZINC_OK;
+  if (!workspace) return ZINC_ERR_NULL;
+  if (!aligned16(workspace)) return ZINC_ERR_ALIGN;
+  const size_t base = align256(zinc::prefill_workspace_bytes(M, hidden, inter));
+  if (workspace_bytes < base + xn_bytes(M, hidden)) return ZINC_ERR_WORKSPACE;
+  _Float16* xn = reinterpret_cast<_Float16*>(static_cast<uint8_t*>(workspace) + base);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  zinc::launch_rms_norm(static_cast<const _Float16*>(x_f16), static_cast<const _Float16*>(norm_weight_f16), norm_eps,
+                        hidden, M, xn, s);
+  return from_hip(zinc::launch_prefill(w_gate, w_up, w_down, hidden, inter, xn, y_f16, M, inter_shift, out_shift,
+                                       workspace, s, mlp_scale, x_f16));
 }
 
 size_t zinc_mlp_q4k_prefill_staged_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
@@ -187,6 +230,31 @@ int zinc_moe_route_topk(const float* logits, int32_t M, int32_t n_experts, int32
   (void)hipGetLastError();
   return from_hip(zinc::launch_route_topk(logits, M, n_experts, top_k, expert_ids, expert_weights,
                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t zinc_mlp_q4k_decode_block_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
+  const size_t base = zinc_mlp_q4k_decode_workspace_size(M, hidden, inter);
+  return base ? align256(base) + xn_bytes(M, hidden) : 0;
+}
+
+int zinc_mlp_q4k_decode_block(const void* w_gate, const void* w_up, const void* w_down, int32_t hidden,
+                              int32_t inter, const void* x_f16, const void* norm_weight_f16, float norm_eps,
+                              float mlp_scale, void* y_f16, int32_t M, int32_t inter_shift, int32_t out_shift,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift, kMaxDecodeM);
+  if (st != ZINC_OK) return st;
+  st = check_block(norm_weight_f16, norm_eps, mlp_scale);
+  if (st != ZINC_OK) return st;
+  if (M == 0) return ZINC_OK;
+  if (!workspace) return ZINC_ERR_NULL;
+  if (!aligned16(workspace)) return ZINC_ERR_ALIGN;
+  const size_t base = align256(zinc::decode_workspace_bytes(M, hidden, inter));
+  if (workspace_bytes < base + xn_bytes(M, hidden)) return ZINC_ERR_WORKSPACE;
+  void* xn = static_cast<uint8_t*>(workspace) + base;
+  (void)hipGetLastError();
+  return from_hip(zinc::launch_decode(w_gate, w_up, w_down, hidden, inter, x_f16, y_f16, M, inter_shift, out_shift,
+                                      workspace, static_cast<hipStream_t>(stream), mlp_scale, x_f16,
+                                      norm_weight_f16, norm_eps, xn));
 }
 
 }  // extern "C"

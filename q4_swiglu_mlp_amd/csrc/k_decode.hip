@@ -33,6 +33,7 @@
 // nibble unpack produces.
 #include "fused_core.hpp"
 #include "launch.hpp"
+#include "util_kernels.hpp"
 
 #include <algorithm>
 #include <cstdio>
@@ -118,7 +119,8 @@ template <int MM, bool GATEUP, int KQ, bool PF, int NW>
 __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint8_t* __restrict__ W0,
                                                             const uint8_t* __restrict__ W1, int K, int N,
                                                             const _Float16* __restrict__ xin, int M,
-                                                            _Float16* __restrict__ out, float scale) {
+                                                            _Float16* out, float scale, const _Float16* res,
+                                                            float res_scale, const _Float16* gamma, float eps) {
   constexpr int NMAT = GATEUP ? 2 : 1;
   constexpr int DR_WAVES = DrShape<NW>::WAVES, DR_THREADS = DrShape<NW>::THREADS;
   extern __shared__ __attribute__((aligned(16))) unsigned char dr_smem[];
@@ -186,7 +188,9 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
 #pragma unroll
       for (int t = 0; t < MM; ++t) {
         if (t < M) {
-          const float v = GATEUP ? silu_f32(acc[0][t]) * acc[NMAT - 1][t] * scale : acc[0][t] * scale;
+          float v = GATEUP ? silu_f32(acc[0][t]) * acc[NMAT - 1][t] * scale : acc[0][t] * scale;
+          // the residual (down pass only; it may be out itself: read, then written, here)
+          if (!GATEUP && res) v += (float)res[(size_t)t * N + j] * res_scale;
           out[(size_t)t * N + j] = (_Float16)v;
         }
       }
@@ -209,6 +213,39 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
   Buf buf, buf2;
   int j = w0;
   load_row(j, buf);
+  // the pre-MLP RMS norm (gate/up pass of one token, gamma non-null): every
+  // workgroup holds the whole activation, so it sums the squares itself and
+  // scales its pieces before they are staged
+  if (MM == 1 && gamma) {
+    __shared__ float part[DR_WAVES];
+    float ss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NXG; ++u) {
+      const half8 hv = __builtin_bit_cast(half8, xv[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += (float)hv[e] * (float)hv[e];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if (lane == 0) part[wave] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < DR_WAVES; ++w) tot += part[w];
+    const float r = 1.0f / sqrtf(tot / (float)K + eps);
+#pragma unroll
+    for (int u = 0; u < NXG; ++u) {
+      const int g = tid + u * DR_THREADS;
+      if (g < ngroups) {
+        const half8 hv = __builtin_bit_cast(half8, xv[u]);
+        const half8 gm = *reinterpret_cast<const half8*>(gamma + 8 * g);
+        half8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (_Float16)((float)hv[e] * r * (float)gm[e]);
+        xv[u] = __builtin_bit_cast(uint4, o);
+      }
+    }
+  }
   // stage x: groups of four with the middle two swapped; fp32 sums of every 32
   // elements (four consecutive groups = four consecutive lanes of a quad)
 #pragma unroll
@@ -287,7 +324,8 @@ inline DrCfg dr_cfg(bool gateup) {
 
 template <int MM, bool GATEUP, int KQ, bool PF, int NW>
 hipError_t launch_rows_cfg(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
-                           float scale, int wg_per_cu, hipStream_t stream) {
+                           float scale, const _Float16* res, float res_scale, const _Float16* gamma, float eps,
+                           int wg_per_cu, hipStream_t stream) {
   const size_t smem = (size_t)MM * (K + 8) * 2 + (size_t)MM * 2 * (4 * (K / QK)) * 4;
   static size_t attr_set = 0;   // largest dynamic LDS size allowed so far
   if (smem > attr_set) {
@@ -309,31 +347,38 @@ hipError_t launch_rows_cfg(const void* W0, const void* W1, int K, int N, const _
   const int per_cu = (wg_per_cu > 0 && wg_per_cu < occ) ? wg_per_cu : occ;
   const int grid = std::max(1, std::min(cu_count() * per_cu, (N + NW - 1) / NW));
   hipLaunchKernelGGL((k_decode_rows<MM, GATEUP, KQ, PF, NW>), dim3(grid), dim3(DrShape<NW>::THREADS), smem, stream,
-                     static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), K, N, x, M, out, scale);
+                     static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), K, N, x, M, out, scale, res,
+                     res_scale, gamma, eps);
   return hipGetLastError();
 }
 
 template <int MM, bool GATEUP, int KQ>
 hipError_t launch_rows(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
-                       float scale, hipStream_t stream) {
+                       float scale, const _Float16* res, float res_scale, const _Float16* gamma, float eps,
+                       hipStream_t stream) {
   const DrCfg c = dr_cfg(GATEUP);
   if (c.pf && c.waves == 4)
-    return launch_rows_cfg<MM, GATEUP, KQ, true, 4>(W0, W1, K, N, x, M, out, scale, c.wg_per_cu, stream);
+    return launch_rows_cfg<MM, GATEUP, KQ, true, 4>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu,
+                                                    stream);
   if (c.pf)
-    return launch_rows_cfg<MM, GATEUP, KQ, true, 8>(W0, W1, K, N, x, M, out, scale, c.wg_per_cu, stream);
+    return launch_rows_cfg<MM, GATEUP, KQ, true, 8>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu,
+                                                    stream);
   if (c.waves == 4)
-    return launch_rows_cfg<MM, GATEUP, KQ, false, 4>(W0, W1, K, N, x, M, out, scale, c.wg_per_cu, stream);
-  return launch_rows_cfg<MM, GATEUP, KQ, false, 8>(W0, W1, K, N, x, M, out, scale, c.wg_per_cu, stream);
+    return launch_rows_cfg<MM, GATEUP, KQ, false, 4>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu,
+                                                     stream);
+  return launch_rows_cfg<MM, GATEUP, KQ, false, 8>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu,
+                                                   stream);
 }
 
 template <int MM, bool GATEUP>
 hipError_t launch_rows_k(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
-                         float scale, hipStream_t stream) {
+                         float scale, const _Float16* res, float res_scale, const _Float16* gamma, float eps,
+                         hipStream_t stream) {
   const int Q = 4 * (K / QK);
-  if (Q <= 64) return launch_rows<MM, GATEUP, 1>(W0, W1, K, N, x, M, out, scale, stream);
-  if (Q <= 128) return launch_rows<MM, GATEUP, 2>(W0, W1, K, N, x, M, out, scale, stream);
-  if (Q <= 192) return launch_rows<MM, GATEUP, 3>(W0, W1, K, N, x, M, out, scale, stream);
-  return launch_rows<MM, GATEUP, 4>(W0, W1, K, N, x, M, out, scale, stream);
+  if (Q <= 64) return launch_rows<MM, GATEUP, 1>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, stream);
+  if (Q <= 128) return launch_rows<MM, GATEUP, 2>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, stream);
+  if (Q <= 192) return launch_rows<MM, GATEUP, 3>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, stream);
+  return launch_rows<MM, GATEUP, 4>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, stream);
 }
 
 }  // namespace
@@ -344,21 +389,32 @@ size_t decode_workspace_bytes(int M, int hidden, int inter) {
 }
 
 hipError_t launch_decode(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x, void* y,
-                         int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
+                         int M, int inter_shift, int out_shift, void* ws, hipStream_t stream, float mlp_scale,
+                         const void* res, const void* gamma, float eps, void* xn) {
+  const _Float16* gm = static_cast<const _Float16*>(gamma);
   // The row kernels cover contractions up to DR_KMAX (four 64-chunk slots per
   // lane); a longer down-projection contraction takes the MFMA path, which
-  // walks any K in passes.
-  if (M >= 2 || inter > DR_KMAX)
-    return launch_decode_mfma(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream);
-  const float gu_scale = ldexpf(1.0f, -inter_shift), dn_scale = ldexpf(1.0f, inter_shift - out_shift);
+  // walks any K in passes.  That path normalises the activation in a kernel
+  // of its own first; the row kernels do it while staging.
+  if (M >= 2 || inter > DR_KMAX) {
+    if (gm) {
+      launch_rms_norm(static_cast<const _Float16*>(x), gm, eps, hidden, M, static_cast<_Float16*>(xn), stream);
+      x = xn;
+    }
+    return launch_decode_mfma(wg, wu, wd, hidden, inter, x, y, M, inter_shift, out_shift, ws, stream, mlp_scale,
+                              res);
+  }
+  const float gu_scale = ldexpf(1.0f, -inter_shift);
+  const float dn_scale = ldexpf(1.0f, inter_shift - out_shift) * mlp_scale, res_scale = ldexpf(1.0f, -out_shift);
   _Float16* hbuf = static_cast<_Float16*>(ws);
   timing_begin(stream);
   hipError_t e = launch_rows_k<1, true>(wg, wu, hidden, inter, static_cast<const _Float16*>(x), M, hbuf, gu_scale,
-                                        stream);
+                                        nullptr, 0.0f, gm, eps, stream);
   timing_end(stream);
   if (e != hipSuccess) return e;
   timing_begin(stream);
-  e = launch_rows_k<1, false>(wd, nullptr, inter, hidden, hbuf, M, static_cast<_Float16*>(y), dn_scale, stream);
+  e = launch_rows_k<1, false>(wd, nullptr, inter, hidden, hbuf, M, static_cast<_Float16*>(y), dn_scale,
+                              static_cast<const _Float16*>(res), res_scale, nullptr, 0.0f, stream);
   timing_end(stream);
   return e;
 }

@@ -112,7 +112,8 @@ __device__ __forceinline__ int piece_slot(int bl, int c, int j) {
 template <int MM, bool GATEUP, int KS, int NBW>
 __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
                                                     int K, int N, const _Float16* __restrict__ xin, int M,
-                                                    _Float16* __restrict__ out, float scale) {
+                                                    _Float16* out, float scale, const _Float16* res,
+                                                    float res_scale) {
   constexpr int NMAT = GATEUP ? 2 : 1;
   constexpr int TSTRIDE = NBW * 256 + 32;     // halves per staged token (+64 B against bank conflicts)
   constexpr int NPIECE = MM * NBW * 32;       // pieces of 8 halves per pass
@@ -303,7 +304,9 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
   if (r < M) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float v = GATEUP ? silu_f32(acc0[e]) * acc1[e] * scale : acc0[e] * scale;
+      float v = GATEUP ? silu_f32(acc0[e]) * acc1[e] * scale : acc0[e] * scale;
+      // the residual (down pass only; it may be out itself: read, then written, here)
+      if (!GATEUP && res) v += (float)res[(size_t)r * N + tile * 16 + 4 * o + e] * res_scale;
       out[(size_t)r * N + tile * 16 + 4 * o + e] = (_Float16)v;
     }
   }
@@ -311,40 +314,49 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
 
 template <int MM>
 void launch_group_mfma(const void* wg, const void* wu, const void* wd, int hidden, int inter, const _Float16* x,
-                  _Float16* y, _Float16* h, int M, float gu_scale, float dn_scale, int stage, hipStream_t stream) {
+                       _Float16* y, _Float16* h, int M, float gu_scale, float dn_scale, const _Float16* res,
+                       float res_scale, int stage, hipStream_t stream) {
   if (stage == 0) {
     hipLaunchKernelGGL((k_decode<MM, true, KS_GU, NBW_GU>), dim3(inter / 16), dim3(64 * KS_GU), 0, stream,
                        static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu), hidden, inter, x, M, h,
-                       gu_scale);
+                       gu_scale, (const _Float16*)nullptr, 0.0f);
   } else {
     hipLaunchKernelGGL((k_decode<MM, false, KS_DN, NBW_DN>), dim3(hidden / 16), dim3(64 * KS_DN), 0, stream,
                        static_cast<const uint8_t*>(wd), static_cast<const uint8_t*>(nullptr), inter, hidden, h, M,
-                       y, dn_scale);
+                       y, dn_scale, res, res_scale);
   }
 }
 
 void launch_tokens_mfma(const void* wg, const void* wu, const void* wd, int hidden, int inter, const _Float16* x,
-                   _Float16* y, _Float16* h, int M, float gu_scale, float dn_scale, int stage, hipStream_t stream) {
-  if (M <= 1) launch_group_mfma<1>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, stage, stream);
-  else if (M <= 2) launch_group_mfma<2>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, stage, stream);
-  else launch_group_mfma<4>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, stage, stream);
+                        _Float16* y, _Float16* h, int M, float gu_scale, float dn_scale, const _Float16* res,
+                        float res_scale, int stage, hipStream_t stream) {
+  if (M <= 1)
+    launch_group_mfma<1>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, res, res_scale, stage, stream);
+  else if (M <= 2)
+    launch_group_mfma<2>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, res, res_scale, stage, stream);
+  else
+    launch_group_mfma<4>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, res, res_scale, stage, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
-                              void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
+                              void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream,
+                              float mlp_scale, const void* res) {
   const _Float16* xh = static_cast<const _Float16*>(x);
   _Float16* yh = static_cast<_Float16*>(y);
+  const _Float16* rh = static_cast<const _Float16*>(res);
   _Float16* hbuf = static_cast<_Float16*>(ws);
-  const float gu_scale = ldexpf(1.0f, -inter_shift), dn_scale = ldexpf(1.0f, inter_shift - out_shift);
+  const float gu_scale = ldexpf(1.0f, -inter_shift);
+  const float dn_scale = ldexpf(1.0f, inter_shift - out_shift) * mlp_scale, res_scale = ldexpf(1.0f, -out_shift);
   // groups of at most four tokens (the staged activation of one group fits LDS)
   for (int stage = 0; stage < 2; ++stage) {
     timing_begin(stream);
     for (int t0 = 0; t0 < M; t0 += 4) {
       const int mg = min(4, M - t0);
       launch_tokens_mfma(wg, wu, wd, hidden, inter, xh + (size_t)t0 * hidden, yh + (size_t)t0 * hidden,
-                         hbuf + (size_t)t0 * inter, mg, gu_scale, dn_scale, stage, stream);
+                         hbuf + (size_t)t0 * inter, mg, gu_scale, dn_scale, rh ? rh + (size_t)t0 * hidden : nullptr,
+                         res_scale, stage, stream);
     }
     timing_end(stream);
   }

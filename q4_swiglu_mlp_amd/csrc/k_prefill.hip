@@ -128,8 +128,11 @@ __global__ __launch_bounds__(256) void k_swiglu_f16(const _Float16* __restrict__
 // y[t][n] = fp16(sum_c P[c][n][t]) through a 64x64 LDS transpose.  Thread
 // (tx, ty) sums tokens 8tx..8tx+7 (one 16-byte load) of hidden rows ty and
 // ty + 32 over all chunks in fp32, four chunks' loads in flight at a time.
+// With RES, y = fp16(sum + res * res_scale): res is the [M x H] residual,
+// which may be y itself (each element is read and then written by one thread).
+template <bool RES>
 __global__ __launch_bounds__(256) void k_reduce_partials(const _Float16* __restrict__ P, int S, int H, int Mpad,
-                                                        _Float16* __restrict__ y, int M) {
+                                                        _Float16* y, int M, const _Float16* res, float res_scale) {
   __shared__ float tile[64][65];
   const int n0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
@@ -171,7 +174,11 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const _Float16* __restr
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int t = t0 + wy + 4 * i;
-    if (t < M) y[(size_t)t * H + n0 + wx] = (_Float16)tile[wx][wy + 4 * i];
+    if (t < M) {
+      float v = tile[wx][wy + 4 * i];
+      if constexpr (RES) v += (float)res[(size_t)t * H + n0 + wx] * res_scale;
+      y[(size_t)t * H + n0 + wx] = (_Float16)v;
+    }
   }
 }
 
@@ -180,8 +187,9 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const _Float16* __restr
 // 2np, 2np+1 x tokens 4tq..4tq+3) over all chunks in fp32, four chunks' loads
 // in flight at a time, and writes four 4-byte pieces of y; consecutive threads
 // take consecutive row pairs, so loads and stores are contiguous runs.
+template <bool RES>
 __global__ __launch_bounds__(256) void k_reduce_quads(const _Float16* __restrict__ P, int S, int H, int Mpad,
-                                                     _Float16* __restrict__ y, int M) {
+                                                     _Float16* y, int M, const _Float16* res, float res_scale) {
   const int np = blockIdx.x * 32 + (threadIdx.x & 31);   // row pair
   const int tq = blockIdx.y * 8 + (threadIdx.x >> 5);    // token quad
   const size_t plane = (size_t)(Mpad / 4) * H * 4;       // halves per chunk
@@ -208,7 +216,13 @@ __global__ __launch_bounds__(256) void k_reduce_quads(const _Float16* __restrict
   for (int e = 0; e < 4; ++e) {
     const int t = 4 * tq + e;
     if (t < M) {
-      const half2v v = {(_Float16)acc[e], (_Float16)acc[4 + e]};
+      float v0 = acc[e], v1 = acc[4 + e];
+      if constexpr (RES) {
+        const half2v rv = *reinterpret_cast<const half2v*>(res + (size_t)t * H + 2 * np);
+        v0 += (float)rv[0] * res_scale;
+        v1 += (float)rv[1] * res_scale;
+      }
+      const half2v v = {(_Float16)v0, (_Float16)v1};
       *reinterpret_cast<half2v*>(y + (size_t)t * H + 2 * np) = v;
     }
   }
@@ -322,17 +336,21 @@ hipError_t launch_prefill_staged(const void* wg, const void* wu, const void* wd,
                      inter_scale);
   hipLaunchKernelGGL((k_prefill_staged16<192, kUnitDown>), grid, block, 0, stream, bg, bu, bd, hidden, inter, xg, M,
                      P, p.Mpad, out_scale, p.n_tiles, p.n_chunks, (_Float16*)nullptr, (_Float16*)nullptr, Hm);
-  hipLaunchKernelGGL(k_reduce_quads, dim3(hidden / 64, p.Mpad / 32), dim3(256), 0, stream, P, p.n_chunks, hidden,
-                     p.Mpad, static_cast<_Float16*>(y), M);
+  hipLaunchKernelGGL(k_reduce_quads<false>, dim3(hidden / 64, p.Mpad / 32), dim3(256), 0, stream, P, p.n_chunks,
+                     hidden, p.Mpad, static_cast<_Float16*>(y), M, (const _Float16*)nullptr, 0.0f);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
-                          void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream) {
+                          void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream,
+                          float mlp_scale, const void* res) {
   const Plan p = make_plan(M, hidden, inter);
   _Float16* P = static_cast<_Float16*>(ws);
   const float inter_scale = ldexpf(1.0f, -inter_shift);
-  const float out_scale = ldexpf(1.0f, inter_shift - out_shift);
+  const float out_scale = ldexpf(1.0f, inter_shift - out_shift) * mlp_scale;
+  const float res_scale = ldexpf(1.0f, -out_shift);
+  const _Float16* rh = static_cast<const _Float16*>(res);
+  _Float16* yh = static_cast<_Float16*>(y);
   uint8_t* xg = static_cast<uint8_t*>(ws) + partial_bytes(p, hidden);
   if (p.cfg == 'D')
     hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream,
@@ -345,12 +363,19 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
     default: launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
   }
   timing_end(stream);
-  if (p.cfg == 'D')
-    hipLaunchKernelGGL(k_reduce_quads, dim3(hidden / 64, p.Mpad / 32), dim3(256), 0, stream, P, p.n_chunks, hidden,
-                       p.Mpad, static_cast<_Float16*>(y), M);
+  const dim3 rq(hidden / 64, p.Mpad / 32), rp(hidden / 64, p.Mpad / 64);
+  if (p.cfg == 'D' && rh)
+    hipLaunchKernelGGL(k_reduce_quads<true>, rq, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
+                       res_scale);
+  else if (p.cfg == 'D')
+    hipLaunchKernelGGL(k_reduce_quads<false>, rq, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
+                       res_scale);
+  else if (rh)
+    hipLaunchKernelGGL(k_reduce_partials<true>, rp, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
+                       res_scale);
   else
-    hipLaunchKernelGGL(k_reduce_partials, dim3(hidden / 64, p.Mpad / 64), dim3(256), 0, stream, P, p.n_chunks,
-                       hidden, p.Mpad, static_cast<_Float16*>(y), M);
+    hipLaunchKernelGGL(k_reduce_partials<false>, rp, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
+                       res_scale);
   return hipGetLastError();
 }
 

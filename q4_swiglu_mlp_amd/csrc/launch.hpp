@@ -17,9 +17,11 @@ hipError_t launch_q4k_dequant_f32(const void* blocks, int rows, int cols, float*
 
 // Fused prefill.
 size_t prefill_workspace_bytes(int M, int hidden, int inter);
+// mlp_scale multiplies the MLP output; res (nullable, [M x hidden] fp16, may be
+// y) is added at the output scale: y = fp16((res + mlp_scale * MLP(x)) * 2^-out_shift).
 hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter,
                           const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
-                          hipStream_t stream);
+                          hipStream_t stream, float mlp_scale = 1.0f, const void* res = nullptr);
 
 // The staged comparison baseline of the prefill: the same units with the
 // gate/up outputs and the intermediate in device memory (four main launches).
@@ -32,12 +34,16 @@ hipError_t launch_prefill_staged(const void* wg, const void* wu, const void* wd,
 // 16x16x32 MFMA tiles for M >= 2 (k_decode_mfma.hip); both write the fp16
 // intermediate [M x inter] into the workspace between their two kernels.
 size_t decode_workspace_bytes(int M, int hidden, int inter);
+// gamma (nullable): the pre-MLP RMS norm of x with weight gamma and eps is the
+// MLP's input; xn ([M x hidden] fp16 scratch) receives it where a kernel of its
+// own computes it.
 hipError_t launch_decode(const void* wg, const void* wu, const void* wd, int hidden, int inter,
                          const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
-                         hipStream_t stream);
+                         hipStream_t stream, float mlp_scale = 1.0f, const void* res = nullptr,
+                         const void* gamma = nullptr, float eps = 0.0f, void* xn = nullptr);
 hipError_t launch_decode_mfma(const void* wg, const void* wu, const void* wd, int hidden, int inter,
                               const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
-                              hipStream_t stream);
+                              hipStream_t stream, float mlp_scale = 1.0f, const void* res = nullptr);
 
 // Batched-expert MoE.
 size_t moe_workspace_bytes(int M, int top_k, int n_experts, int hidden, int inter);

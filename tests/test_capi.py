@@ -152,3 +152,36 @@ def test_router_argument_errors():
     # no tokens: nothing is read, so empty (NULL) buffers are accepted
     assert route(M=0) == 0 and route(M=0, logits=None, ids=None, p=None) == 0
     assert route(M=0, k=0) == -5
+
+
+def block(fn_name, **kw):
+    args = dict(wg=A, wu=A, wd=A, hidden=4096, inter=11008, x=A, g=A, eps=1e-5, s=1.0, y=A, M=4, a=0, b=0, ws=A,
+                wsb=1 << 31)
+    args.update(kw)
+    return getattr(Z.lib, fn_name)(args["wg"], args["wu"], args["wd"], args["hidden"], args["inter"], args["x"],
+                                   args["g"], args["eps"], args["s"], args["y"], args["M"], args["a"], args["b"],
+                                   args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("fn_name", ["zinc_mlp_q4k_prefill_block", "zinc_mlp_q4k_decode_block"])
+def test_block_argument_errors(fn_name):
+    f = lambda **kw: block(fn_name, **kw)
+    assert f(g=None) == -1 and f(x=None) == -1 and f(wd=None) == -1
+    assert f(g=A + 2) == -3 and f(x=MIS) == -3
+    assert f(eps=-1e-6) == -5 and f(eps=float("nan")) == -5 and f(eps=float("inf")) == -5
+    assert f(s=float("nan")) == -5 and f(s=float("inf")) == -5
+    assert f(hidden=300) == -2 and f(M=-1) == -5
+    assert f(ws=None) == -1 and f(wsb=16) == -4
+    assert f(M=0, ws=None, wsb=0) == 0
+    assert f(eps=0.0, M=0) == 0 and f(s=0.0, M=0) == 0
+
+
+def test_block_workspace_sizes():
+    for M in (1, 4):
+        assert Z.lib.zinc_mlp_q4k_decode_block_workspace_size(M, 4096, 11008) >= \
+            Z.decode_workspace_size(M, 4096, 11008) + M * 4096 * 2
+    assert Z.lib.zinc_mlp_q4k_prefill_block_workspace_size(256, 4096, 11008) >= \
+        Z.prefill_workspace_size(256, 4096, 11008) + 256 * 4096 * 2
+    assert Z.lib.zinc_mlp_q4k_decode_block_workspace_size(9, 4096, 11008) == 0
+    assert Z.lib.zinc_mlp_q4k_prefill_block_workspace_size(256, 4000, 11008) == 0
+    assert block("zinc_mlp_q4k_decode_block", M=9) == -5

@@ -393,6 +393,57 @@ def test_moe_out_of_range_ids_contribute_nothing():
 
 
 # ---------------------------------------------------------------------------
+# Pre-MLP RMS norm and the residual block
+# ---------------------------------------------------------------------------
+def test_rms_norm_matches_torch():
+    import torch
+    rng = np.random.default_rng(81)
+    x = rng.standard_normal((7, 512)) * 3
+    g = rng.uniform(0.5, 1.5, 512)
+    for eps in (0.0, 1e-6, 1e-2):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (512,), torch.from_numpy(g), eps).numpy()
+        assert np.allclose(O.rms_norm(x, g, eps), ref, rtol=1e-12, atol=0)
+
+
+def test_rms_norm_closed_forms():
+    # a row of +-c has mean square c^2: entries become +-c / sqrt(c^2 + eps)
+    c, eps = 3.0, 0.5
+    x = np.array([[c, -c, c, c]])
+    assert np.allclose(O.rms_norm(x, np.ones(4), eps), x / math.sqrt(c * c + eps), rtol=1e-15)
+    # with eps = 0 the result is scale invariant and has unit mean square
+    rng = np.random.default_rng(82)
+    x = rng.standard_normal((5, 64))
+    xn = O.rms_norm(x, np.ones(64), 0.0)
+    assert np.allclose(np.mean(xn * xn, axis=1), 1.0, rtol=1e-13)
+    assert np.allclose(O.rms_norm(x * 7.5, np.ones(64), 0.0), xn, rtol=1e-13)
+    # gamma multiplies column-wise
+    g = np.arange(1, 65, dtype=np.float64)
+    assert np.allclose(O.rms_norm(x, g, 0.0), xn * g, rtol=1e-13)
+
+
+def test_mlp_block_reductions():
+    H, I, M = 256, 512, 6
+    rng = np.random.default_rng(83)
+    wg, wu, wd = S.gen_q4k_blob(rng, I, H), S.gen_q4k_blob(rng, I, H), S.gen_q4k_blob(rng, H, I)
+    x = rng.standard_normal((M, H))
+    g = rng.uniform(0.5, 1.5, H)
+    # zero scale: the residual alone, exactly
+    y0, _ = O.mlp_block(x, g, 1e-5, 0.0, wg, wu, wd, H, I)
+    assert np.array_equal(y0, x)
+    # zero down weights: the MLP contributes exactly zero
+    wd0 = np.zeros((H, I // 256, 144), dtype=np.uint8)   # d = dmin = 0: every weight is zero
+    yz, _ = O.mlp_block(x, g, 1e-5, 2.0, wg, wu, wd0, H, I)
+    assert np.array_equal(yz, x)
+    # the MLP part is linear in the scale and is the MLP of the normalised rows
+    y1, xn = O.mlp_block(x, g, 1e-5, 1.0, wg, wu, wd, H, I)
+    y3, _ = O.mlp_block(x, g, 1e-5, 3.0, wg, wu, wd, H, I)
+    assert np.allclose(y3 - x, 3.0 * (y1 - x), rtol=1e-12, atol=1e-9)
+    # the norm's output does not depend on the residual's scale (eps = 0)
+    y2, xn2 = O.mlp_block(2.0 * x, g, 0.0, 1.0, wg, wu, wd, H, I)
+    assert np.allclose(xn2, O.rms_norm(x, g, 0.0), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # Router: top-k selection and the softmax of the chosen logits
 # ---------------------------------------------------------------------------
 def test_router_matches_brute_force_subset_search():
