@@ -21,6 +21,10 @@ Plain, slow, obviously-correct float64 numpy:
 * ``moe``: the batched-expert form of "Four bottlenecks, one CUDA backend",
   "Bottleneck 2": each token's output is the mixing-weighted sum of its chosen
   experts' MLP outputs; expert ids are inputs.
+* ``q5k_fields`` / ``q5k_dequant`` and ``q5_1_fields`` / ``q5_1_dequant``: the
+  two other block formats the pages name for the experts' down projections,
+  written out from the public GGUF definitions like Q4_K; ``mlp`` and ``moe``
+  take the down projection's format.
 * ``rms_norm`` / ``mlp_block``: the block with its neighbours -- the pre-MLP
   RMS norm and the residual add (with a per-layer scale on the MLP output).
 * ``route_topk``: the router step before it -- per token the top-k experts by
@@ -109,6 +113,82 @@ def q4k_dequant_f32(blob: np.ndarray, rows: int, cols: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Q5_K and Q5_1 decode (the experts' down projections of "Four bottlenecks,
+# one CUDA backend", "Bottleneck 2": Q5_K for one MoE family, Q5_1 for the
+# other).  The pages name the formats only; the layouts are the public GGUF
+# blocks, as for Q4_K.
+# ----------------------------------------------------------------------------
+Q5K_BLOCK_BYTES = 176
+Q5_1_WEIGHTS = 32
+Q5_1_BLOCK_BYTES = 24
+
+
+def q5k_fields(blob: np.ndarray):
+    """Unpack every Q5_K super-block of ``blob`` (uint8, last axis 176).
+
+    Returns ``d, dmin, sc, m`` as ``q4k_fields`` and ``q`` (int64, ``[..., 256]``,
+    0..31).  Layout (GGUF Q5_K, little-endian): bytes 0-15 as in Q4_K (d, dmin
+    and the twelve bytes of 6-bit scales and mins, same packing); QH = bytes
+    16..47; Q = bytes 48..175.  Weight i = 64*c + 32*u + l (chunk c, half u,
+    l < 32): its low four bits are the low (u = 0) or high (u = 1) nibble of
+    Q[32*c + l], its fifth bit is bit 2*c + u of QH[l]."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    if blob.shape[-1] != Q5K_BLOCK_BYTES:
+        raise ValueError("last axis must be 176 bytes")
+    d, dmin, sc, m, _ = q4k_fields(np.concatenate([blob[..., :16], blob[..., 48:176]], axis=-1))
+    QH = blob[..., 16:48].astype(np.int64)
+    Q = blob[..., 48:176].astype(np.int64)
+    i = np.arange(QK_K)
+    c, u, l = i // 64, (i % 64) // 32, i % 32
+    byte = Q[..., 32 * c + l]
+    low4 = np.where(u == 1, byte >> 4, byte & 15)
+    fifth = (QH[..., l] >> (2 * c + u)) & 1
+    return d, dmin, sc, m, low4 | (fifth << 4)
+
+
+def q5k_dequant(blob: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Exact float64 weights of a Q5_K matrix: d*sc_{i//32}*q_i - dmin*m_{i//32}
+    (every product fits 22 significant bits, so the value is exact)."""
+    blob = np.asarray(blob, dtype=np.uint8).reshape(rows, cols // QK_K, Q5K_BLOCK_BYTES)
+    d, dmin, sc, m, q = q5k_fields(blob)
+    sub = np.arange(QK_K) // 32
+    w = d[..., None] * sc[..., sub] * q - dmin[..., None] * m[..., sub]
+    return w.reshape(rows, cols)
+
+
+def q5_1_fields(blob: np.ndarray):
+    """Unpack every Q5_1 block of ``blob`` (uint8, last axis 24): ``d, m``
+    (float64) and ``q`` (int64, ``[..., 32]``, 0..31).  Layout (GGUF Q5_1,
+    little-endian): bytes 0-1 ``d``, bytes 2-3 ``m`` (IEEE fp16), bytes 4-7 QH (a
+    32-bit word), bytes 8..23 Q.  Weight i < 16 takes the low nibble of Q[i],
+    weight 16 + i the high nibble of Q[i]; bit i of QH is the fifth bit of
+    weight i."""
+    blob = np.asarray(blob, dtype=np.uint8)
+    if blob.shape[-1] != Q5_1_BLOCK_BYTES:
+        raise ValueError("last axis must be 24 bytes")
+    d = blob[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
+    mm = blob[..., 2:4].copy().view(np.float16)[..., 0].astype(np.float64)
+    qh = (blob[..., 4].astype(np.int64) | (blob[..., 5].astype(np.int64) << 8) |
+          (blob[..., 6].astype(np.int64) << 16) | (blob[..., 7].astype(np.int64) << 24))
+    Q = blob[..., 8:24].astype(np.int64)
+    i = np.arange(Q5_1_WEIGHTS)
+    byte = Q[..., i % 16]
+    low4 = np.where(i >= 16, byte >> 4, byte & 15)
+    fifth = (qh[..., None] >> i) & 1
+    return d, mm, low4 | (fifth << 4)
+
+
+def q5_1_dequant(blob: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Exact float64 weights of a Q5_1 matrix: W[r, 32*b + i] = d*q_i + m."""
+    blob = np.asarray(blob, dtype=np.uint8).reshape(rows, cols // Q5_1_WEIGHTS, Q5_1_BLOCK_BYTES)
+    d, mm, q = q5_1_fields(blob)
+    return (d[..., None] * q + mm[..., None]).reshape(rows, cols)
+
+
+DOWN_DECODERS = {"q4_k": q4k_dequant, "q5_k": q5k_dequant, "q5_1": q5_1_dequant}
+
+
+# ----------------------------------------------------------------------------
 # SwiGLU MLP
 # ----------------------------------------------------------------------------
 def silu(z: np.ndarray) -> np.ndarray:
@@ -131,11 +211,12 @@ def mlp_from_weights(x: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarr
     return y, h
 
 
-def mlp(x, wg_blob, wu_blob, wd_blob, hidden: int, inter: int):
-    """Dense Q4_K SwiGLU block: ``(y, h)`` in float64 from the raw blobs."""
+def mlp(x, wg_blob, wu_blob, wd_blob, hidden: int, inter: int, down_format: str = "q4_k"):
+    """Dense SwiGLU block: ``(y, h)`` in float64 from the raw blobs (Q4_K gate
+    and up; the down projection in ``down_format``)."""
     Wg = q4k_dequant(wg_blob, inter, hidden)
     Wu = q4k_dequant(wu_blob, inter, hidden)
-    Wd = q4k_dequant(wd_blob, hidden, inter)
+    Wd = DOWN_DECODERS[down_format](wd_blob, hidden, inter)
     return mlp_from_weights(x, Wg, Wu, Wd)
 
 
@@ -160,11 +241,12 @@ def mlp_block(x, gamma, eps: float, mlp_scale: float, wg_blob, wu_blob, wd_blob,
     return np.asarray(x, dtype=np.float64) + float(mlp_scale) * ym, xn
 
 
-def moe(x, wg_blobs, wu_blobs, wd_blobs, ids, p, hidden: int, inter: int):
+def moe(x, wg_blobs, wu_blobs, wd_blobs, ids, p, hidden: int, inter: int, down_format: str = "q4_k"):
     """Batched-expert MLP: y[t] = sum_s p[t,s] * MLP_{ids[t,s]}(x[t]).
 
     ``wg_blobs``/``wu_blobs``: ``[E, inter, hidden/256, 144]``; ``wd_blobs``:
-    ``[E, hidden, inter/256, 144]``; ``ids`` int ``[M, k]``; ``p`` float32
+    ``[E, hidden, ...]`` blocks of ``down_format`` (Q4_K by default, or Q5_K /
+    Q5_1); ``ids`` int ``[M, k]``; ``p`` float32
     ``[M, k]`` (widened to float64).  A slot whose id is outside [0, E)
     contributes nothing.  Returns ``(y [M x hidden] float64, n_bad_slots)``."""
     x64 = np.asarray(x, dtype=np.float64)
@@ -178,7 +260,7 @@ def moe(x, wg_blobs, wu_blobs, wd_blobs, ids, p, hidden: int, inter: int):
         rows, slots = np.nonzero(ids == e)
         if rows.size == 0:
             continue
-        ye, _ = mlp(x64[rows], wg_blobs[e], wu_blobs[e], wd_blobs[e], hidden, inter)
+        ye, _ = mlp(x64[rows], wg_blobs[e], wu_blobs[e], wd_blobs[e], hidden, inter, down_format)
         np.add.at(y, rows, p64[rows, slots][:, None] * ye)
     return y, bad
 

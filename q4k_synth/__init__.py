@@ -146,3 +146,31 @@ def gen_router_logits(rng: np.random.Generator, M: int, n_experts: int, scale: f
 def workload_router_logits(w: Workload, M: int | None = None):
     rng = np.random.default_rng([w.seed, 2000])
     return gen_router_logits(rng, w.M if M is None else M, w.n_experts)
+
+
+def gen_q5k_blob(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
+    """A Q5_K matrix ``[rows, cols/256, 176]``: uniform random bytes for the
+    scales, the fifth bits and the quants; d and dmin as for Q4_K."""
+    nb = cols // 256
+    blob = rng.integers(0, 256, size=(rows, nb, 176), dtype=np.uint8)
+    for off in (0, 2):
+        v = rng.uniform(1e-3, 1e-2, size=(rows, nb)).astype(np.float16)
+        blob[..., off:off + 2] = v.view(np.uint8).reshape(rows, nb, 2)
+    return blob
+
+
+def gen_q5_1_blob(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
+    """A Q5_1 matrix ``[rows, cols/32, 24]``: uniform random fifth bits and
+    quants, d ~ U[1e-3, 1e-2] and m = -16 d u with u ~ U[0.5, 1.5] (so the
+    weights d q + m straddle zero), both rounded to fp16."""
+    nb = cols // 32
+    blob = rng.integers(0, 256, size=(rows, nb, 24), dtype=np.uint8)
+    d = rng.uniform(1e-3, 1e-2, size=(rows, nb))
+    m = -16.0 * d * rng.uniform(0.5, 1.5, size=(rows, nb))
+    blob[..., 0:2] = d.astype(np.float16).view(np.uint8).reshape(rows, nb, 2)
+    blob[..., 2:4] = m.astype(np.float16).view(np.uint8).reshape(rows, nb, 2)
+    return blob
+
+
+def gen_down_blob(rng: np.random.Generator, fmt: str, rows: int, cols: int) -> np.ndarray:
+    return {"q4_k": gen_q4k_blob, "q5_k": gen_q5k_blob, "q5_1": gen_q5_1_blob}[fmt](rng, rows, cols)

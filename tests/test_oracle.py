@@ -393,6 +393,133 @@ def test_moe_out_of_range_ids_contribute_nothing():
 
 
 # ---------------------------------------------------------------------------
+# Q5_K and Q5_1 blocks (the experts' other down-projection formats)
+# ---------------------------------------------------------------------------
+def _q5k_block(d_bits=0x3C00, dmin_bits=0, S=None, QH=None, Q=None):
+    b = np.zeros(176, dtype=np.uint8)
+    b[0:2] = [d_bits & 0xFF, d_bits >> 8]
+    b[2:4] = [dmin_bits & 0xFF, dmin_bits >> 8]
+    b[4:16] = B.S_UNIT_SCALES if S is None else S
+    if QH is not None:
+        b[16:48] = QH
+    if Q is not None:
+        b[48:176] = Q
+    return b
+
+
+def _q5_1_block(d_bits=0x3C00, m_bits=0, qh=0, Q=None):
+    b = np.zeros(24, dtype=np.uint8)
+    b[0:2] = [d_bits & 0xFF, d_bits >> 8]
+    b[2:4] = [m_bits & 0xFF, m_bits >> 8]
+    b[4:8] = [(qh >> (8 * k)) & 0xFF for k in range(4)]
+    if Q is not None:
+        b[8:24] = Q
+    return b
+
+
+def test_q5k_unit_scales_closed_forms():
+    # quants 0x21 everywhere: low nibble 1, high nibble 2; no fifth bits
+    w = O.q5k_dequant(_q5k_block(Q=[0x21] * 128), 1, 256)[0]
+    assert np.array_equal(w, np.where((np.arange(256) % 64) < 32, 1.0, 2.0))
+    # every fifth bit set: +16 on every weight
+    w = O.q5k_dequant(_q5k_block(QH=[0xFF] * 32, Q=[0x21] * 128), 1, 256)[0]
+    assert np.array_equal(w, np.where((np.arange(256) % 64) < 32, 17.0, 18.0))
+
+
+@pytest.mark.parametrize("bit", range(8))
+def test_q5k_fifth_bit_walk(bit):
+    """Bit b of QH[l] is the fifth bit of weight 64*(b//2) + 32*(b%2) + l only
+    (the inverse of the field formula, walked bit by bit)."""
+    for l in (0, 7, 31):
+        QH = np.zeros(32, dtype=np.uint8)
+        QH[l] = 1 << bit
+        w = O.q5k_dequant(_q5k_block(QH=QH), 1, 256)[0]
+        expect = np.zeros(256)
+        expect[64 * (bit // 2) + 32 * (bit % 2) + l] = 16.0
+        assert np.array_equal(w, expect)
+
+
+def test_q5k_scales_and_mins_follow_q4k_packing():
+    rng = np.random.default_rng(91)
+    blob = S.gen_q5k_blob(rng, 3, 512)
+    # the same header and quant nibbles in a Q4_K block decode to the Q5_K
+    # weights minus 16*d*sc on the weights whose fifth bit is set
+    q4 = np.concatenate([blob[..., :16], blob[..., 48:]], axis=-1)
+    w4 = O.q4k_dequant(q4, 3, 512).reshape(3, 2, 256)
+    w5 = O.q5k_dequant(blob, 3, 512).reshape(3, 2, 256)
+    d, dmin, sc, m, q = O.q5k_fields(blob)
+    sub = np.arange(256) // 32
+    assert np.array_equal(w5 - w4, d[..., None] * sc[..., sub] * 16.0 * (q >> 4))
+
+
+def test_q5_1_closed_forms():
+    # d = 1, m = 0: low nibbles 1 (weights 0..15), high nibbles 2 (16..31)
+    w = O.q5_1_dequant(_q5_1_block(Q=[0x21] * 16), 1, 32)[0]
+    assert np.array_equal(w, np.r_[np.ones(16), 2 * np.ones(16)])
+    # m = -1 adds -1; d = 0.5 halves
+    w = O.q5_1_dequant(_q5_1_block(d_bits=0x3800, m_bits=0xBC00, Q=[0x21] * 16), 1, 32)[0]
+    assert np.array_equal(w, np.r_[-0.5 * np.ones(16), np.zeros(16)])
+    # each bit of QH is one weight's fifth bit
+    for j in (0, 5, 15, 16, 31):
+        w = O.q5_1_dequant(_q5_1_block(qh=1 << j), 1, 32)[0]
+        expect = np.zeros(32)
+        expect[j] = 16.0
+        assert np.array_equal(w, expect)
+
+
+def test_q5_1_matrix_layout_and_brute_force():
+    rng = np.random.default_rng(92)
+    blob = S.gen_q5_1_blob(rng, 2, 64)
+    w = O.q5_1_dequant(blob, 2, 64)
+    for r in range(2):
+        for col in range(64):
+            b = blob[r, col // 32]
+            i = col % 32
+            d = float(np.frombuffer(b[0:2].tobytes(), np.float16)[0])
+            m = float(np.frombuffer(b[2:4].tobytes(), np.float16)[0])
+            qh = int.from_bytes(b[4:8].tobytes(), "little")
+            nib = (b[8 + i % 16] >> (4 if i >= 16 else 0)) & 15
+            assert w[r, col] == d * (nib + 16 * ((qh >> i) & 1)) + m
+
+
+@pytest.mark.parametrize("fmt", ["q5_k", "q5_1"])
+def test_q5_float64_weights_are_exact(fmt):
+    """The float64 weights equal the exact rational values of the fields, so
+    rounding them once to fp32 gives the unique fp32 weight."""
+    rng = np.random.default_rng(93)
+    blob = S.gen_down_blob(rng, fmt, 4, 512)
+    w = O.DOWN_DECODERS[fmt](blob, 4, 512)
+    F = lambda v: Fraction(float(v))
+    if fmt == "q5_k":
+        d, dmin, sc, m, q = O.q5k_fields(blob)
+        for r, b, i in [(0, 0, 0), (1, 1, 77), (3, 0, 255), (2, 1, 130)]:
+            j = i // 32
+            exact = F(d[r, b]) * int(sc[r, b, j]) * int(q[r, b, i]) - F(dmin[r, b]) * int(m[r, b, j])
+            assert Fraction(float(w[r, 256 * b + i])) == exact
+    else:
+        d, mm, q = O.q5_1_fields(blob)
+        for r, b, i in [(0, 0, 0), (1, 7, 19), (3, 15, 31), (2, 3, 16)]:
+            exact = F(d[r, b]) * int(q[r, b, i]) + F(mm[r, b])
+            assert Fraction(float(w[r, 32 * b + i])) == exact
+
+
+def test_moe_down_formats_reduce_to_dense():
+    E, H, I, M = 3, 256, 256, 5
+    rng = np.random.default_rng(94)
+    wg = np.stack([S.gen_q4k_blob(rng, I, H) for _ in range(E)])
+    wu = np.stack([S.gen_q4k_blob(rng, I, H) for _ in range(E)])
+    x = rng.standard_normal((M, H))
+    for fmt in ("q5_k", "q5_1"):
+        wd = np.stack([S.gen_down_blob(rng, fmt, H, I) for _ in range(E)])
+        ids = np.full((M, 1), 2, np.int32)
+        y, _ = O.moe(x, wg, wu, wd, ids, np.ones((M, 1), np.float32), H, I, fmt)
+        Wd = O.DOWN_DECODERS[fmt](wd[2], H, I)
+        g = x @ O.q4k_dequant(wg[2], I, H).T
+        u = x @ O.q4k_dequant(wu[2], I, H).T
+        assert np.allclose(y, (O.silu(g) * u) @ Wd.T, rtol=1e-12, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
 # Pre-MLP RMS norm and the residual block
 # ---------------------------------------------------------------------------
 def test_rms_norm_matches_torch():
