@@ -376,6 +376,27 @@ def moe_lines(args, torch, np, Z, S, dev, t):
         Z.zinc_moe_q4k_experts(eg, eu, ed, w.n_experts, w.hidden, w.inter, gx, rids, rp, w.inter_shift, w.out_shift,
                                y=y, workspace=ws)
 
+    # the same experts with their down projections in Q5_K and Q5_1 (one
+    # expert set each, the weights rotated with the Q4_K set's up projections)
+    rng = np.random.default_rng([w.seed, 50])
+    for fmt in ("q5_k", "q5_1"):
+        wd5 = t(np.stack([S.gen_down_blob(rng, fmt, w.hidden, w.inter) for _ in range(w.n_experts)]))
+
+        def fcall(i):
+            eg, eu, _ = sets[i % 2]
+            Z.zinc_moe_experts_fmt(eg, eu, wd5, fmt, w.n_experts, w.hidden, w.inter, gx, gids, gp, w.inter_shift,
+                                   w.out_shift, y=y, workspace=ws)
+
+        fwall, fms = time_calls(fcall, steps, 10, torch)
+        out.append({
+            "workload": f"MoE E=64 top-8, 2048->768, M=512, down projections in {fmt.upper()}",
+            "tokens_per_s": round(w.M / (fwall / steps), 1),
+            "us_per_call": round(fwall / steps * 1e6, 3),
+            "k_moe_fused_us": round(sum(fms) / len(fms) * 1e3, 3),
+        })
+        log(f"[bench] {out[-1]}")
+        del wd5
+
     rwall, rms = time_calls(rcall, steps, 10, torch)
     lwall, _ = time_calls(lcall, steps, 10, torch)
     out.append({

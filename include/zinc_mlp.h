@@ -86,6 +86,24 @@ const char* zinc_hip_error_string(void);
 int zinc_q4k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* out, void* stream);
 
 /*
+ * The decoders of the two other block formats the experts' down projections
+ * use ("Four bottlenecks, one CUDA backend", "Bottleneck 2": Q5_K for one MoE
+ * family, Q5_1 for the other; layouts are the public GGUF blocks):
+ *   Q5_K: 176-byte super-blocks of 256 weights: bytes 0-15 as Q4_K (d, dmin,
+ *         6-bit scales and mins), bytes 16-47 the fifth bits (bit 2c+u of byte
+ *         l for weight 64c + 32u + l), bytes 48-175 the low nibbles as Q4_K;
+ *         w = d*sc*q - dmin*m with q in 0..31.  cols % 256 == 0.
+ *   Q5_1: 24-byte blocks of 32 weights: fp16 d, fp16 m, a 32-bit word of fifth
+ *         bits (bit i for weight i), 16 quant bytes (weight i < 16 the low
+ *         nibble of byte i, weight 16 + i the high nibble); w = d*q + m.
+ *         cols % 32 == 0.
+ * Each weight is the exact value rounded once to fp32 (unique); out is
+ * [rows x cols] fp32, 16-byte aligned, as blocks.  Errors as the Q4_K decoder.
+ */
+int zinc_q5k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* out, void* stream);
+int zinc_q5_1_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* out, void* stream);
+
+/*
  * Batched prefill: y[M x hidden] = MLP(x[M x hidden]) for any M >= 0.
  * One fused kernel decodes the gate/up Q4_K blocks in registers into fp16 MFMA
  * operands (fp32 accumulation), applies SwiGLU in registers, stages the
@@ -198,6 +216,28 @@ int zinc_mlp_q4k_decode(const void* w_gate, const void* w_up, const void* w_down
 size_t zinc_moe_q4k_experts_workspace_size(int32_t M, int32_t top_k, int32_t n_experts,
                                            int32_t hidden, int32_t inter);
 int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_down,
+                         int32_t n_experts, int32_t hidden, int32_t inter,
+                         const void* x_f16, int32_t M,
+                         const int32_t* expert_ids, const float* expert_weights, int32_t top_k,
+                         void* y_f16, int32_t inter_shift, int32_t out_shift,
+                         void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                         void* stream);
+
+/*
+ * The batched-expert call with W_down in another block format ("Four
+ * bottlenecks, one CUDA backend", "Bottleneck 2": one MoE family's experts
+ * project down in Q5_K, another's in Q5_1; gate and up stay Q4_K).
+ * down_format: ZINC_DOWN_Q4_K (the same as zinc_moe_q4k_experts), ZINC_DOWN_Q5_K
+ * (w_down holds n_experts [hidden x inter] matrices of 176-byte blocks) or
+ * ZINC_DOWN_Q5_1 (24-byte blocks of 32 weights); the layouts are those of the
+ * decoders above.  The fifth bits are OR'ed into the same fp16 operand
+ * patterns, so the unit and its arithmetic are the Q4_K call's; the Q5_1 min
+ * term (+m per 32 weights) is contracted against the strip's 32-row means as
+ * the Q4_K one is.  Any other down_format -> ZINC_ERR_ARG.  Everything else
+ * (arguments, limits, errors, workspace size) as zinc_moe_q4k_experts.
+ */
+enum { ZINC_DOWN_Q4_K = 0, ZINC_DOWN_Q5_K = 1, ZINC_DOWN_Q5_1 = 2 };
+int zinc_moe_experts_fmt(const void* w_gate, const void* w_up, const void* w_down, int32_t down_format,
                          int32_t n_experts, int32_t hidden, int32_t inter,
                          const void* x_f16, int32_t M,
                          const int32_t* expert_ids, const float* expert_weights, int32_t top_k,

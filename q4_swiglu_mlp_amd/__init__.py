@@ -37,6 +37,8 @@ EXPORTS = (
     "zinc_strerror",
     "zinc_hip_error_string",
     "zinc_q4k_dequant_f32",
+    "zinc_q5k_dequant_f32",
+    "zinc_q5_1_dequant_f32",
     "zinc_mlp_q4k_prefill_workspace_size",
     "zinc_mlp_q4k_prefill",
     "zinc_mlp_q4k_prefill_block_workspace_size",
@@ -49,6 +51,7 @@ EXPORTS = (
     "zinc_mlp_q4k_decode",
     "zinc_moe_q4k_experts_workspace_size",
     "zinc_moe_q4k_experts",
+    "zinc_moe_experts_fmt",
     "zinc_moe_route_topk",
     "zinc_timing_enable",
     "zinc_timing_collect",
@@ -83,6 +86,9 @@ def _load() -> ctypes.CDLL:
     lib.zinc_hip_error_string.argtypes = []
     lib.zinc_q4k_dequant_f32.restype = ctypes.c_int
     lib.zinc_q4k_dequant_f32.argtypes = [P, I32, I32, P, P]
+    for name in ("zinc_q5k_dequant_f32", "zinc_q5_1_dequant_f32"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [P, I32, I32, P, P]
     for name in ("zinc_mlp_q4k_prefill_workspace_size", "zinc_mlp_q4k_prefill_staged_workspace_size",
                  "zinc_mlp_q4k_decode_workspace_size", "zinc_mlp_q4k_prefill_block_workspace_size",
                  "zinc_mlp_q4k_decode_block_workspace_size"):
@@ -102,6 +108,8 @@ def _load() -> ctypes.CDLL:
     lib.zinc_moe_q4k_experts_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.zinc_moe_q4k_experts.restype = ctypes.c_int
     lib.zinc_moe_q4k_experts.argtypes = [P, P, P, I32, I32, I32, P, I32, P, P, I32, P, I32, I32, P, SZ, P, P]
+    lib.zinc_moe_experts_fmt.restype = ctypes.c_int
+    lib.zinc_moe_experts_fmt.argtypes = [P, P, P, I32, I32, I32, I32, P, I32, P, P, I32, P, I32, I32, P, SZ, P, P]
     lib.zinc_moe_route_topk.restype = ctypes.c_int
     lib.zinc_moe_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
     lib.zinc_timing_enable.restype = ctypes.c_int
@@ -175,6 +183,17 @@ def zinc_q4k_dequant_f32(blocks, rows: int, cols: int, out=None, stream=None):
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=blocks.device)
     _check(lib.zinc_q4k_dequant_f32(_ptr(blocks), rows, cols, _ptr(out), _stream(stream)), "zinc_q4k_dequant_f32")
+    return out
+
+
+def zinc_q5_dequant_f32(fmt: str, blocks, rows: int, cols: int, out=None, stream=None):
+    """The fp32 weights of a Q5_K (``fmt="q5_k"``) or Q5_1 (``"q5_1"``) matrix."""
+    torch = _torch()
+    _require_cuda(blocks, out)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=blocks.device)
+    name = {"q5_k": "zinc_q5k_dequant_f32", "q5_1": "zinc_q5_1_dequant_f32"}[fmt]
+    _check(getattr(lib, name)(_ptr(blocks), rows, cols, _ptr(out), _stream(stream)), name)
     return out
 
 
@@ -282,6 +301,30 @@ def zinc_moe_q4k_experts(w_gate, w_up, w_down, n_experts: int, hidden: int, inte
                                   _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                   _ptr(dev_error), _stream(stream))
     _check(st, "zinc_moe_q4k_experts")
+    return y
+
+
+DOWN_FORMATS = {"q4_k": 0, "q5_k": 1, "q5_1": 2}
+
+
+def zinc_moe_experts_fmt(w_gate, w_up, w_down, down_format: str, n_experts: int, hidden: int, inter: int, x,
+                         expert_ids, expert_weights, inter_shift: int = 0, out_shift: int = 0, y=None,
+                         workspace=None, dev_error=None, stream=None):
+    """The batched-expert call with W_down in ``down_format`` ("q4_k", "q5_k" or "q5_1")."""
+    torch = _torch()
+    _require_cuda(w_gate, w_up, w_down, x, expert_ids, expert_weights, y, workspace, dev_error)
+    M = int(x.shape[0])
+    top_k = int(expert_ids.shape[1]) if expert_ids.dim() == 2 else 1
+    if y is None:
+        y = torch.empty((M, hidden), dtype=torch.float16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(moe_workspace_size(M, top_k, n_experts, hidden, inter), 16), dtype=torch.uint8,
+                                device=x.device)
+    st = lib.zinc_moe_experts_fmt(_ptr(w_gate), _ptr(w_up), _ptr(w_down), DOWN_FORMATS[down_format], n_experts,
+                                  hidden, inter, _ptr(x), M, _ptr(expert_ids), _ptr(expert_weights), top_k, _ptr(y),
+                                  inter_shift, out_shift, _ptr(workspace),
+                                  int(workspace.numel() * workspace.element_size()), _ptr(dev_error), _stream(stream))
+    _check(st, "zinc_moe_experts_fmt")
     return y
 
 

@@ -100,6 +100,25 @@ int zinc_q4k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* 
   return from_hip(zinc::launch_q4k_dequant_f32(blocks, rows, cols, out, static_cast<hipStream_t>(stream)));
 }
 
+static int q5_dequant(int fmt, const void* blocks, int32_t rows, int32_t cols, float* out, void* stream) {
+  if (!blocks || !out) return ZINC_ERR_NULL;
+  if (cols <= 0 || cols % (fmt == 1 ? 256 : 32) != 0) return ZINC_ERR_SHAPE;
+  if (rows < 0) return ZINC_ERR_ARG;
+  if ((long long)rows * cols > INT32_MAX) return ZINC_ERR_SHAPE;
+  if (!aligned16(blocks) || !aligned16(out)) return ZINC_ERR_ALIGN;
+  if (rows == 0) return ZINC_OK;
+  (void)hipGetLastError();
+  return from_hip(zinc::launch_q5_dequant_f32(fmt, blocks, rows, cols, out, static_cast<hipStream_t>(stream)));
+}
+
+int zinc_q5k_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* out, void* stream) {
+  return q5_dequant(1, blocks, rows, cols, out, stream);
+}
+
+int zinc_q5_1_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float* out, void* stream) {
+  return q5_dequant(2, blocks, rows, cols, out, stream);
+}
+
 size_t zinc_mlp_q4k_prefill_workspace_size(int32_t M, int32_t hidden, int32_t inter) {
   if (M < 0 || M > kMaxPrefillM || !dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return 0;
   if (!staged_ok(M, hidden)) return 0;
@@ -200,6 +219,16 @@ int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_dow
                          const float* expert_weights, int32_t top_k, void* y_f16, int32_t inter_shift,
                          int32_t out_shift, void* workspace, size_t workspace_bytes, int32_t* dev_error,
                          void* stream) {
+  return zinc_moe_experts_fmt(w_gate, w_up, w_down, ZINC_DOWN_Q4_K, n_experts, hidden, inter, x_f16, M, expert_ids,
+                              expert_weights, top_k, y_f16, inter_shift, out_shift, workspace, workspace_bytes,
+                              dev_error, stream);
+}
+
+int zinc_moe_experts_fmt(const void* w_gate, const void* w_up, const void* w_down, int32_t down_format,
+                         int32_t n_experts, int32_t hidden, int32_t inter, const void* x_f16, int32_t M,
+                         const int32_t* expert_ids, const float* expert_weights, int32_t top_k, void* y_f16,
+                         int32_t inter_shift, int32_t out_shift, void* workspace, size_t workspace_bytes,
+                         int32_t* dev_error, void* stream) {
   if (!w_gate || !w_up || !w_down || !x_f16 || !y_f16 || !expert_ids || !expert_weights) return ZINC_ERR_NULL;
   if (!dim_ok(hidden, kMaxHidden) || !dim_ok(inter, kMaxInter)) return ZINC_ERR_SHAPE;
   if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(x_f16) || !aligned16(y_f16) ||
@@ -209,6 +238,8 @@ int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_dow
   if (M < 0 || (long long)M * top_k > kMaxMoeSlots) return ZINC_ERR_ARG;
   if (!moe_rows_ok(M, top_k, hidden) || !staged_ok(M, hidden)) return ZINC_ERR_ARG;
   if (inter_shift < 0 || inter_shift > kMaxShift || out_shift < 0 || out_shift > kMaxShift) return ZINC_ERR_ARG;
+  if (down_format != ZINC_DOWN_Q4_K && down_format != ZINC_DOWN_Q5_K && down_format != ZINC_DOWN_Q5_1)
+    return ZINC_ERR_ARG;
   if (M == 0) return ZINC_OK;
   if (!workspace) return ZINC_ERR_NULL;
   if (!aligned16(workspace)) return ZINC_ERR_ALIGN;
@@ -216,7 +247,7 @@ int zinc_moe_q4k_experts(const void* w_gate, const void* w_up, const void* w_dow
   (void)hipGetLastError();
   return from_hip(zinc::launch_moe(w_gate, w_up, w_down, n_experts, hidden, inter, x_f16, M, expert_ids,
                                    expert_weights, top_k, y_f16, inter_shift, out_shift, workspace, dev_error,
-                                   static_cast<hipStream_t>(stream)));
+                                   static_cast<hipStream_t>(stream), down_format));
 }
 
 int zinc_moe_route_topk(const float* logits, int32_t M, int32_t n_experts, int32_t top_k, int32_t* expert_ids,

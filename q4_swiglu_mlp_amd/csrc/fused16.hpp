@@ -316,6 +316,121 @@ struct OutQuads {
   }
 };
 
+// Formats of W_down in the unit's phase 2: Q4_K (the dense path and the
+// default), and the experts' other two, Q5_K and Q5_1.
+enum : int { kDownQ4K = 0, kDownQ5K = 1, kDownQ51 = 2 };
+
+// w' = q*s for one quant dword and its fifth bits: the Q4_K operand slots of
+// dequant_dword_scaled, with the fifth bit of each low nibble taken from bit
+// 2*CH of the same byte of QH and that of each high nibble from bit 2*CH + 1,
+// OR'ed into the exponent patterns (1024 + q and 64 + q stay within one fp16
+// binade for q < 32).
+template <int CH>
+__device__ __forceinline__ half8 dequant5_dword_sc(uint32_t Q, uint32_t QH, half2v sc_lo, half2v sc_hi,
+                                                   const NibbleK& k) {
+  const half2v s_lo = __builtin_shufflevector(sc_lo, sc_lo, 0, 0), c_lo = __builtin_shufflevector(sc_lo, sc_lo, 1, 1);
+  const half2v s_hi = __builtin_shufflevector(sc_hi, sc_hi, 0, 0), c_hi = __builtin_shufflevector(sc_hi, sc_hi, 1, 1);
+  const uint32_t Q8 = Q >> 8, QH8 = QH >> 8;
+  // bytes 0 and 2 (QH) and 1 and 3 (QH8): the low-nibble bit to 4 / 20, the
+  // high-nibble bit to 8 / 24 (shifting the odd bytes down first keeps byte
+  // 3's high-nibble bit inside the word)
+  auto lo_bits = [](uint32_t v) { return (4 - 2 * CH >= 0) ? (v << (4 - 2 * CH)) : (v >> (2 * CH - 4)); };
+  auto hi_bits = [](uint32_t v) { return v << (7 - 2 * CH); };
+  const half2v p0 =
+      __builtin_elementwise_fma(bits_h2((Q & k.lo_mask) | k.lo_magic | (lo_bits(QH) & 0x00100010u)), s_lo, c_lo);
+  const half2v p1 =
+      __builtin_elementwise_fma(bits_h2((Q8 & k.lo_mask) | k.lo_magic | (lo_bits(QH8) & 0x00100010u)), s_lo, c_lo);
+  const half2v p2 =
+      __builtin_elementwise_fma(bits_h2((Q & k.hi_mask) | k.hi_magic | (hi_bits(QH) & 0x01000100u)), s_hi, c_hi);
+  const half2v p3 =
+      __builtin_elementwise_fma(bits_h2((Q8 & k.hi_mask) | k.hi_magic | (hi_bits(QH8) & 0x01000100u)), s_hi, c_hi);
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Q5_1 quant bytes of a block (bytes 8..23, 8-byte aligned).
+__device__ __forceinline__ uint4 load_q51_quants(const uint8_t* blk) {
+  const uint2 a = *reinterpret_cast<const uint2*>(blk + 8), b = *reinterpret_cast<const uint2*>(blk + 16);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// One 32-row output tile's W_down data for a lane, per format.
+template <int FMT, int NP, int NB>
+struct DownTile;
+
+template <int NP, int NB>
+struct DownTile<kDownQ4K, NP, NB> {
+  using type = DownTileData<NP, NB>;
+  template <int OFF>
+  __device__ __forceinline__ static type load(const uint8_t* blk0, int nblk, int npan, int h) {
+    return load_down_tile<NP, NB, OFF>(blk0, nblk, npan, h);
+  }
+};
+
+template <int NP, int NB>
+struct DownTileQ5K {
+  uint4 hdr[NB];   // block headers (Q4_K layout)
+  uint4 qh[NB];    // fifth bits of the lane's half: bytes 16 + 16h .. +16
+  uint4 qs[NP];    // the lane's 16 quant bytes per panel
+};
+
+template <int NP, int NB>
+struct DownTile<kDownQ5K, NP, NB> {
+  using type = DownTileQ5K<NP, NB>;
+  template <int OFF>
+  __device__ __forceinline__ static type load(const uint8_t* blk0, int nblk, int npan, int h) {
+    type d;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      d.hdr[k] = (k < nblk) ? *reinterpret_cast<const uint4*>(blk0 + k * Q5K_BLOCK_BYTES) : make_uint4(0, 0, 0, 0);
+      d.qh[k] = (k < nblk) ? *reinterpret_cast<const uint4*>(blk0 + k * Q5K_BLOCK_BYTES + 16 + 16 * h)
+                           : make_uint4(0, 0, 0, 0);
+    }
+    const uint8_t* qb = blk0 + 48 + 16 * h;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int k = (p + OFF) >> 2, c = (p + OFF) & 3;
+      d.qs[p] = (p < npan) ? *reinterpret_cast<const uint4*>(qb + k * Q5K_BLOCK_BYTES + 32 * c) : make_uint4(0, 0, 0, 0);
+    }
+    return d;
+  }
+};
+
+template <int NP, int NB>
+struct DownTileQ51 {
+  uint2 ha[NP], hb[NP];   // per panel, blocks A and B: (d | m << 16, fifth bits)
+  uint4 qa[NP], qb[NP];   // their 16 quant bytes
+};
+
+template <int NP, int NB>
+struct DownTile<kDownQ51, NP, NB> {
+  using type = DownTileQ51<NP, NB>;
+  // blk0: the row's first block of the chunk's first 256-column group; panel
+  // p's blocks are 2 (p + OFF) and the one after it
+  template <int OFF>
+  __device__ __forceinline__ static type load(const uint8_t* blk0, int nblk, int npan, int h) {
+    (void)nblk;
+    (void)h;
+    type d;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint8_t* a = blk0 + (size_t)(2 * (p + OFF)) * Q5_1_BLOCK_BYTES;
+      if (p < npan) {
+        d.ha[p] = *reinterpret_cast<const uint2*>(a);
+        d.hb[p] = *reinterpret_cast<const uint2*>(a + Q5_1_BLOCK_BYTES);
+        d.qa[p] = load_q51_quants(a);
+        d.qb[p] = load_q51_quants(a + Q5_1_BLOCK_BYTES);
+      } else {
+        d.ha[p] = d.hb[p] = make_uint2(0, 0);
+        d.qa[p] = d.qb[p] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    return d;
+  }
+};
+
 // Phase 2 of the unit: the down projection of the chunk [r0, r1) for
 // all hidden output rows, from the strip in LDS.  The same contraction as
 // fu_phase2 (32x32x16 MFMAs, one decoded W_down operand for both 32-token
@@ -323,7 +438,7 @@ struct OutQuads {
 // strip as the A operand: a lane's sixteen accumulators of a token half are
 // then one output row n and the tokens 8q + 4(l/32) + {0..3}, which the
 // output policy stores.  OFF = (r0 / 64) % 4.
-template <class C, int ICMAX, int OFF, int NTT, class Out>
+template <class C, int ICMAX, int OFF, int NTT, class Out, int FMT = kDownQ4K>
 __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int H, int I, int r0, int r1,
                                             const Out& out, const _Float16* __restrict__ hs,
                                             const _Float16* __restrict__ hsum, const NibbleK& nk,
@@ -331,16 +446,48 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
   constexpr int HS = C::HS, HSS = C::HSS;
   constexpr int NB = C::NBMAX;
   constexpr int NP = ICMAX / 64;
+  constexpr int BB = (FMT == kDownQ5K) ? Q5K_BLOCK_BYTES : BLOCK_BYTES;   // super-block bytes (Q4_K, Q5_K)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int npan = (r1 - r0) / 64;
   const int b0 = r0 >> 8;
   const int nblk = ((r1 - 1) >> 8) - b0 + 1;         // W_down blocks the chunk touches
-  const size_t row_bytes = (size_t)(I / QK) * BLOCK_BYTES;
+  // row l32 of tile 0: from the chunk's first 256-column group (Q5_1: its
+  // first 32-weight block)
+  const size_t row_bytes =
+      (FMT == kDownQ51) ? (size_t)(I / 32) * Q5_1_BLOCK_BYTES : (size_t)(I / QK) * BB;
   const int NT = H / 32;                             // output row tiles
-  const uint8_t* blk_base = wd + (size_t)l32 * row_bytes + (size_t)b0 * BLOCK_BYTES;   // row l32 of tile 0
+  const uint8_t* blk_base = wd + (size_t)l32 * row_bytes +
+                            ((FMT == kDownQ51) ? (size_t)b0 * 8 * Q5_1_BLOCK_BYTES : (size_t)b0 * BB);
+  using TD = typename DownTile<FMT, NP, NB>::type;
 
-  auto down_tile = [&](DownTileData<NP, NB>& dt, int nt, const uint8_t* nxt) {
+  auto zero_acc = [&](float16v (&acc)[C::MTS / 32]) {
+#pragma unroll
+    for (int tt = 0; tt < C::MTS / 32; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tt][e] = 0.0f;
+  };
+  // the strip's 32-row means of block group 2g + h against the lane's
+  // min-correction operand
+  auto min_mfma = [&](float16v (&acc)[C::MTS / 32], int g, const half8& b) {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const half8 a = *reinterpret_cast<const half8*>(hsum + (tt * 32 + l32) * HSS + 16 * g + 8 * h);
+      acc[tt] = mfma32(a, b, acc[tt]);
+    }
+  };
+  auto strip_mfma = [&](float16v (&acc)[C::MTS / 32], int P, int s, const half8& b) {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const half8 a = *reinterpret_cast<const half8*>(hs + (tt * 32 + l32) * HS + P * 64 + (2 * s + h) * 8);
+      acc[tt] = mfma32(a, b, acc[tt]);
+    }
+  };
+  (void)zero_acc;
+  (void)min_mfma;
+  (void)strip_mfma;
+
+  auto down_tile_q4k = [&](DownTileData<NP, NB>& dt, int nt, const uint8_t* nxt) {
     const uint8_t* nq = nxt + 16 + 16 * h;
     float16v acc[C::MTS / 32];
 #pragma unroll
@@ -392,6 +539,119 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
     out.template store<NTT>(acc, nt, l32, h);
   };
 
+  auto down_tile = [&](TD& dt, int nt, const uint8_t* nxt) {
+    if constexpr (FMT == kDownQ4K) {
+      down_tile_q4k(dt, nt, nxt);
+    } else if constexpr (FMT == kDownQ5K) {
+      // Q5_K: Q4_K's panels and headers, plus the fifth bits of the lane's
+      // half (bytes 16 + 16h .. +16 of each block: bit 2c / 2c+1 for chunk c)
+      float16v acc[C::MTS / 32];
+      zero_acc(acc);
+      const uint8_t* nq = nxt + 48 + 16 * h;
+      auto panel = [&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        constexpr int CH = (P + OFF) & 3, K = (P + OFF) >> 2;
+        if (P < NP && P < npan) {
+          const PanelS ps = panel_scales<CH>(dt.hdr[K]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const half8 b = dequant5_dword_sc<CH>(dword_of(dt.qs[P], s), dword_of(dt.qh[K], s), ps.lo, ps.hi, nk);
+            strip_mfma(acc, P, s, b);
+          }
+          dt.qs[P] = *reinterpret_cast<const uint4*>(nq + K * BB + 32 * CH);
+        }
+      };
+      panel(std::integral_constant<int, 0>{});
+      if constexpr (NP > 1) panel(std::integral_constant<int, 1>{});
+      if constexpr (NP > 2) panel(std::integral_constant<int, 2>{});
+#pragma unroll
+      for (int g = 0; g < (NB + 1) / 2; ++g) {
+        if (2 * g < nblk) {
+          uint4 hd = dt.hdr[2 * g];
+          if (2 * g + 1 < NB) {
+            if (h) hd = dt.hdr[2 * g + 1];
+          } else if (h) {
+            hd = make_uint4(0, 0, 0, 0);
+          }
+          min_mfma(acc, g, block_neg_dm32(hd));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (k < nblk) {
+          dt.hdr[k] = *reinterpret_cast<const uint4*>(nxt + k * BB);
+          dt.qh[k] = *reinterpret_cast<const uint4*>(nxt + k * BB + 16 + 16 * h);
+        }
+      out.template store<NTT>(acc, nt, l32, h);
+    } else {
+      // Q5_1: a 64-row panel is two 32-weight blocks A, B; the lane half h
+      // takes nibble h of both, repacked into the Q4_K operand order (A's
+      // weights 16h + 4s + e in the low-nibble slots, B's in the high ones)
+      // with the fifth bits as bits 0 (A) and 1 (B) of each byte, and the
+      // blocks' own d as the two scales
+      float16v acc[C::MTS / 32];
+      zero_acc(acc);
+      auto panel = [&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        if (P < NP && P < npan) {
+          const half2v da = splat_lo(dt.ha[P].x), db = splat_lo(dt.hb[P].x);
+          const half2v slo = da * half2v{(_Float16)1.0f, (_Float16)-1024.0f};
+          const half2v shi = db * half2v{(_Float16)1.0f, (_Float16)-64.0f};
+          const uint32_t fa = dt.ha[P].y >> (16 * h), fb = dt.hb[P].y >> (16 * h);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const uint32_t A = dword_of(dt.qa[P], s), Bq = dword_of(dt.qb[P], s);
+            const uint32_t Q = h ? (((A >> 4) & 0x0F0F0F0Fu) | (Bq & 0xF0F0F0F0u))
+                                 : ((A & 0x0F0F0F0Fu) | ((Bq & 0x0F0F0F0Fu) << 4));
+            // four fifth bits to bit 0 of four bytes: x * 0x204081 puts bit e at 8e
+            const uint32_t QH = ((((fa >> (4 * s)) & 0xFu) * 0x00204081u) & 0x01010101u) |
+                                (((((fb >> (4 * s)) & 0xFu) * 0x00204081u) & 0x01010101u) << 1);
+            strip_mfma(acc, P, s, dequant5_dword_sc<0>(Q, QH, slo, shi, nk));
+          }
+          const uint8_t* nb = nxt + (size_t)(2 * (P + OFF)) * Q5_1_BLOCK_BYTES;
+          dt.qa[P] = load_q51_quants(nb);
+          dt.qb[P] = load_q51_quants(nb + Q5_1_BLOCK_BYTES);
+        }
+      };
+      panel(std::integral_constant<int, 0>{});
+      if constexpr (NP > 1) panel(std::integral_constant<int, 1>{});
+      if constexpr (NP > 2) panel(std::integral_constant<int, 2>{});
+      // min term +m per block: +32 m_j against the 32-row means, block j of
+      // group 2g + h sits in panel 4(2g + h) + j/2 - OFF (A for even j);
+      // blocks outside the chunk's panels meet zero means and take 0
+#pragma unroll
+      for (int g = 0; g < (NB + 1) / 2; ++g) {
+        if (2 * g < nblk) {
+          half8 b;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            _Float16 v[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int P = 4 * (2 * g + hh) + j / 2 - OFF;
+              v[hh] = (_Float16)0.0f;
+              if (P >= 0 && P < NP) {
+                if (P < npan) {
+                  const uint32_t mb = ((j & 1) ? dt.hb[P < NP ? P : 0].x : dt.ha[P < NP ? P : 0].x) >> 16;
+                  v[hh] = (_Float16)32.0f * __builtin_bit_cast(_Float16, (uint16_t)mb);
+                }
+              }
+            }
+            b[sb_slot(j)] = h ? v[1] : v[0];
+          }
+          min_mfma(acc, g, b);
+        }
+      }
+#pragma unroll
+      for (int P = 0; P < NP; ++P)
+        if (P < npan) {
+          const uint8_t* nb = nxt + (size_t)(2 * (P + OFF)) * Q5_1_BLOCK_BYTES;
+          dt.ha[P] = *reinterpret_cast<const uint2*>(nb);
+          dt.hb[P] = *reinterpret_cast<const uint2*>(nb + Q5_1_BLOCK_BYTES);
+        }
+      out.template store<NTT>(acc, nt, l32, h);
+    }
+  };
   // Two rolling tile buffers, so a wave's loads run two tiles ahead: each
   // panel's bytes and each header are refilled with the wave's tile after
   // next as soon as they have been consumed.  Wave w starts on tiles w and
@@ -411,8 +671,8 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
     return __builtin_amdgcn_readfirstlane(v);
   };
   int t0 = wave, t1 = wave + W;
-  DownTileData<NP, NB> d0 = load_down_tile<NP, NB, OFF>(blk_base + (size_t)t0 * tile_step, nblk, npan, h);
-  DownTileData<NP, NB> d1 = load_down_tile<NP, NB, OFF>(blk_base + (size_t)clamp_tile(t1) * tile_step, nblk, npan, h);
+  TD d0 = DownTile<FMT, NP, NB>::template load<OFF>(blk_base + (size_t)t0 * tile_step, nblk, npan, h);
+  TD d1 = DownTile<FMT, NP, NB>::template load<OFF>(blk_base + (size_t)clamp_tile(t1) * tile_step, nblk, npan, h);
   while (t0 < NT) {
     const int t2 = claim();
     down_tile(d0, t0, blk_base + (size_t)clamp_tile(t2) * tile_step);
@@ -445,7 +705,7 @@ struct StagedIO {
 // the zero token M for padding rows); rows = how many of them are real (1..MT,
 // the rest are padding: 16-token groups and 32-token halves wholly past it
 // are skipped); out = the phase-2 output policy.
-template <int ICMAX, class Out, int MT_, int MODE = kUnitFused>
+template <int ICMAX, class Out, int MT_, int MODE = kUnitFused, int FMT = kDownQ4K>
 __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
                                              const uint8_t* __restrict__ wd, int H, int I,
                                              const uint8_t* __restrict__ xtok, const int* __restrict__ tok,
@@ -761,10 +1021,10 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   auto phase2 = [&](auto ntt_tag) {
     constexpr int NTT = decltype(ntt_tag)::value;
     switch (off) {
-      case 0: fu16_phase2<C, ICMAX, 0, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
-      case 1: fu16_phase2<C, ICMAX, 1, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
-      case 2: fu16_phase2<C, ICMAX, 2, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
-      default: fu16_phase2<C, ICMAX, 3, NTT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
+      case 0: fu16_phase2<C, ICMAX, 0, NTT, Out, FMT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
+      case 1: fu16_phase2<C, ICMAX, 1, NTT, Out, FMT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
+      case 2: fu16_phase2<C, ICMAX, 2, NTT, Out, FMT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
+      default: fu16_phase2<C, ICMAX, 3, NTT, Out, FMT>(wd, H, I, r0, r1, out, sm.u.s.hs, sm.u.s.hsum, nk, &sm.p2_next); break;
     }
   };
   if constexpr (MTS > 64) {

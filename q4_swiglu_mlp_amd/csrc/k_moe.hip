@@ -36,6 +36,12 @@ namespace zinc {
 
 namespace {
 
+// Bytes of one [H x I] W_down matrix in the given format.
+__host__ __device__ inline size_t down_matrix_bytes(int fmt, int H, int I) {
+  return (fmt == kDownQ51) ? (size_t)H * (I / 32) * Q5_1_BLOCK_BYTES
+                           : (size_t)H * (I / QK) * ((fmt == kDownQ5K) ? Q5K_BLOCK_BYTES : BLOCK_BYTES);
+}
+
 constexpr int ICMAX_MOE = 192;  // intermediate rows per chunk (three 64-row panels)
 constexpr int MT_MOE = 80;      // routed rows per tile: an expert of up to 80 rows is one tile
 using MoeCfg = Fused16Cfg<ICMAX_MOE, MT_MOE>;
@@ -287,6 +293,7 @@ struct OutSlots {
   }
 };
 
+template <int FMT>
 __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, const uint8_t* __restrict__ wd, int H, int I,
     int M, const uint8_t* __restrict__ xtok, int top_k, const int* __restrict__ n_tiles,
@@ -332,10 +339,10 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
   const int r0 = (int)((long long)chunk * npan / nc) * 64;
   const int r1 = (int)((long long)(chunk + 1) * npan / nc) * 64;
   const size_t gu_bytes = (size_t)I * (H / QK) * BLOCK_BYTES;   // one expert's gate (or up) matrix
-  const size_t d_bytes = (size_t)H * (I / QK) * BLOCK_BYTES;    // one expert's down matrix
+  const size_t d_bytes = down_matrix_bytes(FMT, H, I);          // one expert's down matrix
   const OutSlots out{Q, (size_t)pairs, H, out_scale, chunk, slot_of_row};
-  fused_unit16<ICMAX_MOE>(wg + e * gu_bytes, wu + e * gu_bytes, wd + e * d_bytes, H, I, xtok, tok, rows, r0, r1,
-                          inter_scale, out, sm);
+  fused_unit16<ICMAX_MOE, OutSlots, MT_MOE, kUnitFused, FMT>(wg + e * gu_bytes, wu + e * gu_bytes, wd + e * d_bytes,
+                                                             H, I, xtok, tok, rows, r0, r1, inter_scale, out, sm);
 }
 
 // y[t][n] = fp16(sum_s p[t*k+s] * sum_c Q[c][t*k+s][n]) over the token's valid
@@ -384,7 +391,7 @@ size_t moe_workspace_bytes(int M, int top_k, int n_experts, int hidden, int inte
 
 hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_experts, int hidden, int inter,
                       const void* x, int M, const int32_t* ids, const float* p, int top_k, void* y, int inter_shift,
-                      int out_shift, void* ws, int32_t* dev_error, hipStream_t stream) {
+                      int out_shift, void* ws, int32_t* dev_error, hipStream_t stream, int down_fmt) {
   const int E = n_experts;
   const int n_slots = M * top_k;
   MoePlan pl = carve(ws, M, top_k, E, hidden, inter, nullptr);
@@ -409,12 +416,20 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
                      hidden, M, pl.xtok);
   const int n_chunks = chunks_for(inter), n_chunks_small = chunks_small_for(inter);
   const int max_tiles = max_tiles_for(M, top_k, E);
+  auto fused = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(max_tiles * n_chunks_small), dim3(MoeCfg::THREADS), 0, stream,
+                       static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
+                       static_cast<const uint8_t*>(wd), hidden, inter, M, pl.xtok, top_k, pl.n_tiles, pl.tile_expert,
+                       pl.tile_start, pl.tile_rows, pl.slots, pl.Q, n_slots, ldexpf(1.0f, -inter_shift),
+                       ldexpf(1.0f, inter_shift - out_shift), n_chunks, n_chunks_small);
+  };
   timing_begin(stream);
-  hipLaunchKernelGGL(k_moe_fused16, dim3(max_tiles * n_chunks_small), dim3(MoeCfg::THREADS), 0, stream,
-                     static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
-                     static_cast<const uint8_t*>(wd), hidden, inter, M, pl.xtok, top_k, pl.n_tiles, pl.tile_expert,
-                     pl.tile_start, pl.tile_rows, pl.slots, pl.Q, n_slots, ldexpf(1.0f, -inter_shift),
-                     ldexpf(1.0f, inter_shift - out_shift), n_chunks, n_chunks_small);
+  if (down_fmt == kDownQ5K)
+    fused(k_moe_fused16<kDownQ5K>);
+  else if (down_fmt == kDownQ51)
+    fused(k_moe_fused16<kDownQ51>);
+  else
+    fused(k_moe_fused16<kDownQ4K>);
   timing_end(stream);
   hipLaunchKernelGGL(k_moe_combine, dim3(M), dim3(256), 0, stream, pl.Q, pl.pos, p, top_k, n_chunks, n_chunks_small,
                      n_slots, hidden, static_cast<_Float16*>(y));

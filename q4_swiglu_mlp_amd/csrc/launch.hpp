@@ -14,6 +14,8 @@ void timing_begin(hipStream_t stream);
 void timing_end(hipStream_t stream);
 
 hipError_t launch_q4k_dequant_f32(const void* blocks, int rows, int cols, float* out, hipStream_t stream);
+// fmt 1: Q5_K (cols % 256 == 0), 2: Q5_1 (cols % 32 == 0).
+hipError_t launch_q5_dequant_f32(int fmt, const void* blocks, int rows, int cols, float* out, hipStream_t stream);
 
 // Fused prefill.
 size_t prefill_workspace_bytes(int M, int hidden, int inter);
@@ -47,9 +49,11 @@ hipError_t launch_decode_mfma(const void* wg, const void* wu, const void* wd, in
 
 // Batched-expert MoE.
 size_t moe_workspace_bytes(int M, int top_k, int n_experts, int hidden, int inter);
+// down_fmt: 0 Q4_K, 1 Q5_K, 2 Q5_1 (W_down's block format; gate and up are Q4_K).
 hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_experts, int hidden, int inter,
                       const void* x, int M, const int32_t* ids, const float* p, int top_k, void* y,
-                      int inter_shift, int out_shift, void* ws, int32_t* dev_error, hipStream_t stream);
+                      int inter_shift, int out_shift, void* ws, int32_t* dev_error, hipStream_t stream,
+                      int down_fmt = 0);
 
 // MoE router: per token the top_k largest logits' experts and their softmax
 // weights (k_router.hip).  1 <= top_k <= min(64, n_experts), n_experts <= 1024.

@@ -17,6 +17,11 @@ namespace zinc {
 
 constexpr int QK = 256;          // weights per super-block
 constexpr int BLOCK_BYTES = 144; // bytes per super-block
+// The experts' other down-projection formats: Q5_K super-blocks (the Q4_K
+// header, 32 bytes of fifth bits, 128 quant bytes) and Q5_1 blocks of 32
+// weights (fp16 d and m, 32 fifth bits, 16 quant bytes).
+constexpr int Q5K_BLOCK_BYTES = 176;
+constexpr int Q5_1_BLOCK_BYTES = 24;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));

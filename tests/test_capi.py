@@ -185,3 +185,15 @@ def test_block_workspace_sizes():
     assert Z.lib.zinc_mlp_q4k_decode_block_workspace_size(9, 4096, 11008) == 0
     assert Z.lib.zinc_mlp_q4k_prefill_block_workspace_size(256, 4000, 11008) == 0
     assert block("zinc_mlp_q4k_decode_block", M=9) == -5
+
+
+def test_moe_down_format_errors():
+    f = Z.lib.zinc_moe_experts_fmt
+    call = lambda fmt, **kw: f(A, A, A, fmt, 64, 2048, 768, A, kw.get("M", 512), A, A, 8, A, 0, 0, A, 1 << 30, None,
+                               None)
+    assert call(3) == -5 and call(-1) == -5
+    assert call(1, M=0) == 0 and call(2, M=0) == 0
+    g = Z.lib.zinc_q5_1_dequant_f32
+    assert g(A, 4, 48, A, None) == -2          # Q5_1 rows are whole 32-weight blocks
+    assert g(None, 4, 64, A, None) == -1 and g(A, -1, 64, A, None) == -5 and g(A, 0, 64, A, None) == 0
+    assert Z.lib.zinc_q5k_dequant_f32(A, 4, 288, A, None) == -2
