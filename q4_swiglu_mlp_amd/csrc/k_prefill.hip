@@ -9,11 +9,12 @@
 // I/IC.  Units must also cover the 256 CUs.  Configurations (MT, IC <= ICMAX):
 //   D: MT=64, ICMAX=192 -- the 64-token 16x16x32 unit (fused16.hpp) on an
 //      activation staged once per call (k_stage_x16): 256 units at M=256
-//      (4 tiles x 64 chunks).  The default: fastest measured at every M from
-//      32 to 1024.
-//   A: MT=32, ICMAX=384, B: MT=64, ICMAX=640, C: MT=64, ICMAX=384 -- the
-//      32x32x16 unit of fused_core.hpp, kept as tuning alternatives
-//      (ZINC_PREFILL_CFG).
+//      (4 tiles x 64 chunks).  The default below 384 tokens.
+//   C: MT=64, ICMAX=384 -- the 32x32x16 unit of fused_core.hpp: half the
+//      chunks, so half the partial traffic and one round of units at 512
+//      tokens.  The default from 384 tokens.
+//   A: MT=32, ICMAX=384, B: MT=64, ICMAX=640 -- the same unit, kept as tuning
+//      alternatives (ZINC_PREFILL_CFG).
 #include <cstdlib>
 #include <cstring>
 
@@ -242,7 +243,12 @@ int round_up(int a, int b) { return (a + b - 1) / b * b; }
 Plan make_plan(int M, int H, int I, bool force_d = false) {
   (void)H;
   Plan p;
-  p.cfg = 'D';
+  // D up to 383 tokens, C from 384 (measured on the 4096/11008 layer): past
+  // four 64-token tiles D's 192-row chunks (at least 58 of them) leave a second
+  // round of units mostly empty, while C's 384-row chunks keep 512 tokens in
+  // one round and halve the partial traffic (M=512: 255 vs 285 us, M=1024: 498
+  // vs 550, M=2048: 995 vs 1044; M=384 even; M=4096 even; M=256: 150 vs 126)
+  p.cfg = (M >= 384 && !force_d) ? 'C' : 'D';
   int chunks_wanted = 0;
   // tuning override: ZINC_PREFILL_CFG="<A|B|C|D>[:<chunks>]"
   if (const char* e = std::getenv("ZINC_PREFILL_CFG")) {

@@ -118,6 +118,17 @@ def test_prefill_m256_workload_full():
     assert_parity(y, y_ref, "prefill 4096/11008 M=256")
 
 
+@pytest.mark.parametrize("M", [383, 384, 520])
+def test_prefill_default_plan_switch(M):
+    # the default unit changes at 384 tokens (16x16x32 unit below, 32x32x16
+    # unit with 384-row chunks from there): both sides of the switch
+    H, I = 1024, 2304
+    wg, wu, wd, x = _rand_mlp(40 + M, H, I, M)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
+    a, b = shifts_for(y_ref, h_ref)
+    assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill default plan M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 65, 256])
 def test_prefill_staged_baseline_matches(M):
     # the comparison baseline (intermediate in device memory) computes the
