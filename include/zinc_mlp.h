@@ -64,7 +64,7 @@ typedef enum {
   ZINC_ERR_WORKSPACE = -4,   /* workspace smaller than the matching *_workspace_size() */
   ZINC_ERR_ARG = -5,         /* M < 0, M above the entry point's limit, shift or top_k out of range */
   ZINC_ERR_HIP = -6,         /* a HIP launch or runtime call failed */
-  ZINC_ERR_UNSUPPORTED = -7  /* a size this build does not handle */
+  ZINC_ERR_UNSUPPORTED = -7  /* a size the library does not handle */
 } zinc_status;
 
 /* Text of a status code (static storage; never NULL). */

@@ -82,7 +82,7 @@ const char* zinc_strerror(int status) {
     case ZINC_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_size()";
     case ZINC_ERR_ARG: return "argument out of range (M, shift or top_k)";
     case ZINC_ERR_HIP: return "a HIP launch or runtime call failed";
-    case ZINC_ERR_UNSUPPORTED: return "size not supported by this build";
+    case ZINC_ERR_UNSUPPORTED: return "size not supported by the library";
     default: return "unknown zinc status";
   }
 }
