@@ -118,6 +118,19 @@ def test_prefill_m256_workload_full():
     assert_parity(y, y_ref, "prefill 4096/11008 M=256")
 
 
+@pytest.mark.parametrize("H,I,M", [(16384, 256, 3), (256, 65536, 2)])
+def test_max_sizes(H, I, M):
+    # the library's largest hidden and intermediate widths (the row decode
+    # kernels' longest contraction is hidden = 16384; inter = 65536 sends M = 1
+    # decode to the MFMA kernels' passes)
+    wg, wu, wd, x = _rand_mlp(70 + M, H, I, M)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
+    a, b = shifts_for(y_ref, h_ref)
+    assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill H={H} I={I} M={M}")
+    assert_parity(decode(wg, wu, wd, H, I, x, a, b), y_ref, f"decode H={H} I={I} M={M}")
+    assert_parity(decode(wg, wu, wd, H, I, x[:1], a, b), y_ref[:1], f"decode H={H} I={I} M=1")
+
+
 @pytest.mark.parametrize("M", [383, 384, 520])
 def test_prefill_default_plan_switch(M):
     # the default unit changes at 384 tokens (16x16x32 unit below, 32x32x16
