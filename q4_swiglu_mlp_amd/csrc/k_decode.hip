@@ -115,7 +115,7 @@ __device__ __forceinline__ void chunk_dot(const Chunk& ch, int c, const _Float16
     acc[t] += slo * alo[t] - clo * X2[t * X2S] + shi * ahi[t] - chi * X2[t * X2S + 1];
 }
 
-template <int MM, bool GATEUP, int KQ, bool PF, int NW>
+template <int MM, bool GATEUP, int KQ, int DEPTH, int NW>
 __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint8_t* __restrict__ W0,
                                                             const uint8_t* __restrict__ W1, int K, int N,
                                                             const _Float16* __restrict__ xin, int M,
@@ -210,9 +210,9 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
     xv[u] = make_uint4(0, 0, 0, 0);
     if (g < ngroups && t < M) xv[u] = *reinterpret_cast<const uint4*>(xin + (size_t)t * K + 8 * a);
   }
-  Buf buf, buf2;
+  Buf bufs[DEPTH];
   int j = w0;
-  load_row(j, buf);
+  load_row(j, bufs[0]);
   // the pre-MLP RMS norm (gate/up pass of one token, gamma non-null): every
   // workgroup holds the whole activation, so it sums the squares itself and
   // scales its pieces before they are staged
@@ -267,22 +267,26 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
   }
   __syncthreads();
 
-  if constexpr (PF) {
-    // two rows in flight per wave: the row after next is requested as soon
-    // as a buffer has been consumed, so the arithmetic of one row runs under
-    // the loads of the next
-    load_row(j + nwaves, buf2, j);
-    for (; j < N; j += 2 * nwaves) {
-      compute_row(j, buf);
-      load_row(j + 2 * nwaves, buf, j);
-      if (j + nwaves >= N) break;
-      compute_row(j + nwaves, buf2);
-      load_row(j + 3 * nwaves, buf2, j + nwaves);
+  if constexpr (DEPTH > 1) {
+    // DEPTH rows in flight per wave: a buffer is refilled with the row DEPTH
+    // strides ahead as soon as it has been consumed, so the arithmetic of one
+    // row runs under the loads of the next ones (the ring is unrolled, so
+    // every buffer stays in registers)
+#pragma unroll
+    for (int d = 1; d < DEPTH; ++d) load_row(j + d * nwaves, bufs[d], j);
+    for (; j < N; j += DEPTH * nwaves) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int jd = j + d * nwaves;
+        if (jd >= N) break;
+        compute_row(jd, bufs[d]);
+        load_row(jd + DEPTH * nwaves, bufs[d], jd);
+      }
     }
   } else {
     for (; j < N; j += nwaves) {
-      if (j != w0) load_row(j, buf);
-      compute_row(j, buf);
+      if (j != w0) load_row(j, bufs[0]);
+      compute_row(j, bufs[0]);
     }
   }
 }
@@ -301,35 +305,36 @@ int cu_count() {
 
 // Persistent grid: as many workgroups as are resident at once (occupancy of
 // this instantiation at this LDS size), so no workgroup waits for another to end.
-// Launch shape of the row kernels: two rows in flight per wave or one,
-// waves per workgroup, workgroups per CU (0: as many as are resident).
-// Measured on the 4096/11008 layer sweep: two rows in flight on persistent
-// four-wave workgroups, two per CU for the gate/up pass (about 11 rows per
-// wave) and one for the down pass (4 rows per wave), beat the one-row,
-// full-occupancy shape by ~1.8 us per layer in kernel time.  ZINC_DR_GU /
-// ZINC_DR_DN = "pf,waves,wg_per_cu" override them.
+// Launch shape of the row kernels: rows in flight per wave (1 to 4; eight-wave
+// workgroups take 1 or 2), waves per workgroup, workgroups per CU (0: as many
+// as are resident).  Measured on the 4096/11008 layer sweep: two rows in
+// flight on persistent four-wave workgroups, two per CU for the gate/up pass
+// (about 11 rows per wave) and one for the down pass (4 rows per wave), beat
+// the one-row, full-occupancy shape by ~1.8 us per layer in kernel time.
+// ZINC_DR_GU / ZINC_DR_DN = "depth,waves,wg_per_cu" override them.
 struct DrCfg {
-  bool pf;
-  int waves, wg_per_cu;
+  int depth, waves, wg_per_cu;
 };
 
 inline DrCfg dr_cfg(bool gateup) {
-  DrCfg c = gateup ? DrCfg{true, 4, 2} : DrCfg{true, 4, 1};
+  DrCfg c = gateup ? DrCfg{2, 4, 2} : DrCfg{2, 4, 1};
   if (const char* e = std::getenv(gateup ? "ZINC_DR_GU" : "ZINC_DR_DN")) {
-    int pf = 0, w = 8, g = 0;
-    if (std::sscanf(e, "%d,%d,%d", &pf, &w, &g) == 3 && (w == 4 || w == 8) && g >= 0) c = DrCfg{pf != 0, w, g};
+    int d = 0, w = 0, g = -1;
+    const bool ok = std::sscanf(e, "%d,%d,%d", &d, &w, &g) == 3 && g >= 0 &&
+                    ((w == 4 && d >= 1 && d <= 4) || (w == 8 && d >= 1 && d <= 2));
+    if (ok) c = DrCfg{d, w, g};
   }
   return c;
 }
 
-template <int MM, bool GATEUP, int KQ, bool PF, int NW>
+template <int MM, bool GATEUP, int KQ, int DEPTH, int NW>
 hipError_t launch_rows_cfg(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
                            float scale, const _Float16* res, float res_scale, const _Float16* gamma, float eps,
                            int wg_per_cu, hipStream_t stream) {
   const size_t smem = (size_t)MM * (K + 8) * 2 + (size_t)MM * 2 * (4 * (K / QK)) * 4;
   static size_t attr_set = 0;   // largest dynamic LDS size allowed so far
   if (smem > attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_rows<MM, GATEUP, KQ, PF, NW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_rows<MM, GATEUP, KQ, DEPTH, NW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = smem;
@@ -338,7 +343,7 @@ hipError_t launch_rows_cfg(const void* W0, const void* W1, int K, int N, const _
   static int occ = 0;
   if (occ == 0 || occ_smem != smem) {
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_rows<MM, GATEUP, KQ, PF, NW>,
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_rows<MM, GATEUP, KQ, DEPTH, NW>,
                                                                 DrShape<NW>::THREADS, smem);
     if (e != hipSuccess) return e;
     occ = per_cu < 1 ? 1 : per_cu;
@@ -346,7 +351,7 @@ hipError_t launch_rows_cfg(const void* W0, const void* W1, int K, int N, const _
   }
   const int per_cu = (wg_per_cu > 0 && wg_per_cu < occ) ? wg_per_cu : occ;
   const int grid = std::max(1, std::min(cu_count() * per_cu, (N + NW - 1) / NW));
-  hipLaunchKernelGGL((k_decode_rows<MM, GATEUP, KQ, PF, NW>), dim3(grid), dim3(DrShape<NW>::THREADS), smem, stream,
+  hipLaunchKernelGGL((k_decode_rows<MM, GATEUP, KQ, DEPTH, NW>), dim3(grid), dim3(DrShape<NW>::THREADS), smem, stream,
                      static_cast<const uint8_t*>(W0), static_cast<const uint8_t*>(W1), K, N, x, M, out, scale, res,
                      res_scale, gamma, eps);
   return hipGetLastError();
@@ -357,17 +362,20 @@ hipError_t launch_rows(const void* W0, const void* W1, int K, int N, const _Floa
                        float scale, const _Float16* res, float res_scale, const _Float16* gamma, float eps,
                        hipStream_t stream) {
   const DrCfg c = dr_cfg(GATEUP);
-  if (c.pf && c.waves == 4)
-    return launch_rows_cfg<MM, GATEUP, KQ, true, 4>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu,
-                                                    stream);
-  if (c.pf)
-    return launch_rows_cfg<MM, GATEUP, KQ, true, 8>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu,
-                                                    stream);
-  if (c.waves == 4)
-    return launch_rows_cfg<MM, GATEUP, KQ, false, 4>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu,
-                                                     stream);
-  return launch_rows_cfg<MM, GATEUP, KQ, false, 8>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu,
-                                                   stream);
+#define ZINC_DR_LAUNCH(D, W)                                                                                         \
+  return launch_rows_cfg<MM, GATEUP, KQ, D, W>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu, \
+                                               stream)
+  if (c.waves == 8) {
+    if (c.depth == 1) ZINC_DR_LAUNCH(1, 8);
+    ZINC_DR_LAUNCH(2, 8);
+  }
+  switch (c.depth) {
+    case 1: ZINC_DR_LAUNCH(1, 4);
+    case 3: ZINC_DR_LAUNCH(3, 4);
+    case 4: ZINC_DR_LAUNCH(4, 4);
+    default: ZINC_DR_LAUNCH(2, 4);
+  }
+#undef ZINC_DR_LAUNCH
 }
 
 template <int MM, bool GATEUP>

@@ -247,10 +247,10 @@ def test_decode_tiny_workload(M):
     assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift), y_ref, f"decode tiny M={M}")
 
 
-@pytest.mark.parametrize("shape", ["0,8,0", "1,8,1", "0,4,3"])
+@pytest.mark.parametrize("shape", ["1,8,0", "2,8,1", "1,4,3", "3,4,1", "4,4,1", "4,4,2"])
 def test_decode_m1_launch_shapes(shape, monkeypatch):
-    # the M = 1 row kernels under the other launch shapes (rows in flight,
-    # waves per workgroup, workgroups per CU) that ZINC_DR_GU / ZINC_DR_DN select
+    # the M = 1 row kernels under the other launch shapes (rows in flight per
+    # wave, waves per workgroup, workgroups per CU) that ZINC_DR_GU / ZINC_DR_DN select
     monkeypatch.setenv("ZINC_DR_GU", shape)
     monkeypatch.setenv("ZINC_DR_DN", shape)
     H, I = 1024, 2816
