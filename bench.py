@@ -13,7 +13,8 @@ library's timing hook), the HBM traffic from the committed rocprofv3 counter
 summary when it matches the current kernel source, and the CPU oracle timed
 on the host.  Secondary lines (decode M=1/M=4 over 32 independent layers,
 the 64-expert MoE over two rotated expert sets, the router, the MLP block
-with its RMS norm and residual) ride in "secondary".  ``--only staged`` instead times the fused prefill against its
+with its RMS norm and residual, the 2048-token prefill over 32 layers) ride in
+"secondary".  ``--only staged`` instead times the fused prefill against its
 staged baseline (the intermediate in device memory) at M=256 and M=2048.
 
 usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-secondary] [--no-cpu-baseline]
@@ -192,8 +193,39 @@ def secondary(args, torch):
         out += moe_lines(args, torch, np, Z, S, dev, t)
     if args.only in (None, "block"):
         out += block_lines(args, torch, np, Z, S, dev, t)
+    if args.only in (None, "m2048"):
+        out += m2048_lines(args, torch, np, Z, S, dev, t)
     if args.only == "staged":   # its own run: its fused calls at M=2048 would mix into the headline kernel's trace
         out += staged_lines(args, torch, np, Z, S, dev, t)
+    return out
+
+
+def m2048_lines(args, torch, np, Z, S, dev, t):
+    """The large prefill: 2048 tokens through 32 independent 4096/11008 layers
+    (seed 2, x sd 0.5), each layer one call; whole-call time per layer."""
+    w = S.WORKLOADS["prefill_m2048"]
+    layers = [tuple(t(a) for a in S.layer_weights(w.seed, l, w.hidden, w.inter)) for l in range(w.layers)]
+    gx = t(S.workload_x(w))
+    y = torch.empty((w.M, w.hidden), dtype=torch.float16, device=dev)
+    ws = torch.empty(Z.prefill_workspace_size(w.M, w.hidden, w.inter), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        lg, lu, ld = layers[i % w.layers]
+        Z.zinc_mlp_q4k_prefill(lg, lu, ld, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
+
+    steps = 3 * w.layers
+    wall, _ = time_calls(call, steps, w.layers, torch)
+    per = wall / steps
+    flops = 6.0 * w.M * w.hidden * w.inter
+    out = [{
+        "workload": "prefill 4096/11008 M=2048, 32-layer sweep (seed 2)",
+        "tokens_per_s": round(w.M / per, 1),
+        "us_per_layer": round(per * 1e6, 2),
+        "whole_call_tflops": round(flops / per / 1e12, 2),
+        "whole_call_mfma_frac": round(flops / per / 1e12 / PEAK_F16_TFLOPS, 4),
+    }]
+    log(f"[bench] {out[-1]}")
+    del layers
     return out
 
 
@@ -427,7 +459,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "moe", "block", "staged"], default=None,
+    ap.add_argument("--only", choices=["decode", "moe", "block", "m2048", "staged"], default=None,
                     help="development runs: skip the headline and the CPU baseline, run one secondary part")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3x), the reference kernel that "
