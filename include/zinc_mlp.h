@@ -113,7 +113,9 @@ int zinc_q5_1_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float*
  * last one" and "What it is worth").  `workspace` holds the activation
  * rearranged into the MFMA operand order (written first, by a small kernel)
  * and the down-projection partial sums of the intermediate chunks, stored as
- * fp16 at the output scale and summed in fp32 by a reduce kernel.
+ * fp16 at the output scale and summed in fp32 by a reduce kernel.  The
+ * workspace size is non-decreasing in M (here and for the _staged and _block
+ * variants): a workspace sized for M serves every call with fewer tokens.
  * Limits: hidden, inter multiples of 256, hidden <= 16384, inter <= 65536,
  * M <= 2^20 and (M + 1) * (hidden / 256) * 544 < 2^32 (else ZINC_ERR_ARG, and
  * the workspace size query returns 0).

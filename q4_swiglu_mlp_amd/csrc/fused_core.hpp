@@ -284,21 +284,6 @@ __device__ __forceinline__ DownTileData<NP, NB> load_down_tile(const uint8_t* __
   return d;
 }
 
-// Dense-prefill output: fp16 partial sums P[chunk][n][t] (t < Mpad), already
-// multiplied by the output scale 2^(inter_shift - out_shift), so each is of
-// the order of y itself (fp16-safe by the choice of out_shift).
-struct OutPartial {
-  _Float16* P;
-  int Mpad;
-  int H;
-  float scale;
-  __device__ __forceinline__ void put(int chunk, int n, int row_in_unit, int tok, float w, float v) const {
-    (void)tok;
-    (void)w;
-    P[((size_t)chunk * H + n) * Mpad + row_in_unit] = (_Float16)(v * scale);
-  }
-};
-
 __device__ __forceinline__ uint32_t dword_of(const uint4& q, int s) {
   return (s == 0) ? q.x : (s == 1) ? q.y : (s == 2) ? q.z : q.w;
 }
@@ -320,13 +305,10 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
   const int nblk = ((r1 - 1) >> 8) - b0 + 1;         // W_down blocks the chunk touches
   const size_t row_bytes = (size_t)(I / QK) * BLOCK_BYTES;
   const int NT = H / 32;                             // output row tiles
-  int tokc[TT];
-  float wc[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    tokc[tt] = tok[tt * 32 + l32];
-    wc[tt] = wrow[tt * 32 + l32];
-  }
+  (void)tok;
+  (void)wrow;
+  (void)chunk;
+  (void)row0;
   const uint8_t* blk_base = wd + (size_t)l32 * row_bytes + (size_t)b0 * BLOCK_BYTES;   // row l32 of tile 0
 
   auto down_tile = [&](DownTileData<NP, NB>& dt, int nt, const uint8_t* nxt) {
@@ -349,7 +331,7 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) {
             const half8 bf = *reinterpret_cast<const half8*>(hs + (tt * 32 + l32) * HS + p * 64 + (2 * s + h) * 8);
-            acc[tt] = mfma32(a, bf, acc[tt]);
+            acc[tt] = mfma32(bf, a, acc[tt]);   // strip as A: accumulator rows are tokens
           }
         }
         // panel used up: refill it with the next tile's bytes
@@ -372,21 +354,17 @@ __device__ __forceinline__ void fu_phase2(const uint8_t* __restrict__ wd, int H,
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
           const half8 bf = *reinterpret_cast<const half8*>(hsum + (tt * 32 + l32) * HSS + 16 * g + 8 * h);
-          acc[tt] = mfma32(a, bf, acc[tt]);
+          acc[tt] = mfma32(bf, a, acc[tt]);
         }
       }
     }
 #pragma unroll
     for (int k = 0; k < NB; ++k)
       if (k < nblk) dt.hdr[k] = *reinterpret_cast<const uint4*>(nxt + k * BLOCK_BYTES);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = nt * 32 + mfma32_row(r, lane);
-        out.put(chunk, n, row0 + tt * 32 + l32, tokc[tt], wc[tt], acc[tt][r]);
-      }
-    }
+    // a lane's sixteen accumulators of token tile tt: output row n = 32 nt +
+    // (lane % 32), tokens 32 tt + 8 q + 4 (lane / 32) + {0..3} -- whole token
+    // quads, which the output policy stores
+    out.template store<TT>(acc, nt, l32, h);
   };
 
   // one rolling tile buffer: each panel's bytes and each header are refilled

@@ -8,11 +8,13 @@
 // partial output is MT x hidden fp16, so the reduction traffic grows with
 // I/IC.  Units must also cover the 256 CUs.  Configurations (MT, IC <= ICMAX):
 //   D: MT=64, ICMAX=192 -- the 64-token 16x16x32 unit (fused16.hpp) on an
-//      activation staged once per call (k_stage_x16): 256 units at M=256
-//      (4 tiles x 64 chunks).  The default below 384 tokens.
+//      activation staged once per call (k_stage_x16): 232 units at M=256
+//      (4 tiles x 58 chunks).  The default up to 4 token tiles (256 tokens).
 //   C: MT=64, ICMAX=384 -- the 32x32x16 unit of fused_core.hpp: half the
 //      chunks, so half the partial traffic and one round of units at 512
-//      tokens.  The default from 384 tokens.
+//      tokens.  The default past 4 token tiles.
+// Every configuration stores its partials in token quads, P[chunk][t/4][n][t%4],
+// which k_reduce_quads sums.
 //   A: MT=32, ICMAX=384, B: MT=64, ICMAX=640 -- the same unit, kept as tuning
 //      alternatives (ZINC_PREFILL_CFG).
 #include <cstdlib>
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(64 * FuWaves<TT>::value) void k_prefill_fused(const
     wrow[threadIdx.x] = 1.0f;
   }
   __syncthreads();
-  OutPartial out{P, Mpad, H, out_scale};
+  const OutQuads out{P, Mpad, H, out_scale, chunk, tile * C::MT};
   fused_unit<TT, RTW, ICMAX>(wg, wu, wd, H, I, x, tok, wrow, chunk, r0, r1, tile * C::MT, inter_scale, out, sm);
 }
 
@@ -126,63 +128,6 @@ __global__ __launch_bounds__(256) void k_swiglu_f16(const _Float16* __restrict__
   *reinterpret_cast<half8*>(h + 8 * i) = hv;
 }
 
-// y[t][n] = fp16(sum_c P[c][n][t]) through a 64x64 LDS transpose.  Thread
-// (tx, ty) sums tokens 8tx..8tx+7 (one 16-byte load) of hidden rows ty and
-// ty + 32 over all chunks in fp32, four chunks' loads in flight at a time.
-// With RES, y = fp16(sum + res * res_scale): res is the [M x H] residual,
-// which may be y itself (each element is read and then written by one thread).
-template <bool RES>
-__global__ __launch_bounds__(256) void k_reduce_partials(const _Float16* __restrict__ P, int S, int H, int Mpad,
-                                                        _Float16* y, int M, const _Float16* res, float res_scale) {
-  __shared__ float tile[64][65];
-  const int n0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
-  float acc[2][8];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
-  const size_t plane = (size_t)H * Mpad;
-  const _Float16* base = P + (size_t)(n0 + ty) * Mpad + t0 + 8 * tx;
-  auto add = [&](int i, const uint4& v) {
-    const half8 h = __builtin_bit_cast(half8, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] += (float)h[e];
-  };
-  int c = 0;
-  for (; c + 4 <= S; c += 4) {
-    uint4 v[4][2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        v[u][i] = *reinterpret_cast<const uint4*>(base + (c + u) * plane + (size_t)32 * i * Mpad);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) add(i, v[u][i]);
-  }
-  for (; c < S; ++c) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) add(i, *reinterpret_cast<const uint4*>(base + c * plane + (size_t)32 * i * Mpad));
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[ty + 32 * i][8 * tx + e] = acc[i][e];
-  __syncthreads();
-  const int wx = threadIdx.x & 63, wy = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = t0 + wy + 4 * i;
-    if (t < M) {
-      float v = tile[wx][wy + 4 * i];
-      if constexpr (RES) v += (float)res[(size_t)t * H + n0 + wx] * res_scale;
-      y[(size_t)t * H + n0 + wx] = (_Float16)v;
-    }
-  }
-}
-
 // y[t][n] = fp16(sum_c P[c][t / 4][n][t % 4]) for the token-quad partial
 // layout of the 64-token unit.  Thread (np, tq) sums one 16-byte piece (rows
 // 2np, 2np+1 x tokens 4tq..4tq+3) over all chunks in fp32, four chunks' loads
@@ -238,33 +183,52 @@ struct Plan {
 
 int round_up(int a, int b) { return (a + b - 1) / b * b; }
 
+// Units run one per CU, and the unit order below pins chunk c to XCD c % 8,
+// whose 32 CUs run that XCD's units: a plan takes the fewest rounds k for
+// which chunks = 8 * floor(32 k / tiles) reaches the unit's minimum, so every
+// XCD runs at most k rounds of 32 units, and the units are as small as k
+// rounds allow; of the chunk counts that give the same largest unit, the
+// smallest (fewest partials).  D (192-row chunks, at least 58) up to four 64-token tiles,
+// where one round fits; C (384-row chunks, at least 29) beyond.
+// Measured on the 4096/11008 layer (whole calls; "D:86" = D with 86 chunks):
+// M=192 D:86 159 us (some XCDs 33 units: two rounds); M=256 D:64 128; M=320
+// D:58 202, C:43 155; M=384 C:42 310 (36 units on some XCDs), C:29 222;
+// M=2048 C:29 1021, D:58 1078.
 // force_d: configuration D whatever the override names (its chunk count
 // still applies); the staged baseline runs that unit.
-Plan make_plan(int M, int H, int I, bool force_d = false) {
+// Tuning override: ZINC_PREFILL_CFG="<A|B|C|D>[:<chunks>]".
+struct PlanOverride {
+  char cfg = 0;
+  int chunks = 0;
+};
+
+PlanOverride read_override() {
+  PlanOverride o;
+  if (const char* e = std::getenv("ZINC_PREFILL_CFG")) {
+    if (e[0] >= 'A' && e[0] <= 'D') o.cfg = e[0];
+    if (e[0] && e[1] == ':') o.chunks = std::atoi(e + 2);
+  }
+  return o;
+}
+
+Plan make_plan(int M, int H, int I, bool force_d, const PlanOverride& o) {
   (void)H;
   Plan p;
-  // D up to 383 tokens, C from 384 (measured on the 4096/11008 layer): past
-  // four 64-token tiles D's 192-row chunks (at least 58 of them) leave a second
-  // round of units mostly empty, while C's 384-row chunks keep 512 tokens in
-  // one round and halve the partial traffic (M=512: 255 vs 285 us, M=1024: 498
-  // vs 550, M=2048: 995 vs 1044; M=384 even; M=4096 even; M=256: 150 vs 126)
-  p.cfg = (M >= 384 && !force_d) ? 'C' : 'D';
-  int chunks_wanted = 0;
-  // tuning override: ZINC_PREFILL_CFG="<A|B|C|D>[:<chunks>]"
-  if (const char* e = std::getenv("ZINC_PREFILL_CFG")) {
-    if (e[0] >= 'A' && e[0] <= 'D' && !force_d) p.cfg = e[0];
-    if (e[0] && e[1] == ':') chunks_wanted = std::atoi(e + 2);
-  }
+  const int tiles64 = (M + 63) / 64;
+  p.cfg = (tiles64 <= 4 || force_d) ? 'D' : 'C';
+  if (o.cfg && !force_d) p.cfg = o.cfg;
+  const int chunks_wanted = o.chunks;
   p.MT = (p.cfg == 'A') ? 32 : 64;
   p.ICMAX = (p.cfg == 'B') ? 640 : (p.cfg == 'D') ? 192 : 384;
   const int npan = I / 64;
   const int min_chunks = (npan + p.ICMAX / 64 - 1) / (p.ICMAX / 64);
   p.n_tiles = (M + p.MT - 1) / p.MT;
   int chunks = min_chunks;
-  if (p.cfg == 'A' || p.cfg == 'D') {
-    // enough units to cover the 256 CUs, up to one 64-row panel per chunk
-    const int want = (256 + p.n_tiles - 1) / p.n_tiles;
-    chunks = want > chunks ? want : chunks;
+  if (p.cfg != 'B') {
+    const int k = (((min_chunks + 7) / 8) * p.n_tiles + 31) / 32;   // fewest rounds
+    const int most = 8 * ((32 * k) / p.n_tiles);    // chunks that fit k rounds
+    const int per = (npan + most - 1) / most;        // panels of the largest unit
+    chunks = (npan + per - 1) / per;                 // the fewest chunks with units that size
   }
   if (chunks_wanted > 0) chunks = chunks_wanted;
   if (chunks < min_chunks) chunks = min_chunks;
@@ -301,25 +265,46 @@ size_t staged_x_bytes(const Plan& p, int H) {
   return (p.cfg == 'D') ? x16_staged_bytes(p.n_tiles * p.MT, H) : 0;
 }
 
+// A plan's own need is not monotone in M (adding a token tile can lower the
+// chunk count), so a size query returns the largest need of any token count up
+// to M: a workspace sized for M then serves every smaller call too.  Plans
+// change only at 32-token steps.
+template <class Need>
+size_t most_over_smaller_m(int M, Need need) {
+  const int top = M > 0 ? M : 1;
+  size_t most = need(top);
+  for (int m = 32; m < top; m += 32) {
+    const size_t b = need(m);
+    if (b > most) most = b;
+  }
+  return most;
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int M, int hidden, int inter) {
-  const Plan p = make_plan(M > 0 ? M : 1, hidden, inter);
-  return partial_bytes(p, hidden) + staged_x_bytes(p, hidden);
+  const PlanOverride o = read_override();
+  return most_over_smaller_m(M, [&](int m) {
+    const Plan p = make_plan(m, hidden, inter, false, o);
+    return partial_bytes(p, hidden) + staged_x_bytes(p, hidden);
+  });
 }
 
 // Staged baseline workspace: the fused path's (configuration D) plus fp16
 // G, U and the intermediate, [M x inter] each.
 size_t prefill_staged_workspace_bytes(int M, int hidden, int inter) {
-  const Plan p = make_plan(M > 0 ? M : 1, hidden, inter, true);
-  const size_t mi = (((size_t)(M > 0 ? M : 1) * inter * sizeof(_Float16)) + 255) & ~(size_t)255;
-  return partial_bytes(p, hidden) + (x16_staged_bytes(p.n_tiles * p.MT, hidden) + 255) / 256 * 256 + 3 * mi;
+  const PlanOverride o = read_override();
+  return most_over_smaller_m(M, [&](int m) {
+    const Plan p = make_plan(m, hidden, inter, true, o);
+    const size_t mi = (((size_t)m * inter * sizeof(_Float16)) + 255) & ~(size_t)255;
+    return partial_bytes(p, hidden) + (x16_staged_bytes(p.n_tiles * p.MT, hidden) + 255) / 256 * 256 + 3 * mi;
+  });
 }
 
 hipError_t launch_prefill_staged(const void* wg, const void* wu, const void* wd, int hidden, int inter,
                                  const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
                                  hipStream_t stream) {
-  const Plan p = make_plan(M, hidden, inter, true);
+  const Plan p = make_plan(M, hidden, inter, true, read_override());
   _Float16* P = static_cast<_Float16*>(ws);
   uint8_t* xg = static_cast<uint8_t*>(ws) + partial_bytes(p, hidden);
   const size_t mi = (((size_t)M * inter * sizeof(_Float16)) + 255) & ~(size_t)255;
@@ -350,7 +335,7 @@ hipError_t launch_prefill_staged(const void* wg, const void* wu, const void* wd,
 hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
                           void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream,
                           float mlp_scale, const void* res) {
-  const Plan p = make_plan(M, hidden, inter);
+  const Plan p = make_plan(M, hidden, inter, false, read_override());
   _Float16* P = static_cast<_Float16*>(ws);
   const float inter_scale = ldexpf(1.0f, -inter_shift);
   const float out_scale = ldexpf(1.0f, inter_shift - out_shift) * mlp_scale;
@@ -369,18 +354,13 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
     default: launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
   }
   timing_end(stream);
-  const dim3 rq(hidden / 64, p.Mpad / 32), rp(hidden / 64, p.Mpad / 64);
-  if (p.cfg == 'D' && rh)
+  // every configuration stores its partials in token quads
+  const dim3 rq(hidden / 64, p.Mpad / 32);
+  if (rh)
     hipLaunchKernelGGL(k_reduce_quads<true>, rq, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
                        res_scale);
-  else if (p.cfg == 'D')
-    hipLaunchKernelGGL(k_reduce_quads<false>, rq, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
-                       res_scale);
-  else if (rh)
-    hipLaunchKernelGGL(k_reduce_partials<true>, rp, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
-                       res_scale);
   else
-    hipLaunchKernelGGL(k_reduce_partials<false>, rp, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
+    hipLaunchKernelGGL(k_reduce_quads<false>, rq, dim3(256), 0, stream, P, p.n_chunks, hidden, p.Mpad, yh, M, rh,
                        res_scale);
   return hipGetLastError();
 }

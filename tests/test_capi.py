@@ -94,12 +94,23 @@ def test_decode_token_limit():
 
 def test_workspace_sizes():
     assert Z.prefill_workspace_size(256, 4096, 11008) >= 256 * 4096 * 4
-    assert Z.prefill_workspace_size(257, 4096, 11008) > Z.prefill_workspace_size(256, 4096, 11008)
+    assert Z.prefill_workspace_size(257, 4096, 11008) >= Z.prefill_workspace_size(256, 4096, 11008)
     assert Z.prefill_workspace_size(256, 4000, 11008) == 0
     # the staged baseline adds G, U and the intermediate, M x inter fp16 each
     assert (Z.prefill_staged_workspace_size(256, 4096, 11008)
             >= Z.prefill_workspace_size(256, 4096, 11008) + 3 * 256 * 11008 * 2)
     assert Z.prefill_staged_workspace_size(256, 4000, 11008) == 0
+
+
+@pytest.mark.parametrize("size", ["prefill_workspace_size", "prefill_staged_workspace_size"])
+def test_prefill_workspace_size_monotone(size):
+    # a workspace sized for M serves every smaller M, although the chunk count
+    # of the plan drops as token tiles are added (e.g. 256 -> 257 tokens)
+    f = getattr(Z, size)
+    ms = sorted(set(list(range(1, 1200, 13)) + [64 * t + d for t in range(1, 40) for d in (-1, 0, 1)] + [2048, 4096]))
+    sizes = [f(m, 4096, 11008) for m in ms]
+    assert all(s > 0 for s in sizes)
+    assert all(b >= a for a, b in zip(sizes, sizes[1:]))
     assert Z.decode_workspace_size(4, 4096, 11008) >= 4 * 11008 * 2
     assert Z.moe_workspace_size(512, 8, 64, 2048, 768) >= 512 * 2048 * 4 + 512 * 8 * 4
     assert Z.moe_workspace_size(512, 65, 64, 2048, 768) == 0

@@ -131,15 +131,34 @@ def test_max_sizes(H, I, M):
     assert_parity(decode(wg, wu, wd, H, I, x[:1], a, b), y_ref[:1], f"decode H={H} I={I} M=1")
 
 
-@pytest.mark.parametrize("M", [383, 384, 520])
+@pytest.mark.parametrize("M", [150, 256, 257, 320, 383, 520])
 def test_prefill_default_plan_switch(M):
-    # the default unit changes at 384 tokens (16x16x32 unit below, 32x32x16
-    # unit with 384-row chunks from there): both sides of the switch
+    # the default unit changes past four 64-token tiles (16x16x32 unit up to
+    # 256 tokens, 32x32x16 unit with 384-row chunks after), and the chunk count
+    # with the number of tiles: both sides of each change
     H, I = 1024, 2304
     wg, wu, wd, x = _rand_mlp(40 + M, H, I, M)
     y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
     a, b = shifts_for(y_ref, h_ref)
     assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill default plan M={M}")
+
+
+def test_prefill_workspace_sized_for_larger_m():
+    # one workspace sized for 520 tokens serves calls with fewer tokens, on
+    # both sides of the unit switch, with the same result as a workspace of
+    # each call's own size (the plan, hence the arithmetic, is the same)
+    H, I = 1024, 2304
+    M_max = 520
+    wg, wu, wd, x = _rand_mlp(77, H, I, M_max)
+    a, b = shifts_for(*O.mlp(x, wg, wu, wd, H, I))
+    gw, uw, dw = dev(wg), dev(wu), dev(wd)
+    ws = torch.empty(Z.prefill_workspace_size(M_max, H, I), dtype=torch.uint8, device="cuda")
+    for M in (520, 257, 256, 130, 1):
+        xm = dev(x[:M])
+        y_shared = Z.zinc_mlp_q4k_prefill(gw, uw, dw, H, I, xm, a, b, workspace=ws)
+        y_own = Z.zinc_mlp_q4k_prefill(gw, uw, dw, H, I, xm, a, b)
+        torch.cuda.synchronize()
+        assert torch.equal(y_shared, y_own), f"shared workspace M={M}"
 
 
 @pytest.mark.parametrize("M", [1, 65, 256])
