@@ -16,8 +16,11 @@
 // window of the matrix): no tiles, no barriers inside the loop, no cross-wave
 // sums.  The workgroups are persistent (a fixed number per CU, see DrCfg) and
 // stage the contraction vector once in LDS, under the latency of their first
-// rows' loads; each wave keeps two rows in flight, computing one while the
-// next one's loads are outstanding.
+// rows' loads; each wave keeps one or more rows in flight (a template depth),
+// computing one while the next one's loads are outstanding.  A lane takes the
+// same chunks of every row, so for one token and up to three chunks per lane
+// it copies its activation slices from LDS into registers once, and the loop
+// reads only weights from memory.
 //
 // Lanes.  A row's super-blocks split into 64-weight chunks; lane l takes chunks
 // q = l, l+64, ... of the row, i.e. the block's 16-byte header and its 32 quant
@@ -115,6 +118,37 @@ __device__ __forceinline__ void chunk_dot(const Chunk& ch, int c, const _Float16
     acc[t] += slo * alo[t] - clo * X2[t * X2S] + shi * ahi[t] - chi * X2[t * X2S + 1];
 }
 
+// One token's chunk contribution as chunk_dot<1>, with the chunk's 64
+// activations in registers (pair order, eight halves per uint4) and the fp32
+// sums of its two sub-blocks.
+__device__ __forceinline__ float chunk_dot_reg(const Chunk& ch, int c, const uint4 (&xr)[8], float xlo, float xhi,
+                                               const NibbleK& nk) {
+  float alo = 0.0f, ahi = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 qq = h ? ch.q1 : ch.q0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t Q = (k == 0) ? qq.x : (k == 1) ? qq.y : (k == 2) ? qq.z : qq.w;
+      const uint32_t Q8 = Q >> 8;
+      const int e = 16 * h + 4 * k;
+      const uint4 vl = xr[e >> 3], vh = xr[(32 + e) >> 3];
+      const uint32_t l0 = (e & 4) ? vl.z : vl.x, l1 = (e & 4) ? vl.w : vl.y;
+      const uint32_t h0 = (e & 4) ? vh.z : vh.x, h1 = (e & 4) ? vh.w : vh.y;
+      alo = __builtin_amdgcn_fdot2(bits_h2((Q & nk.lo_mask) | nk.lo_magic), bits_h2(l0), alo, false);
+      alo = __builtin_amdgcn_fdot2(bits_h2((Q8 & nk.lo_mask) | nk.lo_magic), bits_h2(l1), alo, false);
+      ahi = __builtin_amdgcn_fdot2(bits_h2((Q & nk.hi_mask) | nk.hi_magic), bits_h2(h0), ahi, false);
+      ahi = __builtin_amdgcn_fdot2(bits_h2((Q8 & nk.hi_mask) | nk.hi_magic), bits_h2(h1), ahi, false);
+    }
+  }
+  const float d = half_bits_to_float(ch.hdr.x & 0xFFFFu), dmin = half_bits_to_float(ch.hdr.x >> 16);
+  const SixBit sb = unpack_sixbit(ch.hdr.y, ch.hdr.z, ch.hdr.w);
+  const float slo = d * (float)sixbit_sc(sb, 2 * c), shi = d * (float)sixbit_sc(sb, 2 * c + 1);
+  const float clo = 1024.0f * slo + dmin * (float)sixbit_m(sb, 2 * c);
+  const float chi = 64.0f * shi + dmin * (float)sixbit_m(sb, 2 * c + 1);
+  return slo * alo - clo * xlo + shi * ahi - chi * xhi;
+}
+
 template <int MM, bool GATEUP, int KQ, int DEPTH, int NW>
 __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint8_t* __restrict__ W0,
                                                             const uint8_t* __restrict__ W1, int K, int N,
@@ -149,6 +183,12 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
     boff[k] = (size_t)(qc >> 2) * BLOCK_BYTES;
     qoff[k] = boff[k] + 16 + 32 * (qc & 3);
   }
+  // one token and at most three chunks per lane: the lane's activation
+  // slices (the same for every row it takes) are read from LDS into registers
+  // once, after staging
+  constexpr bool XREG = (MM == 1 && KQ <= 3);
+  uint4 xr[KQ][8];
+  float xr2[KQ][2];
   using Buf = Chunk[NMAT][KQ];
   // past the last row: re-read row fb (the wave's current row, cache-hot), or
   // row 0 if that is past the end too (never used either way)
@@ -174,11 +214,16 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
 #pragma unroll
     for (int k = 0; k < KQ; ++k) {
       if (!has[k]) continue;
-      const int q = lane + 64 * k;
-      const _Float16* xq = xs + 64 * q;        // chunk q covers weights [64q, 64q+64)
-      const float* xq2 = X2 + 2 * q;
+      if constexpr (XREG) {
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) chunk_dot<MM>(buf[m][k], cq[k], xq, TS, xq2, 2 * Q, nk, acc[m]);
+        for (int m = 0; m < NMAT; ++m) acc[m][0] += chunk_dot_reg(buf[m][k], cq[k], xr[k], xr2[k][0], xr2[k][1], nk);
+      } else {
+        const int q = lane + 64 * k;
+        const _Float16* xq = xs + 64 * q;        // chunk q covers weights [64q, 64q+64)
+        const float* xq2 = X2 + 2 * q;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) chunk_dot<MM>(buf[m][k], cq[k], xq, TS, xq2, 2 * Q, nk, acc[m]);
+      }
     }
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
@@ -266,6 +311,16 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
     if (g < ngroups && (a & 3) == 0) X2[t * 2 * Q + (a >> 2)] = s8;
   }
   __syncthreads();
+  if constexpr (XREG) {
+#pragma unroll
+    for (int k = 0; k < KQ; ++k) {
+      const int q = has[k] ? lane + 64 * k : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xr[k][i] = *reinterpret_cast<const uint4*>(xs + 64 * q + 8 * i);
+      xr2[k][0] = X2[2 * q];
+      xr2[k][1] = X2[2 * q + 1];
+    }
+  }
 
   if constexpr (DEPTH > 1) {
     // DEPTH rows in flight per wave: a buffer is refilled with the row DEPTH
@@ -307,17 +362,19 @@ int cu_count() {
 // this instantiation at this LDS size), so no workgroup waits for another to end.
 // Launch shape of the row kernels: rows in flight per wave (1 to 4; eight-wave
 // workgroups take 1 or 2), waves per workgroup, workgroups per CU (0: as many
-// as are resident).  Measured on the 4096/11008 layer sweep: two rows in
-// flight on persistent four-wave workgroups, two per CU for the gate/up pass
-// (about 11 rows per wave) and one for the down pass (4 rows per wave), beat
-// the one-row, full-occupancy shape by ~1.8 us per layer in kernel time.
+// as are resident).  Measured on the 4096/11008 layer sweep (graph replay)
+// with the activation slices in registers: one row in flight on three
+// four-wave workgroups per CU for the gate/up pass (about 7 rows per wave),
+// two rows on one eight-wave workgroup per CU for the down pass (2 rows per
+// wave): 20.8-20.9 us per layer against 22.1-22.3 for two rows on two
+// four-wave workgroups (gate/up) and one (down).
 // ZINC_DR_GU / ZINC_DR_DN = "depth,waves,wg_per_cu" override them.
 struct DrCfg {
   int depth, waves, wg_per_cu;
 };
 
 inline DrCfg dr_cfg(bool gateup) {
-  DrCfg c = gateup ? DrCfg{2, 4, 2} : DrCfg{2, 4, 1};
+  DrCfg c = gateup ? DrCfg{1, 4, 3} : DrCfg{2, 8, 1};
   if (const char* e = std::getenv(gateup ? "ZINC_DR_GU" : "ZINC_DR_DN")) {
     int d = 0, w = 0, g = -1;
     const bool ok = std::sscanf(e, "%d,%d,%d", &d, &w, &g) == 3 && g >= 0 &&
