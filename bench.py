@@ -264,6 +264,23 @@ def staged_lines(args, torch, np, Z, S, dev, t):
     """The fused prefill against its staged comparison baseline (the same
     units with G, U and the intermediate in device memory), whole calls."""
     out = []
+    # the fused call runs the staged baseline's unit (configuration D) at
+    # every M, so the two differ only in where the intermediate lives; the
+    # override is in place before the workspace size query, which follows it
+    saved = os.environ.get("ZINC_PREFILL_CFG")
+    os.environ["ZINC_PREFILL_CFG"] = "D"
+    try:
+        out = _staged_lines_d(torch, Z, S, dev, t)
+    finally:
+        if saved is None:
+            os.environ.pop("ZINC_PREFILL_CFG", None)
+        else:
+            os.environ["ZINC_PREFILL_CFG"] = saved
+    return out
+
+
+def _staged_lines_d(torch, Z, S, dev, t):
+    out = []
     for name, steps in (("prefill_m256", 50), ("prefill_m2048", 10)):
         w = S.WORKLOADS[name]
         wg, wu, wd = (t(a) for a in S.layer_weights(w.seed, 0, w.hidden, w.inter))
@@ -279,21 +296,11 @@ def staged_lines(args, torch, np, Z, S, dev, t):
             Z.zinc_mlp_q4k_prefill_staged(wg, wu, wd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y,
                                           workspace=wss)
 
-        # alternate the two a few times (same thermal state), keep each one's best
-        # round; the fused call runs the staged baseline's unit (configuration
-        # D) at every M, so the two differ only in where the intermediate lives
+        # alternate the two a few times (same thermal state), keep each one's best round
         best_f, best_s = float("inf"), float("inf")
-        saved = os.environ.get("ZINC_PREFILL_CFG")
-        os.environ["ZINC_PREFILL_CFG"] = "D"
-        try:
-            for _ in range(3):
-                best_f = min(best_f, time_calls(fused, steps, 3, torch)[0] / steps)
-                best_s = min(best_s, time_calls(staged, steps, 3, torch)[0] / steps)
-        finally:
-            if saved is None:
-                os.environ.pop("ZINC_PREFILL_CFG", None)
-            else:
-                os.environ["ZINC_PREFILL_CFG"] = saved
+        for _ in range(3):
+            best_f = min(best_f, time_calls(fused, steps, 3, torch)[0] / steps)
+            best_s = min(best_s, time_calls(staged, steps, 3, torch)[0] / steps)
         crossing = 6 * w.M * w.inter * 2
         out.append({
             "workload": f"fused vs staged prefill 4096/11008 M={w.M} (seed {w.seed}, layer 0)",
