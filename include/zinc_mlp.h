@@ -116,6 +116,10 @@ int zinc_q5_1_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float*
  * fp16 at the output scale and summed in fp32 by a reduce kernel.  The
  * workspace size is non-decreasing in M (here and for the _staged and _block
  * variants): a workspace sized for M serves every call with fewer tokens.
+ * Tuning override: the environment variable ZINC_PREFILL_CFG = "<A|B|C|D>" or
+ * "<A|B|C|D>:<chunks>" forces a unit configuration (and a chunk count); it is
+ * read by each call and each size query, so it must be set before the query
+ * whose workspace the call uses.
  * Limits: hidden, inter multiples of 256, hidden <= 16384, inter <= 65536,
  * M <= 2^20 and (M + 1) * (hidden / 256) * 544 < 2^32 (else ZINC_ERR_ARG, and
  * the workspace size query returns 0).
