@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64 * kRouterTokensPerBlock) void k_route_topk(const
       my_val = value_of(top);
     }
   }
-  // softmax over the chosen logits; round 0 picked the largest (or NaN, if
+  // softmax over the chosen logits; the first pick was the largest (or NaN, if
   // every logit is NaN, which makes every weight NaN as the definition does)
   const float lmax = __shfl(my_val, 0, 64);
   const float e = (lane < top_k) ? expf(my_val - lmax) : 0.0f;
