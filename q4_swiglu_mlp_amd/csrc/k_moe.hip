@@ -138,8 +138,12 @@ __device__ int build_tile_table(int e, int E, int c, int MT, int* s0, int* s1, i
   s3[e] = fb;
   s4[e] = rb;
   __syncthreads();
-  // inclusive Hillis-Steele scans
-  for (int d = 1; d < 1024; d <<= 1) {
+  // inclusive Hillis-Steele scans over the first P entries, P the power of
+  // two at or above E (the entries from E on are zero, so entry P - 1 holds
+  // the totals and later entries are never read)
+  int P = 1;
+  while (P < E) P <<= 1;
+  for (int d = 1; d < P; d <<= 1) {
     const int a0 = (e >= d) ? s0[e - d] : 0;
     const int a1 = (e >= d) ? s1[e - d] : 0;
     const int a2 = (e >= d) ? s2[e - d] : 0;
@@ -154,7 +158,7 @@ __device__ int build_tile_table(int e, int E, int c, int MT, int* s0, int* s1, i
     __syncthreads();
   }
   const int off = s0[e] - c;   // exclusive
-  const int tfa = s1[1023], tra = s2[1023], tfb = s3[1023], trb = s4[1023];
+  const int tfa = s1[P - 1], tra = s2[P - 1], tfb = s3[P - 1], trb = s4[P - 1];
   if (e < E) offsets[e] = off;
   if (e == E - 1) {
     offsets[E] = s0[e];
