@@ -369,8 +369,22 @@ __global__ __launch_bounds__(256) void k_moe_combine(const _Float16* __restrict_
       float part[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) part[e] = 0.0f;
-      for (int c = 0; c < nc; ++c) {
-        const half8 v = *reinterpret_cast<const half8*>(Q + ((size_t)c * (pairs + 1) + slot) * H + n);
+      const _Float16* base = Q + (size_t)slot * H + n;
+      const size_t cstride = (size_t)(pairs + 1) * H;
+      int c = 0;
+      // four chunks' loads in flight at a time (a slot has 4 or 6 chunks);
+      // the sum keeps chunk order
+      for (; c + 4 <= nc; c += 4) {
+        half8 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const half8*>(base + (size_t)(c + u) * cstride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part[e] += (float)v[u][e];
+      }
+      for (; c < nc; ++c) {
+        const half8 v = *reinterpret_cast<const half8*>(base + (size_t)c * cstride);
 #pragma unroll
         for (int e = 0; e < 8; ++e) part[e] += (float)v[e];
       }
