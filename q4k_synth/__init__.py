@@ -51,6 +51,46 @@ def gen_q4k_blob(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
     return blob
 
 
+def gen_q4k_blob_centred(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
+    """Random Q4_K matrix whose sub-blocks are centred on zero, as the blocks of
+    a real GGUF tensor are: every sub-block's min field equals its scale field
+    (m_j = sc_j) and dmin = fp16(7.5 * d), so each weight is close to
+    d * sc_j * (q - 7.5), spread evenly around 0 (the uniform recipe of
+    gen_q4k_blob has a mean of about +1.1).  Scales and quants stay uniform
+    random.
+
+    The equal fields come from the byte layout of the block's 12 scale bytes
+    S: sc_j and m_j of the first four sub-blocks are the low six bits of S[j]
+    and S[j + 4], and those of the last four are split between the nibbles of
+    S[j + 4] and the top two bits of S[j - 4] and S[j].  So S[4:8] = S[0:4]
+    with both nibbles of each of S[8:12] equal gives m_j = sc_j for all eight.
+    """
+    if cols % QK_K:
+        raise ValueError("cols must be a multiple of 256")
+    nb = cols // QK_K
+    blob = np.empty((rows, nb, BLOCK_BYTES), dtype=np.uint8)
+    d = rng.uniform(1e-3, 1e-2, size=(rows, nb)).astype(np.float16)
+    dmin = (d.astype(np.float64) * 7.5).astype(np.float16)
+    blob[:, :, 0:2] = d.view(np.uint8).reshape(rows, nb, 2)
+    blob[:, :, 2:4] = dmin.view(np.uint8).reshape(rows, nb, 2)
+    low = rng.integers(0, 256, size=(rows, nb, 4), dtype=np.uint8)
+    nib = rng.integers(0, 16, size=(rows, nb, 4), dtype=np.uint8)
+    blob[:, :, 4:8] = low
+    blob[:, :, 8:12] = low
+    blob[:, :, 12:16] = nib | (nib << 4)
+    blob[:, :, 16:] = rng.integers(0, 256, size=(rows, nb, BLOCK_BYTES - 16), dtype=np.uint8)
+    return blob
+
+
+def centred_layer_weights(seed: int, layer: int, hidden: int, inter: int):
+    """The zero-centred recipe's gate, up and down blobs for one layer."""
+    rng = np.random.default_rng([seed, 500 + layer])
+    wg = gen_q4k_blob_centred(rng, inter, hidden)
+    wu = gen_q4k_blob_centred(rng, inter, hidden)
+    wd = gen_q4k_blob_centred(rng, hidden, inter)
+    return wg, wu, wd
+
+
 def gen_x(rng: np.random.Generator, M: int, hidden: int, sd: float = 1.0) -> np.ndarray:
     """fp16 activations ``[M x hidden]``, normal(0, sd) rounded to fp16."""
     return (rng.standard_normal((M, hidden)) * sd).astype(np.float16)

@@ -677,3 +677,85 @@ def test_oracle_matches_committed_regression_fixture(root_dir):
     assert np.array_equal(O.q4k_dequant_f32(wg[0:1, 0:1], 1, 256)[0], np.array(sections["w32"], np.float32))
     assert np.allclose(y[0], sections["y0"], rtol=1e-12, atol=0)
     assert np.allclose(y[7], sections["y7"], rtol=1e-12, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# acceptance metrics: closed forms on hand-built arrays
+# ---------------------------------------------------------------------------
+def test_parity_metrics_closed_forms():
+    # y_ref = (3, -4, 0, 1): sum|r| = 8, mean r^2 = 26/4, RMS = sqrt(6.5)
+    # err = (0.5, 0, 0.25, 0): max 0.5, sum 0.75
+    ref = np.array([3.0, -4.0, 0.0, 1.0])
+    got = np.array([3.5, -4.0, 0.25, 1.0])
+    m = O.parity_metrics(got, ref)
+    assert m["rms_ref"] == pytest.approx(np.sqrt(6.5), rel=1e-15)
+    assert m["max_err_over_rms"] == pytest.approx(0.5 / np.sqrt(6.5), rel=1e-15)
+    assert m["mean_rel_err"] == pytest.approx(0.75 / 8.0, rel=1e-15)
+    assert m["finite"]
+    # the plausible slips give other numbers here: a per-element mean of
+    # |e|/|r| (infinite: r has a zero), RMS of the error over RMS(ref)
+    # (0.2795/2.55), max error over max |ref| (0.125)
+    assert m["max_err_over_rms"] != pytest.approx(0.125)
+    assert m["max_err_over_rms"] != pytest.approx(np.sqrt(0.3125 / 4) / np.sqrt(6.5))
+
+
+def test_parity_metrics_pool_every_output_of_the_call():
+    # two rows of very different size: the sums run over all four outputs,
+    # not row by row (a row-wise mean relative error would be (0.05 + 0) / 2)
+    ref = np.array([[1.0, 1.0], [10.0, 10.0]])
+    got = np.array([[1.1, 1.0], [10.0, 10.0]])
+    m = O.parity_metrics(got, ref)
+    assert m["mean_rel_err"] == pytest.approx(0.1 / 22.0, rel=1e-12)
+    assert m["max_err_over_rms"] == pytest.approx(0.1 / np.sqrt(50.5), rel=1e-12)
+    assert m["rms_ref"] == pytest.approx(np.sqrt(50.5), rel=1e-15)
+
+
+def test_within_tolerance_bounds_are_inclusive_and_both_bind():
+    assert O.MAX_ERR_OVER_RMS == 2e-2 and O.MEAN_REL_ERR == 5e-3
+    ref = np.ones(1000)                       # RMS 1, sum|r| 1000
+    # mean relative error 2^-8 = 0.0039 (inside), 2^-7 = 0.0078 (outside);
+    # max|err|/RMS stays below 2e-2 in both
+    assert O.within_tolerance(ref + 2.0 ** -8, ref)
+    assert not O.within_tolerance(ref + 2.0 ** -7, ref)
+    # one large error: 2^-6 = 0.0156 (inside), 2^-5 = 0.031 (outside); the
+    # mean relative error stays tiny in both
+    for e, ok in ((2.0 ** -6, True), (2.0 ** -5, False)):
+        got = ref.copy()
+        got[17] += e
+        assert O.within_tolerance(got, ref) is ok
+    # at the mean bound (as exact as binary allows): decided by <=, not <
+    ref2 = np.full(4, 2.0)
+    got2 = ref2 + np.array([0.04, 0.0, 0.0, 0.0])   # sum|e| / sum|r| = 0.04 / 8 = 5e-3
+    assert O.parity_metrics(got2, ref2)["mean_rel_err"] == pytest.approx(5e-3, rel=1e-12)
+    assert O.within_tolerance(got2, ref2) == (O.parity_metrics(got2, ref2)["mean_rel_err"] <= 5e-3)
+
+
+def test_within_tolerance_rejects_non_finite_outputs():
+    ref = np.ones(8)
+    for bad in (np.nan, np.inf, -np.inf):
+        got = ref.copy()
+        got[2] = bad
+        assert not O.within_tolerance(got, ref)
+        assert not O.parity_metrics(got, ref)["finite"]
+    assert O.within_tolerance(ref.copy(), ref)
+
+
+# ---------------------------------------------------------------------------
+# the zero-centred weight recipe (input generator) read by the oracle
+# ---------------------------------------------------------------------------
+def test_centred_recipe_fields_and_mean():
+    rng = np.random.default_rng(9)
+    blob = S.gen_q4k_blob_centred(rng, 64, 512)
+    d, dmin, sc, m, q = O.q4k_fields(blob)
+    assert np.array_equal(sc, m)                                   # m_j = sc_j for every sub-block
+    assert np.array_equal(dmin, np.float16(d * 7.5).astype(np.float64))
+    assert sc.min() == 0 and sc.max() == 63 and q.min() == 0 and q.max() == 15
+    w = O.q4k_dequant(blob, 64, 512)
+    # each weight is sc*(d*q - dmin) with dmin within an fp16 rounding of 7.5*d
+    d_b = np.repeat(d[..., None], 256, axis=-1).reshape(64, 512)
+    assert np.all(np.abs(w) <= 63 * 8.0 * d_b * (1 + 2e-3))
+    # centred: the mean is small against the spread (the uniform recipe's
+    # mean is about 1.1 at a spread of about 1.5)
+    assert abs(w.mean()) < 0.02 * w.std()
+    wu = O.q4k_dequant(S.gen_q4k_blob(rng, 64, 512), 64, 512)
+    assert wu.mean() > 0.5 * wu.std()
