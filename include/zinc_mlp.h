@@ -43,7 +43,9 @@
  *     host.  Buffers must stay valid until the stream has passed the call.
  *   - A failed kernel launch returns ZINC_ERR_HIP.
  *   - M == 0 is a no-op returning ZINC_OK.
- *   - Calls are stateless; concurrent calls need distinct workspaces and outputs.
+ *   - Calls hold no state between them (the optional timing hook at the end of
+ *     this header is the one process-wide recorder, off by default and outside
+ *     this statement); concurrent calls need distinct workspaces and outputs.
  *   - y must not alias x, the weights or the workspace.
  */
 #ifndef ZINC_MLP_H
@@ -116,10 +118,8 @@ int zinc_q5_1_dequant_f32(const void* blocks, int32_t rows, int32_t cols, float*
  * fp16 at the output scale and summed in fp32 by a reduce kernel.  The
  * workspace size is non-decreasing in M (here and for the _staged and _block
  * variants): a workspace sized for M serves every call with fewer tokens.
- * Tuning override: the environment variable ZINC_PREFILL_CFG = "<A|B|C|D>" or
- * "<A|B|C|D>:<chunks>" forces a unit configuration (and a chunk count); it is
- * read by each call and each size query, so it must be set before the query
- * whose workspace the call uses.
+ * The kernel plan (unit shape and chunk count) is a function of (M, hidden,
+ * inter) only.
  * Limits: hidden, inter multiples of 256, hidden <= 16384, inter <= 65536,
  * M <= 2^20 and (M + 1) * (hidden / 256) * 544 < 2^32 (else ZINC_ERR_ARG, and
  * the workspace size query returns 0).
@@ -208,9 +208,9 @@ int zinc_mlp_q4k_decode(const void* w_gate, const void* w_up, const void* w_down
  * Batched-expert MoE MLP: y[t] = sum_{s < top_k} p[t,s] * MLP_{ids[t,s]}(x[t]).
  * Expert ids (int32 [M x top_k]) and mixing weights (fp32 [M x top_k]) are read
  * on the GPU; the host never reads them back and launches a fixed number of
- * kernels whatever the routing ("Four bottlenecks, one CUDA backend",
- * "Bottleneck 2": batched experts whose kernels index the chosen experts'
- * weights themselves).  w_gate / w_up hold n_experts [inter x hidden] Q4_K
+ * kernels whatever the routing: the batched-expert form of "Four bottlenecks,
+ * one CUDA backend", "Bottleneck 2", where the device code looks the routing
+ * up and addresses each chosen expert's weights without a host round trip.  w_gate / w_up hold n_experts [inter x hidden] Q4_K
  * matrices back to back, w_down n_experts [hidden x inter] matrices.
  * A slot whose id is outside [0, n_experts) contributes nothing; the kernel
  * then ORs 1 into *dev_error (a device int32, may be NULL) -- the flag is
@@ -257,7 +257,7 @@ int zinc_moe_experts_fmt(const void* w_gate, const void* w_up, const void* w_dow
  * zinc_moe_q4k_experts reads, so no host read-back separates the router from
  * the experts ("Four bottlenecks, one CUDA backend", "Bottleneck 2": every MoE
  * layer computes router logits and picks the top-k experts; "What's next, and
- * what it's worth": the router's remaining per-layer sync).
+ * what it's worth" names the router's host synchronisation as the step left).
  *   logits          fp32 [M x n_experts] row-major, device
  *   expert_ids      int32 [M x top_k], device, written: slot s holds the expert
  *                   of the s-th largest logit; equal logits go to the lower

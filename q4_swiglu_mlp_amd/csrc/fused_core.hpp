@@ -30,11 +30,12 @@
 //   an fp16 partial store per chunk at the output scale; MoE: see k_moe.hip).
 //
 // This is the dataflow of "Fused SwiGLU MLP: ZINC RDNA4 Down-Projection
-// Bandwidth" ("Why this fusion is harder than the last one": compute a block of
-// the intermediate for a set of columns, stage it in the LDS, feed the down
-// projection's accumulation for those columns, advance; the fused row of
-// Fig. 1), with the dequant fused into the producer GEMM as on "VGPR pressure
-// caps the fused RDNA4 prefill GEMM at nine waves" (scale values kept out of
+// Bandwidth" ("Why this fusion is harder than the last one" and the fused row
+// of Fig. 1): the kernel walks the intermediate dimension in pieces, and each
+// piece is produced on chip, held in LDS and consumed at once by the down
+// projection before the next piece is made.  The dequant is fused into the
+// producer GEMM as on "VGPR pressure caps the fused RDNA4 prefill GEMM at nine
+// waves" (scale values kept out of
 // per-lane work as that page's "The recoverable registers versus the stubborn
 // ones" advises).  The RDNA4 16x16 WMMA tiling there is replaced by gfx950
 // 32x32x16 MFMA on 64-wide waves.

@@ -39,8 +39,6 @@
 #include "util_kernels.hpp"
 
 #include <algorithm>
-#include <cstdio>
-#include <cstdlib>
 
 namespace zinc {
 
@@ -360,30 +358,14 @@ int cu_count() {
 
 // Persistent grid: as many workgroups as are resident at once (occupancy of
 // this instantiation at this LDS size), so no workgroup waits for another to end.
-// Launch shape of the row kernels: rows in flight per wave (1 to 4; eight-wave
-// workgroups take 1 or 2), waves per workgroup, workgroups per CU (0: as many
-// as are resident).  Measured on the 4096/11008 layer sweep (graph replay)
-// with the activation slices in registers: one row in flight on three
+// Launch shape of the row kernels: rows in flight per wave, waves per
+// workgroup, workgroups per CU.  Measured on the 4096/11008 layer sweep (graph
+// replay) with the activation slices in registers: one row in flight on three
 // four-wave workgroups per CU for the gate/up pass (about 7 rows per wave),
 // two rows on one eight-wave workgroup per CU for the down pass (2 rows per
 // wave): 20.8-20.9 us per layer against 22.1-22.3 for two rows on two
-// four-wave workgroups (gate/up) and one (down).
-// ZINC_DR_GU / ZINC_DR_DN = "depth,waves,wg_per_cu" override them.
-struct DrCfg {
-  int depth, waves, wg_per_cu;
-};
-
-inline DrCfg dr_cfg(bool gateup) {
-  DrCfg c = gateup ? DrCfg{1, 4, 3} : DrCfg{2, 8, 1};
-  if (const char* e = std::getenv(gateup ? "ZINC_DR_GU" : "ZINC_DR_DN")) {
-    int d = 0, w = 0, g = -1;
-    const bool ok = std::sscanf(e, "%d,%d,%d", &d, &w, &g) == 3 && g >= 0 &&
-                    ((w == 4 && d >= 1 && d <= 4) || (w == 8 && d >= 1 && d <= 2));
-    if (ok) c = DrCfg{d, w, g};
-  }
-  return c;
-}
-
+// four-wave workgroups (gate/up) and one (down); 3 or 4 rows in flight were
+// slower for either pass.
 template <int MM, bool GATEUP, int KQ, int DEPTH, int NW>
 hipError_t launch_rows_cfg(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
                            float scale, const _Float16* res, float res_scale, const _Float16* gamma, float eps,
@@ -418,21 +400,10 @@ template <int MM, bool GATEUP, int KQ>
 hipError_t launch_rows(const void* W0, const void* W1, int K, int N, const _Float16* x, int M, _Float16* out,
                        float scale, const _Float16* res, float res_scale, const _Float16* gamma, float eps,
                        hipStream_t stream) {
-  const DrCfg c = dr_cfg(GATEUP);
-#define ZINC_DR_LAUNCH(D, W)                                                                                         \
-  return launch_rows_cfg<MM, GATEUP, KQ, D, W>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, c.wg_per_cu, \
-                                               stream)
-  if (c.waves == 8) {
-    if (c.depth == 1) ZINC_DR_LAUNCH(1, 8);
-    ZINC_DR_LAUNCH(2, 8);
-  }
-  switch (c.depth) {
-    case 1: ZINC_DR_LAUNCH(1, 4);
-    case 3: ZINC_DR_LAUNCH(3, 4);
-    case 4: ZINC_DR_LAUNCH(4, 4);
-    default: ZINC_DR_LAUNCH(2, 4);
-  }
-#undef ZINC_DR_LAUNCH
+  if constexpr (GATEUP)
+    return launch_rows_cfg<MM, GATEUP, KQ, 1, 4>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, 3, stream);
+  else
+    return launch_rows_cfg<MM, GATEUP, KQ, 2, 8>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, 1, stream);
 }
 
 template <int MM, bool GATEUP>

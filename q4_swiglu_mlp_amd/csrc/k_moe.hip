@@ -2,9 +2,10 @@
 //
 // The expert ids and mixing weights stay on the GPU.  The host launches a
 // fixed sequence of kernels sized only by (M, top_k, n_experts) -- never by the
-// routing -- so nothing is read back mid-call ("Four bottlenecks, one CUDA
-// backend", "Bottleneck 2": batched-expert kernels read the chosen expert ids
-// from a GPU buffer and index the expert weights themselves):
+// routing -- so nothing is read back mid-call.  This is the batched-expert
+// design of "Four bottlenecks, one CUDA backend", "Bottleneck 2": the device
+// kernels look up which experts each token uses and address those experts'
+// weights on their own, with no host round trip in between:
 //   1. k_moe_count    per-expert slot counts; invalid ids set *dev_error
 //   2. k_moe_plan     exclusive scan of the counts -> list offsets, and the tile
 //                     table (expert, first list entry, rows) of MT-slot tiles
@@ -25,8 +26,6 @@
 // tiles the scatter put it in), and the combine order is fixed, so the result
 // is deterministic (the atomics only count and place).
 #include <algorithm>
-#include <cstdlib>
-#include <cstring>
 
 #include "fused16.hpp"
 #include "launch.hpp"
@@ -413,9 +412,7 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
   const int E = n_experts;
   const int n_slots = M * top_k;
   MoePlan pl = carve(ws, M, top_k, E, hidden, inter, nullptr);
-  // ZINC_MOE_ROUTE=multi forces the multi-kernel routing (to test it at small sizes)
-  const char* route = std::getenv("ZINC_MOE_ROUTE");
-  const bool one_block = n_slots <= kRouteOneBlockSlots && !(route && std::strcmp(route, "multi") == 0);
+  const bool one_block = n_slots <= kRouteOneBlockSlots;
   if (one_block) {
     hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, stream, ids, n_slots, E, dev_error, pl.offsets,
                        pl.tile_expert, pl.tile_start, pl.tile_rows, pl.n_tiles, pl.slots, pl.pos, MT_MOE);

@@ -13,13 +13,9 @@
 //   C: MT=64, ICMAX=384 -- the 32x32x16 unit of fused_core.hpp: half the
 //      chunks, so half the partial traffic and one round of units at 512
 //      tokens.  The default past 4 token tiles.
-// Every configuration stores its partials in token quads, P[chunk][t/4][n][t%4],
-// which k_reduce_quads sums.
-//   A: MT=32, ICMAX=384, B: MT=64, ICMAX=640 -- the same unit, kept as tuning
-//      alternatives (ZINC_PREFILL_CFG).
-#include <cstdlib>
-#include <cstring>
-
+// Both configurations store their partials in token quads, P[chunk][t/4][n][t%4],
+// which k_reduce_quads sums.  The plan is a function of (M, hidden, inter)
+// alone.
 #include "fused16.hpp"
 #include "launch.hpp"
 #include "util_kernels.hpp"
@@ -175,7 +171,7 @@ __global__ __launch_bounds__(256) void k_reduce_quads(const _Float16* __restrict
 }
 
 struct Plan {
-  char cfg;      // 'A' .. 'D'
+  char cfg;      // 'C' or 'D'
   int MT, ICMAX;
   int n_tiles, n_chunks;
   int Mpad;
@@ -188,49 +184,27 @@ int round_up(int a, int b) { return (a + b - 1) / b * b; }
 // which chunks = 8 * floor(32 k / tiles) reaches the unit's minimum, so every
 // XCD runs at most k rounds of 32 units, and the units are as small as k
 // rounds allow; of the chunk counts that give the same largest unit, the
-// smallest (fewest partials).  D (192-row chunks, at least 58) up to four 64-token tiles,
-// where one round fits; C (384-row chunks, at least 29) beyond.
+// smallest (fewest partials).  D (192-row chunks, at least 58) up to four
+// 64-token tiles, where one round fits; C (384-row chunks, at least 29) beyond.
 // Measured on the 4096/11008 layer (whole calls; "D:86" = D with 86 chunks):
 // M=192 D:86 159 us (some XCDs 33 units: two rounds); M=256 D:64 128; M=320
 // D:58 202, C:43 155; M=384 C:42 310 (36 units on some XCDs), C:29 222;
 // M=2048 C:29 1021, D:58 1078.
-// force_d: configuration D whatever the override names (its chunk count
-// still applies); the staged baseline runs that unit.
-// Tuning override: ZINC_PREFILL_CFG="<A|B|C|D>[:<chunks>]".
-struct PlanOverride {
-  char cfg = 0;
-  int chunks = 0;
-};
-
-PlanOverride read_override() {
-  PlanOverride o;
-  if (const char* e = std::getenv("ZINC_PREFILL_CFG")) {
-    if (e[0] >= 'A' && e[0] <= 'D') o.cfg = e[0];
-    if (e[0] && e[1] == ':') o.chunks = std::atoi(e + 2);
-  }
-  return o;
-}
-
-Plan make_plan(int M, int H, int I, bool force_d, const PlanOverride& o) {
+// force_d: configuration D at every M (the staged baseline runs that unit).
+Plan make_plan(int M, int H, int I, bool force_d) {
   (void)H;
   Plan p;
   const int tiles64 = (M + 63) / 64;
   p.cfg = (tiles64 <= 4 || force_d) ? 'D' : 'C';
-  if (o.cfg && !force_d) p.cfg = o.cfg;
-  const int chunks_wanted = o.chunks;
-  p.MT = (p.cfg == 'A') ? 32 : 64;
-  p.ICMAX = (p.cfg == 'B') ? 640 : (p.cfg == 'D') ? 192 : 384;
+  p.MT = 64;
+  p.ICMAX = (p.cfg == 'D') ? 192 : 384;
   const int npan = I / 64;
   const int min_chunks = (npan + p.ICMAX / 64 - 1) / (p.ICMAX / 64);
   p.n_tiles = (M + p.MT - 1) / p.MT;
-  int chunks = min_chunks;
-  if (p.cfg != 'B') {
-    const int k = (((min_chunks + 7) / 8) * p.n_tiles + 31) / 32;   // fewest rounds
-    const int most = 8 * ((32 * k) / p.n_tiles);    // chunks that fit k rounds
-    const int per = (npan + most - 1) / most;        // panels of the largest unit
-    chunks = (npan + per - 1) / per;                 // the fewest chunks with units that size
-  }
-  if (chunks_wanted > 0) chunks = chunks_wanted;
+  const int k = (((min_chunks + 7) / 8) * p.n_tiles + 31) / 32;   // fewest rounds
+  const int most = 8 * ((32 * k) / p.n_tiles);    // chunks that fit k rounds
+  const int per = (npan + most - 1) / most;        // panels of the largest unit
+  int chunks = (npan + per - 1) / per;             // the fewest chunks with units that size
   if (chunks < min_chunks) chunks = min_chunks;
   if (chunks > npan) chunks = npan;
   p.n_chunks = chunks;
@@ -283,9 +257,8 @@ size_t most_over_smaller_m(int M, Need need) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int M, int hidden, int inter) {
-  const PlanOverride o = read_override();
   return most_over_smaller_m(M, [&](int m) {
-    const Plan p = make_plan(m, hidden, inter, false, o);
+    const Plan p = make_plan(m, hidden, inter, false);
     return partial_bytes(p, hidden) + staged_x_bytes(p, hidden);
   });
 }
@@ -293,9 +266,8 @@ size_t prefill_workspace_bytes(int M, int hidden, int inter) {
 // Staged baseline workspace: the fused path's (configuration D) plus fp16
 // G, U and the intermediate, [M x inter] each.
 size_t prefill_staged_workspace_bytes(int M, int hidden, int inter) {
-  const PlanOverride o = read_override();
   return most_over_smaller_m(M, [&](int m) {
-    const Plan p = make_plan(m, hidden, inter, true, o);
+    const Plan p = make_plan(m, hidden, inter, true);
     const size_t mi = (((size_t)m * inter * sizeof(_Float16)) + 255) & ~(size_t)255;
     return partial_bytes(p, hidden) + (x16_staged_bytes(p.n_tiles * p.MT, hidden) + 255) / 256 * 256 + 3 * mi;
   });
@@ -304,7 +276,7 @@ size_t prefill_staged_workspace_bytes(int M, int hidden, int inter) {
 hipError_t launch_prefill_staged(const void* wg, const void* wu, const void* wd, int hidden, int inter,
                                  const void* x, void* y, int M, int inter_shift, int out_shift, void* ws,
                                  hipStream_t stream) {
-  const Plan p = make_plan(M, hidden, inter, true, read_override());
+  const Plan p = make_plan(M, hidden, inter, true);
   _Float16* P = static_cast<_Float16*>(ws);
   uint8_t* xg = static_cast<uint8_t*>(ws) + partial_bytes(p, hidden);
   const size_t mi = (((size_t)M * inter * sizeof(_Float16)) + 255) & ~(size_t)255;
@@ -335,7 +307,7 @@ hipError_t launch_prefill_staged(const void* wg, const void* wu, const void* wd,
 hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hidden, int inter, const void* x,
                           void* y, int M, int inter_shift, int out_shift, void* ws, hipStream_t stream,
                           float mlp_scale, const void* res) {
-  const Plan p = make_plan(M, hidden, inter, false, read_override());
+  const Plan p = make_plan(M, hidden, inter, false);
   _Float16* P = static_cast<_Float16*>(ws);
   const float inter_scale = ldexpf(1.0f, -inter_shift);
   const float out_scale = ldexpf(1.0f, inter_shift - out_shift) * mlp_scale;
@@ -347,12 +319,10 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
     hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream,
                        static_cast<const _Float16*>(x), hidden, M, xg);
   timing_begin(stream);   // the timed region is the fused kernel alone
-  switch (p.cfg) {
-    case 'D': launch_cfg16<192>(p, wg, wu, wd, hidden, inter, x, M, P, xg, inter_scale, out_scale, stream); break;
-    case 'A': launch_cfg<1, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
-    case 'B': launch_cfg<2, 1, 640>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
-    default: launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream); break;
-  }
+  if (p.cfg == 'D')
+    launch_cfg16<192>(p, wg, wu, wd, hidden, inter, x, M, P, xg, inter_scale, out_scale, stream);
+  else
+    launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream);
   timing_end(stream);
   // every configuration stores its partials in token quads
   const dim3 rq(hidden / 64, p.Mpad / 32);

@@ -2,8 +2,9 @@
 // weights, from the router logits, written straight into the device buffers
 // the batched-expert call reads.  Every MoE layer picks its experts from the
 // router logits; choosing them on the GPU removes the last host read-back of a
-// layer ("Four bottlenecks, one CUDA backend", "Bottleneck 2" and "What's
-// next, and what it's worth": the router still keeps a per-layer sync).
+// layer, which that page names as the remaining per-layer synchronisation
+// ("Four bottlenecks, one CUDA backend", "Bottleneck 2" and "What's next, and
+// what it's worth").
 //
 // Selection order: larger logit first; equal logits by lower expert index; a
 // NaN logit ranks below every number (so it is chosen only when fewer than k

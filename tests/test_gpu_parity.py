@@ -96,17 +96,15 @@ def test_prefill_other_shapes(H, I):
     assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill H={H} I={I}")
 
 
-@pytest.mark.parametrize("cfg", ["A", "B", "C", "D:32"])
-def test_prefill_alternative_units(cfg, monkeypatch):
-    # the alternative fused units behind ZINC_PREFILL_CFG (32x32x16 units on
-    # 32- or 64-token tiles, wider chunks; D with a forced chunk count), at a
-    # shape with several tiles, chunks and a ragged tail
-    monkeypatch.setenv("ZINC_PREFILL_CFG", cfg)
-    H, I, M = 512, 1280, 100
-    wg, wu, wd, x = _rand_mlp(77, H, I, M)
+@pytest.mark.parametrize("M", [257, 320, 700])
+def test_prefill_unit_c(M):
+    # past four 64-token tiles the plan takes the 32x32x16 unit with 384-row
+    # chunks (unit C): several tiles, chunks and a ragged tail
+    H, I = 512, 1280
+    wg, wu, wd, x = _rand_mlp(77 + M, H, I, M)
     y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
     a, b = shifts_for(y_ref, h_ref)
-    assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill config {cfg}")
+    assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill unit C M={M}")
 
 
 def test_prefill_m256_workload_full():
@@ -266,19 +264,6 @@ def test_decode_tiny_workload(M):
     assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift), y_ref, f"decode tiny M={M}")
 
 
-@pytest.mark.parametrize("shape", ["1,8,0", "2,8,1", "1,4,3", "3,4,1", "4,4,1", "4,4,2"])
-def test_decode_m1_launch_shapes(shape, monkeypatch):
-    # the M = 1 row kernels under the other launch shapes (rows in flight per
-    # wave, waves per workgroup, workgroups per CU) that ZINC_DR_GU / ZINC_DR_DN select
-    monkeypatch.setenv("ZINC_DR_GU", shape)
-    monkeypatch.setenv("ZINC_DR_DN", shape)
-    H, I = 1024, 2816
-    wg, wu, wd, x = _rand_mlp(55, H, I, 1)
-    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
-    a, b = shifts_for(y_ref, h_ref)
-    assert_parity(decode(wg, wu, wd, H, I, x, a, b), y_ref, f"decode M=1 shape {shape}")
-
-
 @pytest.mark.parametrize("M", [1, 4])
 def test_decode_long_down_contraction(M):
     # inter = 16640 > 16384: longer than the M = 1 row kernels cover, so both M
@@ -358,22 +343,22 @@ def test_moe_tiny():
     assert_parity(_moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, 8), y_ref, "moe E=4 top-2")
 
 
-def test_moe_both_routing_paths(monkeypatch):
-    # one-workgroup routing (the default at this size) and the multi-kernel
-    # routing used past 65536 slots: the same oracle result, bit-identical y
-    E, H, I, M, k = 16, 256, 512, 300, 4
+@pytest.mark.parametrize("M", [32768, 32769])
+def test_moe_routing_paths_around_the_switch(M):
+    # up to 65536 slots the routing runs in one workgroup, past it as three
+    # grid-wide kernels: both sides of the switch against the oracle, with an
+    # invalid id that is flagged and contributes nothing
+    E, H, I, k = 16, 256, 256, 2
     wg, wu, wd, x, ids, p = _moe_inputs(E, H, I, M, k, 25)
     ids = ids.copy()
-    ids[5, 1] = E + 3                                    # one invalid id: flagged, contributes nothing
+    ids[5, 1] = E + 3
     y_ref, bad = O.moe(x, wg, wu, wd, ids, p, H, I)
     assert bad == 1
     b = max(0, int(np.ceil(np.log2(np.abs(y_ref).max() / 2 ** 13))))
-    y_one = _moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, b)
-    monkeypatch.setenv("ZINC_MOE_ROUTE", "multi")
-    y_multi = _moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, b)
-    assert_parity(y_one, y_ref, "moe one-workgroup routing")
-    assert_parity(y_multi, y_ref, "moe multi-kernel routing")
-    assert np.array_equal(y_one, y_multi)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    y = _moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, b, dev_error=flag)
+    assert int(flag.item()) == 1
+    assert_parity(y, y_ref, f"moe routing, {M * k} slots")
 
 
 def test_moe_top1_weight1_matches_dense():
