@@ -969,18 +969,25 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   if constexpr (MODE == kUnitDown) {
     // staged baseline: the strip and its 32-row sums from the intermediate in
     // device memory (zero rows past the unit's tokens)
-    const int nq = (r1 - r0) >> 2;
-    for (int idx = threadIdx.x; idx < MT * nq; idx += C::THREADS) {
-      const int t = idx / nq, jl = (idx - t * nq) * 4;
-      uint2 v = make_uint2(0u, 0u);
-      if (t < rows) v = *reinterpret_cast<const uint2*>(sio.h + (size_t)(sio.t0 + t) * I + r0 + jl);
-      const half4 hv = __builtin_bit_cast(half4, v);
-      const uint32_t w0 = (v.x & 0xFFFFu) | (v.y << 16);
-      const uint32_t w1 = (v.x >> 16) | (v.y & 0xFFFF0000u);
-      *reinterpret_cast<uint2*>(sm.u.s.hs + t * HS + (jl & ~63) + panel_pos(jl & 63)) = make_uint2(w0, w1);
-      const int jg = off * 64 + jl;
-      const int slot = 8 * (jg >> 8) + sb_slot((jg >> 5) & 7);
-      atomicAdd(&sm.hsum32[t * HSS + slot], ((float)hv[0] + (float)hv[1]) + ((float)hv[2] + (float)hv[3]));
+    // one thread per (token, 32-row group): the group's sum is taken in a
+    // fixed order, so the staged call's result does not depend on scheduling
+    const int n32 = (r1 - r0) >> 5;
+    for (int idx = threadIdx.x; idx < MT * n32; idx += C::THREADS) {
+      const int t = idx / n32, j32 = (idx - t * n32) * 32;
+      float s32 = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int jl = j32 + 4 * k;
+        uint2 v = make_uint2(0u, 0u);
+        if (t < rows) v = *reinterpret_cast<const uint2*>(sio.h + (size_t)(sio.t0 + t) * I + r0 + jl);
+        const half4 hv = __builtin_bit_cast(half4, v);
+        const uint32_t w0 = (v.x & 0xFFFFu) | (v.y << 16);
+        const uint32_t w1 = (v.x >> 16) | (v.y & 0xFFFF0000u);
+        *reinterpret_cast<uint2*>(sm.u.s.hs + t * HS + (jl & ~63) + panel_pos(jl & 63)) = make_uint2(w0, w1);
+        s32 += ((float)hv[0] + (float)hv[1]) + ((float)hv[2] + (float)hv[3]);
+      }
+      const int jg = off * 64 + j32;
+      sm.hsum32[t * HSS + 8 * (jg >> 8) + sb_slot((jg >> 5) & 7)] = s32;
     }
   }
   // SwiGLU in registers -> fp16 strip (panel order) and the 32-row sums.
