@@ -39,11 +39,7 @@ bool moe_rows_ok(int32_t M, int32_t top_k, int32_t hidden) {
 
 thread_local const char* t_last_hip_error = "no HIP error";
 
-int from_hip(hipError_t e) {
-  if (e == hipSuccess) return ZINC_OK;
-  t_last_hip_error = hipGetErrorString(e);
-  return ZINC_ERR_HIP;
-}
+int from_hip(hipError_t e) { return zinc::status_from_hip(e); }
 
 // Checks shared by the dense entry points.
 int check_dense(const void* wg, const void* wu, const void* wd, int32_t hidden, int32_t inter, const void* x,
@@ -70,6 +66,16 @@ int check_block(const void* norm_weight, float eps, float mlp_scale) {
 }
 
 }  // namespace
+
+namespace zinc {
+
+int status_from_hip(hipError_t e) {
+  if (e == hipSuccess) return ZINC_OK;
+  t_last_hip_error = hipGetErrorString(e);
+  return ZINC_ERR_HIP;
+}
+
+}  // namespace zinc
 
 extern "C" {
 

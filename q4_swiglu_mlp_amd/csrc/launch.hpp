@@ -9,6 +9,10 @@
 
 namespace zinc {
 
+// ZINC_OK for hipSuccess; otherwise ZINC_ERR_HIP, and `e` becomes the text
+// that zinc_hip_error_string() returns on this thread (capi.cpp).
+int status_from_hip(hipError_t e);
+
 // Kernel timing hook (timing.cpp): no-ops unless zinc_timing_enable() was called.
 void timing_begin(hipStream_t stream);
 void timing_end(hipStream_t stream);
