@@ -205,6 +205,28 @@ int zinc_mlp_q4k_decode(const void* w_gate, const void* w_up, const void* w_down
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The same call and result as
+ * zinc_mlp_q4k_decode (the same kernels), with the intermediate held in a
+ * device array the library owns instead of a caller workspace: one array per
+ * GPU, zinc_mlp_q4k_decode_noalloc_max_bytes() bytes (512 KiB), kept until the
+ * process ends.  Its address on each device is looked up on the first call
+ * made with that device current.  M * inter * 2 bytes (rounded up to 256)
+ * must fit it, else ZINC_ERR_WORKSPACE before any HIP call (e.g. M = 8 allows
+ * inter <= 32768).  `stream` must belong to the current device, else
+ * ZINC_ERR_ARG.  Every call on a GPU uses that GPU's one array: calls that
+ * overlap in time on one GPU (different streams, or threads) race on it and
+ * must be serialised by the caller.  Other arguments and errors as
+ * zinc_mlp_q4k_decode; no hipMalloc, hipFree or other allocating call is made.
+ */
+size_t zinc_mlp_q4k_decode_noalloc_max_bytes(void);
+int zinc_mlp_q4k_decode_noalloc(const void* w_gate, const void* w_up, const void* w_down,
+                                int32_t hidden, int32_t inter,
+                                const void* x_f16, void* y_f16, int32_t M,
+                                int32_t inter_shift, int32_t out_shift, void* stream);
+
+/*
  * Batched-expert MoE MLP: y[t] = sum_{s < top_k} p[t,s] * MLP_{ids[t,s]}(x[t]).
  * Expert ids (int32 [M x top_k]) and mixing weights (fp32 [M x top_k]) are read
  * on the GPU; the host never reads them back and launches a fixed number of

@@ -49,6 +49,8 @@ EXPORTS = (
     "zinc_mlp_q4k_prefill_staged",
     "zinc_mlp_q4k_decode_workspace_size",
     "zinc_mlp_q4k_decode",
+    "zinc_mlp_q4k_decode_noalloc_max_bytes",
+    "zinc_mlp_q4k_decode_noalloc",
     "zinc_moe_q4k_experts_workspace_size",
     "zinc_moe_q4k_experts",
     "zinc_moe_experts_fmt",
@@ -104,6 +106,10 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P, P, P, I32, I32, P, P, F32, F32, P, I32, I32, I32, P, SZ, P]
+    lib.zinc_mlp_q4k_decode_noalloc_max_bytes.restype = SZ
+    lib.zinc_mlp_q4k_decode_noalloc_max_bytes.argtypes = []
+    lib.zinc_mlp_q4k_decode_noalloc.restype = ctypes.c_int
+    lib.zinc_mlp_q4k_decode_noalloc.argtypes = [P, P, P, I32, I32, P, P, I32, I32, I32, P]
     lib.zinc_moe_q4k_experts_workspace_size.restype = SZ
     lib.zinc_moe_q4k_experts_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.zinc_moe_q4k_experts.restype = ctypes.c_int
@@ -401,6 +407,23 @@ def zinc_mlp_q4k_decode(w_gate, w_up, w_down, hidden: int, inter: int, x, inter_
     """Same result as the prefill entry point for 1 <= M <= 8, via HBM-bound matvecs."""
     return _dense("zinc_mlp_q4k_decode", decode_workspace_size, w_gate, w_up, w_down, hidden, inter, x, inter_shift,
                   out_shift, y, workspace, stream)
+
+
+def zinc_mlp_q4k_decode_noalloc(w_gate, w_up, w_down, hidden: int, inter: int, x, y, inter_shift: int = 0,
+                                out_shift: int = 0, stream=None):
+    """zinc_mlp_q4k_decode with the intermediate in the library's own device
+    array: nothing is allocated, so ``y`` (fp16 [M, hidden]) is required.
+    Calls that overlap in time on one GPU race on that array."""
+    torch = _torch()
+    _dense_weights(w_gate, w_up, w_down, hidden, inter)
+    M = _activation(x, hidden)
+    _need(y, torch.float16, (M, hidden), "y")
+    _on_gpu(w_gate, w_up, w_down, x, y)
+    s = _resolve_stream(stream, x.device)
+    st = lib.zinc_mlp_q4k_decode_noalloc(_ptr(w_gate), _ptr(w_up), _ptr(w_down), hidden, inter, _ptr(x), _ptr(y), M,
+                                         inter_shift, out_shift, s.cuda_stream)
+    _check(st, "zinc_mlp_q4k_decode_noalloc")
+    return y
 
 
 DOWN_FORMATS = {"q4_k": 0, "q5_k": 1, "q5_1": 2}
