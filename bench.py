@@ -17,7 +17,13 @@ with its RMS norm and residual, the 2048-token prefill over 32 layers) ride in
 "secondary".  ``--only staged`` instead times the fused prefill against its
 staged baseline (the intermediate in device memory) at M=256 and M=2048.
 
-usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-secondary] [--no-cpu-baseline]
+Also in the line: the measured peaks of this chip (an MFMA-only loop, HBM
+stream read and copy; libzinc_peaks.so), the graphics clock and socket power
+sampled through amdsmi during the headline's timed calls, and the headline
+fraction against the spec peak, the measured peak and the spec peak at the
+observed clock.
+
+usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-secondary] [--no-cpu-baseline] [--no-peaks]
 """
 from __future__ import annotations
 
@@ -82,7 +88,177 @@ def time_calls(fn, steps: int, warmup: int, torch):
     return t1 - t0, ms
 
 
-def headline(args, torch):
+PEAKS_LIB = os.path.join(ROOT, "q4_swiglu_mlp_amd", "_lib", "libzinc_peaks.so")
+SPEC_GFX_MHZ = 2400.0         # the clock the 2.5 PFLOP/s dense fp16 figure is quoted at
+
+
+def measure_peaks(torch):
+    """What the chip delivers in practice: an MFMA-only loop (16x16x32 and
+    32x32x16 fp16, fp32 accumulate) and streaming HBM reads and copies of
+    buffers far larger than the 256 MB last-level cache, timed with HIP events
+    on the stream the kernels run on (libzinc_peaks.so)."""
+    import ctypes
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.zinc_peak_mfma_f16.restype = ctypes.c_double
+    lib.zinc_peak_mfma_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.zinc_peak_hbm_read.restype = ctypes.c_int
+    lib.zinc_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.zinc_peak_hbm_copy.restype = ctypes.c_int
+    lib.zinc_peak_hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    cur = torch.cuda.current_stream()
+    sh = cur.cuda_stream
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def timed(fn, reps, warm_s=0.3):
+        # run the kernel back to back for warm_s first: the clocks ramp up
+        # under load and a cold first launch would read low
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            fn()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(reps):
+            e0.record(cur)
+            fn()
+            e1.record(cur)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        return best
+
+    out = {}
+    blocks = ncu * 8
+    res = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for shape in (16, 32):
+        flops = [0.0]
+
+        def run(shape=shape):
+            flops[0] = lib.zinc_peak_mfma_f16(shape, blocks, 16384, res.data_ptr(), sh)
+        t = timed(run, 5)
+        out[f"mfma_f16_{shape}x{shape}_tflops"] = round(flops[0] / t / 1e12, 1)
+        if shape == 16:
+            out["clock_during_mfma_loop"] = sample_clock(torch, lambda _i: run(), "the 16x16x32 MFMA-only loop", 0.5)
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
+    dst = torch.empty(nbytes // 8, dtype=torch.int32, device=dev)
+    rres = torch.empty(ncu * 16 * 256, dtype=torch.int32, device=dev)
+    t = timed(lambda: lib.zinc_peak_hbm_read(src.data_ptr(), nbytes, ncu * 16, rres.data_ptr(), sh), 5)
+    out["hbm_read_GBs"] = round(nbytes / t / 1e9, 1)
+    half = nbytes // 2
+    t = timed(lambda: lib.zinc_peak_hbm_copy(src.data_ptr(), dst.data_ptr(), half, ncu * 16, sh), 5)
+    out["hbm_copy_GBs_read_plus_write"] = round(2 * half / t / 1e9, 1)
+    del src, dst, rres, res
+    torch.cuda.empty_cache()
+    out["method"] = ("best of 5 launches each after 0.3 s of the same launches back to back, HIP events on the "
+                     "launch stream: 8 waves of MFMAs per CU with 8 independent accumulators per wave (17.6 TFLOP "
+                     "per launch); 4 GiB read and 2 GiB copied with 16-byte loads")
+    return out
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock and socket power through amdsmi in a
+    background thread while a timed region runs (every ~20 ms).  Any failure
+    leaves the record empty with the reason, and never stops the benchmark."""
+
+    def __init__(self, torch):
+        import threading
+        self.samples, self.error, self._stop = [], None, threading.Event()
+        self._thread, self._h, self._smi = None, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            want = None
+            try:
+                p = torch.cuda.get_device_properties(0)
+                want = (int(getattr(p, "pci_domain_id", 0)), int(p.pci_bus_id), int(p.pci_device_id))
+            except Exception:
+                pass
+            pick = handles[0] if len(handles) == 1 else None
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)        # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if want and (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    pick = h
+            if pick is None:
+                raise RuntimeError(f"no amdsmi device matches the HIP device ({len(handles)} seen)")
+            self._h, self._smi = pick, amdsmi
+        except Exception as e:   # noqa: BLE001 - reported in the record
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        smi = self._smi
+        clk = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)
+        pw = smi.amdsmi_get_power_info(self._h)
+        watts = pw.get("socket_power", pw.get("current_socket_power", pw.get("average_socket_power")))
+        return float(clk.get("clk", clk.get("cur_clk"))), (float(watts) if watts not in (None, "N/A") else None)
+
+    def __enter__(self):
+        import threading
+        import time as _t
+        if self._h is None:
+            return self
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:   # noqa: BLE001
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                _t.sleep(0.01)
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join(timeout=2)
+
+    def record(self, where: str):
+        if not self.samples:
+            return {"samples": 0, "where": where, "error": self.error or "no sample taken"}
+        clk = sorted(c for c, _ in self.samples)
+        pw = [w for _, w in self.samples if w is not None]
+        return {"samples": len(clk), "where": where, "gfx_mhz_median": clk[len(clk) // 2],
+                "gfx_mhz_min": clk[0], "gfx_mhz_max": clk[-1],
+                "power_w_median": (sorted(pw)[len(pw) // 2] if pw else None), "error": self.error}
+
+
+def sample_clock(torch, fn, where, seconds=1.0):
+    """The graphics clock and socket power while `fn` runs back to back."""
+    sampler = ClockSampler(torch)
+    with sampler:
+        t0, i = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            fn(i)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    return sampler.record(where)
+
+
+def call_percentiles(torch, fn, calls=50):
+    """Whole-call durations, one HIP event pair per call on the current stream:
+    median, p10 and p90 in microseconds."""
+    cur = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for i, (a, b) in enumerate(ev):
+        a.record(cur)
+        fn(i)
+        b.record(cur)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    q = lambda f: round(us[min(len(us) - 1, int(f * len(us)))], 2)
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "calls": calls}
+
+
+def headline(args, torch, peaks=None):
     import numpy as np
 
     import q4_swiglu_mlp_amd as Z
@@ -100,7 +276,9 @@ def headline(args, torch):
         Z.zinc_mlp_q4k_prefill(gwg, gwu, gwd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
 
     wall, ms = time_calls(call, args.steps, args.warmup, torch)
+    clock = sample_clock(torch, call, "back-to-back headline calls for 1 s, after the timed region")
     kern_ms = sum(ms) / len(ms)
+    pct = call_percentiles(torch, call)
     graph_us = prefill_graph_us(torch, call, y)
     flops = 6.0 * w.M * w.hidden * w.inter
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -113,12 +291,22 @@ def headline(args, torch):
                 "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "k_prefill_fused16", "kernel_ms": round(kern_ms, 5),
                 "flops_per_launch": flops}
+    if peaks and peaks.get("mfma_f16_16x16_tflops"):
+        mp = max(peaks["mfma_f16_16x16_tflops"], peaks.get("mfma_f16_32x32_tflops", 0.0))
+        roofline["frac_of_measured_peak"] = round(achieved / mp, 4)
+        roofline["measured_peak"] = mp
+    if clock.get("gfx_mhz_median"):
+        # the spec peak scaled to the clock observed during the timed calls
+        roofline["frac_at_observed_clock"] = round(
+            achieved / (PEAK_F16_TFLOPS * clock["gfx_mhz_median"] / SPEC_GFX_MHZ), 4)
     res = {
         "value": w.M * args.steps / wall,
         "ms_per_step": wall / args.steps * 1e3,
         "roofline": roofline,
         "whole_call_tflops": round(flops / (wall / args.steps) / 1e12, 2),
         "graph_replay": {"us_per_call": round(graph_us, 3), "tokens_per_s": round(w.M / (graph_us * 1e-6), 1)},
+        "call_us": pct,
+        "clock": clock,
     }
     inputs = (wg, wu, wd, x)
     return res, inputs
@@ -154,29 +342,94 @@ def prefill_graph_us(torch, call, y, replays=50):
     return (time.perf_counter() - t0) / replays * 1e6
 
 
-def cpu_baseline(inputs):
-    """The oracle as it stands, on the headline workload's full layer (256
-    tokens), on the host cores."""
+def host_cpu():
+    """The host's CPU model, sockets and the cores this process may use."""
+    model, sockets = None, set()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name") and model is None:
+                model = line.split(":", 1)[1].strip()
+            elif line.startswith("physical id"):
+                sockets.add(line.split(":", 1)[1].strip())
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"cpu_model": model, "sockets": len(sockets) or None, "nproc": nproc}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:   # noqa: BLE001
+        return None
+
+
+def _time_until(fn, min_s, max_reps):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or reps >= max_reps:
+            return reps, dt
+
+
+def cpu_baseline(inputs, full: bool = False):
+    """The oracle as it stands (numpy float64: decode + three matmuls), on the
+    host cores: the headline workload's full layer (256 tokens) repeated for
+    at least 10 s, then one call each of the other workloads' shapes (tiny,
+    decode M=1 and M=4, the 64-expert MoE) and the tiny layer on one thread.
+    ``full`` adds the headline layer on one thread (tens of seconds)."""
+    import numpy as np
+
     import oracle as O
     import q4k_synth as S
     w = S.WORKLOADS["prefill_m256"]
     wg, wu, wd, x = inputs
+    cores = blas_threads() or os.cpu_count()
+    reps, dt = _time_until(lambda: O.mlp(x, wg, wu, wd, w.hidden, w.inter), 10.0, 50)
+    res = {"value": round(reps * w.M / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"the full 4096/11008 layer, {w.M} tokens, {reps} times (numpy float64 oracle: decode + 3 "
+                     f"matmuls), {dt:.2f} s; cores = the BLAS threads numpy ran with"}
+    res.update(host_cpu())
+    other = {}
+    t = S.WORKLOADS["tiny"]
+    tw = S.layer_weights(t.seed, 0, t.hidden, t.inter)
+    tx = S.workload_x(t)
+    r, d = _time_until(lambda: O.mlp(tx, *tw, t.hidden, t.inter), 1.0, 1000)
+    other["tiny_256_768_M8_tokens_per_s"] = round(r * t.M / d, 1)
+    dw = S.WORKLOADS["decode_m4"]
+    lw = S.layer_weights(dw.seed, 0, dw.hidden, dw.inter)
+    dx = S.workload_x(dw)
+    for M in (1, 4):
+        r, d = _time_until(lambda: O.mlp(dx[:M], *lw, dw.hidden, dw.inter), 2.0, 20)
+        other[f"decode_M{M}_s_per_layer"] = round(d / r, 3)
+        other[f"decode_M{M}_32_layers_s_extrapolated"] = round(32 * d / r, 2)
+    mw = S.WORKLOADS["moe_e64"]
+    eg, eu, ed = S.expert_weights(mw.seed, mw.n_experts, mw.hidden, mw.inter)
+    mx = S.workload_x(mw)
+    ids, p = S.workload_routing(mw)
+    t0 = time.perf_counter()
+    O.moe(mx, eg, eu, ed, ids, p, mw.hidden, mw.inter)
+    d = time.perf_counter() - t0
+    other["moe_e64_top8_M512_s_per_call"] = round(d, 3)
+    other["moe_e64_top8_M512_tokens_per_s"] = round(mw.M / d, 1)
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
-    # repeat the whole layer until at least 10 s of host work is timed
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        O.mlp(x, wg, wu, wd, w.hidden, w.inter)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 50:
-            break
-    return {"value": round(reps * w.M / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full layer, {w.M} tokens, {reps} times (numpy float64 oracle: decode + 3 matmuls), "
-                      f"{dt:.2f} s"}
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            r, d = _time_until(lambda: O.mlp(tx, *tw, t.hidden, t.inter), 1.0, 1000)
+            other["tiny_tokens_per_s_one_thread"] = round(r * t.M / d, 1)
+            if full:
+                r, d = _time_until(lambda: O.mlp(x, wg, wu, wd, w.hidden, w.inter), 1.0, 3)
+                other["headline_layer_tokens_per_s_one_thread"] = round(r * w.M / d, 3)
+    except Exception as e:   # noqa: BLE001
+        other["one_thread_error"] = f"{type(e).__name__}: {e}"
+    res["other_workloads"] = other
+    return res
 
 
 def secondary(args, torch):
@@ -466,8 +719,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "moe", "block", "m2048", "staged"], default=None,
-                    help="development runs: skip the headline and the CPU baseline, run one secondary part")
+    ap.add_argument("--only", choices=["decode", "moe", "block", "m2048", "staged", "peaks", "cpu"], default=None,
+                    help="development and profiling runs: skip the headline and run one part (a secondary line, "
+                         "the measured peaks, or the full CPU oracle table including one-thread figures)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3x), the reference kernel that "
                          "scales the FETCH_SIZE/WRITE_SIZE counters to bytes")
@@ -489,11 +744,27 @@ def main():
 
     import torch
 
+    if args.only == "peaks":
+        print(json.dumps({"measured_peaks": measure_peaks(torch)}), flush=True)
+        return
+    if args.only == "cpu":
+        import q4k_synth as S
+        w = S.WORKLOADS["prefill_m256"]
+        inputs = (*S.layer_weights(w.seed, 0, w.hidden, w.inter), S.workload_x(w))
+        print(json.dumps({"cpu_baseline": cpu_baseline(inputs, full=True)}), flush=True)
+        return
     if args.only:
         print(json.dumps({"secondary": secondary(args, torch)}), flush=True)
         return
+    peaks = None
+    if not args.no_peaks:
+        try:
+            peaks = measure_peaks(torch)
+            log(f"[bench] measured peaks {peaks}")
+        except Exception as e:   # noqa: BLE001 - the peaks are context, never the headline
+            peaks = {"error": f"{type(e).__name__}: {e}"}
     log("[bench] headline: prefill 4096/11008 M=256")
-    res, inputs = headline(args, torch)
+    res, inputs = headline(args, torch, peaks)
     log(f"[bench] headline {res['value']:.1f} tok/s, kernel {res['roofline']['kernel_ms'] * 1e3:.1f} us, "
         f"{res['roofline']['achieved']} TFLOP/s")
     sec = None if args.no_secondary else secondary(args, torch)
@@ -520,6 +791,9 @@ def main():
         "cpu_baseline": cpu,
         "whole_call_tflops": res["whole_call_tflops"],
         "graph_replay": res["graph_replay"],
+        "call_us": res["call_us"],
+        "clock": res["clock"],
+        "measured_peaks": peaks,
         "secondary": sec,
     }
     print(json.dumps(line), flush=True)
