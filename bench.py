@@ -130,17 +130,25 @@ def measure_peaks(torch):
         return best
 
     out = {}
-    blocks = ncu * 8
-    res = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    # one 12-wave workgroup per CU (three waves per SIMD), each wave with eight
+    # independent accumulators
+    blocks = ncu
+    res = torch.empty(blocks * 768, dtype=torch.float32, device=dev)
     for shape in (16, 32):
         flops = [0.0]
 
-        def run(shape=shape):
-            flops[0] = lib.zinc_peak_mfma_f16(shape, blocks, 16384, res.data_ptr(), sh)
-        t = timed(run, 5)
-        out[f"mfma_f16_{shape}x{shape}_tflops"] = round(flops[0] / t / 1e12, 1)
+        def run(iters, shape=shape):
+            flops[0] = lib.zinc_peak_mfma_f16(shape, blocks, iters, res.data_ptr(), sh)
+        # burst: launches of about 1 ms, as the MLP kernels run (warm-up of a
+        # few launches only); sustained: after 0.3 s of back-to-back launches,
+        # when the clock has settled under the load
+        t = timed(lambda: run(2048), 5, warm_s=0.005)
+        out[f"mfma_f16_{shape}x{shape}_tflops_burst"] = round(flops[0] / t / 1e12, 1)
+        t = timed(lambda: run(2048), 5, warm_s=0.3)
+        out[f"mfma_f16_{shape}x{shape}_tflops_sustained"] = round(flops[0] / t / 1e12, 1)
         if shape == 16:
-            out["clock_during_mfma_loop"] = sample_clock(torch, lambda _i: run(), "the 16x16x32 MFMA-only loop", 0.5)
+            out["clock_during_mfma_loop"] = sample_clock(torch, lambda _i: run(2048), "the 16x16x32 MFMA-only loop",
+                                                         0.5)
     nbytes = 4 << 30
     src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
     dst = torch.empty(nbytes // 8, dtype=torch.int32, device=dev)
@@ -152,9 +160,10 @@ def measure_peaks(torch):
     out["hbm_copy_GBs_read_plus_write"] = round(2 * half / t / 1e9, 1)
     del src, dst, rres, res
     torch.cuda.empty_cache()
-    out["method"] = ("best of 5 launches each after 0.3 s of the same launches back to back, HIP events on the "
-                     "launch stream: 8 waves of MFMAs per CU with 8 independent accumulators per wave (17.6 TFLOP "
-                     "per launch); 4 GiB read and 2 GiB copied with 16-byte loads")
+    out["method"] = ("best of 5 launches each, HIP events on the launch stream; MFMA: 12 waves per CU, 8 "
+                     "independent accumulators per wave, launches of about 1 ms, timed after a few launches (burst) "
+                     "and after 0.3 s of back-to-back launches (sustained); HBM: 4 GiB read and 2 GiB copied with "
+                     "16-byte loads, after 0.3 s of the same launches")
     return out
 
 
@@ -291,8 +300,8 @@ def headline(args, torch, peaks=None):
                 "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "k_prefill_fused16", "kernel_ms": round(kern_ms, 5),
                 "flops_per_launch": flops}
-    if peaks and peaks.get("mfma_f16_16x16_tflops"):
-        mp = max(peaks["mfma_f16_16x16_tflops"], peaks.get("mfma_f16_32x32_tflops", 0.0))
+    if peaks and peaks.get("mfma_f16_16x16_tflops_burst"):
+        mp = max(peaks["mfma_f16_16x16_tflops_burst"], peaks.get("mfma_f16_32x32_tflops_burst", 0.0))
         roofline["frac_of_measured_peak"] = round(achieved / mp, 4)
         roofline["measured_peak"] = mp
     if clock.get("gfx_mhz_median"):
@@ -457,25 +466,29 @@ def m2048_lines(args, torch, np, Z, S, dev, t):
     """The large prefill: 2048 tokens through 32 independent 4096/11008 layers
     (seed 2, x sd 0.5), each layer one call; whole-call time per layer."""
     w = S.WORKLOADS["prefill_m2048"]
-    layers = [tuple(t(a) for a in S.layer_weights(w.seed, l, w.hidden, w.inter)) for l in range(w.layers)]
+    n_layers = min(args.layers, w.layers)
+    layers = [tuple(t(a) for a in S.layer_weights(w.seed, l, w.hidden, w.inter)) for l in range(n_layers)]
     gx = t(S.workload_x(w))
     y = torch.empty((w.M, w.hidden), dtype=torch.float16, device=dev)
     ws = torch.empty(Z.prefill_workspace_size(w.M, w.hidden, w.inter), dtype=torch.uint8, device=dev)
 
     def call(i):
-        lg, lu, ld = layers[i % w.layers]
+        lg, lu, ld = layers[i % n_layers]
         Z.zinc_mlp_q4k_prefill(lg, lu, ld, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
 
-    steps = 3 * w.layers
-    wall, _ = time_calls(call, steps, w.layers, torch)
+    steps = 3 * n_layers
+    wall, ms = time_calls(call, steps, n_layers, torch)
     per = wall / steps
+    kern = sum(ms) / len(ms)   # the fused kernel of each call (HIP events on its stream)
     flops = 6.0 * w.M * w.hidden * w.inter
     out = [{
-        "workload": "prefill 4096/11008 M=2048, 32-layer sweep (seed 2)",
+        "workload": f"prefill 4096/11008 M=2048, {n_layers}-layer sweep (seed 2)",
         "tokens_per_s": round(w.M / per, 1),
         "us_per_layer": round(per * 1e6, 2),
         "whole_call_tflops": round(flops / per / 1e12, 2),
         "whole_call_mfma_frac": round(flops / per / 1e12 / PEAK_F16_TFLOPS, 4),
+        "fused_kernel_us": round(kern * 1e3, 2),
+        "fused_kernel_mfma_frac": round(flops / (kern * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
     }]
     log(f"[bench] {out[-1]}")
     del layers
@@ -596,7 +609,8 @@ def decode_lines(args, torch, np, Z, S, dev, t):
     out = []
     # decode: 32 independent layers so the 2.4 GB of weights stream from HBM
     w1 = S.WORKLOADS["decode_m1"]
-    layers = [tuple(t(a) for a in S.layer_weights(w1.seed, l, w1.hidden, w1.inter)) for l in range(w1.layers)]
+    layers = [tuple(t(a) for a in S.layer_weights(w1.seed, l, w1.hidden, w1.inter))
+              for l in range(min(args.layers, w1.layers))]
     layer_bytes = 2 * q4k_bytes(w1.inter, w1.hidden) + q4k_bytes(w1.hidden, w1.inter)
     for name in ("decode_m1", "decode_m4"):
         w = S.WORKLOADS[name]
@@ -608,13 +622,13 @@ def decode_lines(args, torch, np, Z, S, dev, t):
             lg, lu, ld = layers[i % len(layers)]
             Z.zinc_mlp_q4k_decode(lg, lu, ld, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
 
-        steps = 32 * 10
-        wall, ms = time_calls(call, steps, 32, torch)
+        steps = len(layers) * 10
+        wall, ms = time_calls(call, steps, len(layers), torch)
         per_layer = wall / steps
         kern_ms = sum(ms) / steps   # the timed kernels of one call (gate+up and down)
         graph_us = decode_graph_us(torch, Z, layers, w, gx, y, ws)
         out.append({
-            "workload": f"decode 4096/11008 M={w.M}, 32-layer sweep",
+            "workload": f"decode 4096/11008 M={w.M}, {len(layers)}-layer sweep",
             "tokens_per_s_per_layer": round(w.M / per_layer, 1),
             "us_per_layer": round(per_layer * 1e6, 3),
             "hbm_GBs_whole_call": round(layer_bytes / per_layer / 1e9, 1),
@@ -723,6 +737,8 @@ def main():
                     help="development and profiling runs: skip the headline and run one part (a secondary line, "
                          "the measured peaks, or the full CPU oracle table including one-thread figures)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
+    ap.add_argument("--layers", type=int, default=32,
+                    help="layers of the 32-layer sweeps (decode, 2048-token prefill); fewer for profiling runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3x), the reference kernel that "
                          "scales the FETCH_SIZE/WRITE_SIZE counters to bytes")

@@ -514,7 +514,8 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
     panel(std::integral_constant<int, 0>{});
     if constexpr (NP > 1) panel(std::integral_constant<int, 1>{});
     if constexpr (NP > 2) panel(std::integral_constant<int, 2>{});
-    static_assert(NP <= 3, "panels per chunk");
+    if constexpr (NP > 3) panel(std::integral_constant<int, 3>{});
+    static_assert(NP <= 4, "panels per chunk");
     // min correction: lane half h covers block 2g + h (block-aligned strip means)
 #pragma unroll
     for (int g = 0; g < (NB + 1) / 2; ++g) {
@@ -564,6 +565,7 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
       panel(std::integral_constant<int, 0>{});
       if constexpr (NP > 1) panel(std::integral_constant<int, 1>{});
       if constexpr (NP > 2) panel(std::integral_constant<int, 2>{});
+      if constexpr (NP > 3) panel(std::integral_constant<int, 3>{});
 #pragma unroll
       for (int g = 0; g < (NB + 1) / 2; ++g) {
         if (2 * g < nblk) {
@@ -616,6 +618,7 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
       panel(std::integral_constant<int, 0>{});
       if constexpr (NP > 1) panel(std::integral_constant<int, 1>{});
       if constexpr (NP > 2) panel(std::integral_constant<int, 2>{});
+      if constexpr (NP > 3) panel(std::integral_constant<int, 3>{});
       // min term +m per block: +32 m_j against the 32-row means, block j of
       // group 2g + h sits in panel 4(2g + h) + j/2 - OFF (A for even j);
       // blocks outside the chunk's panels meet zero means and take 0

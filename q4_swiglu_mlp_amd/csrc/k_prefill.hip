@@ -16,6 +16,7 @@
 // Both configurations store their partials in token quads, P[chunk][t/4][n][t%4],
 // which k_reduce_quads sums.  The plan is a function of (M, hidden, inter)
 // alone.
+#include "fused128.hpp"
 #include "fused16.hpp"
 #include "launch.hpp"
 #include "util_kernels.hpp"
@@ -78,6 +79,29 @@ __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused
   __syncthreads();
   const OutQuads out{P, Mpad, H, out_scale, chunk, tile * 64};
   fused_unit16<ICMAX>(wg, wu, wd, H, I, xg, tok, min(64, M - tile * 64), r0, r1, inter_scale, out, sm);
+}
+
+// The 128-token unit (fused128.hpp, two 128-row passes per chunk) over
+// (token tiles) x (chunks), same XCD-aware unit order.
+template <int NPASS>
+__global__ __launch_bounds__(512) void k_prefill_fused128(
+    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, const uint8_t* __restrict__ wd, int H, int I,
+    const uint8_t* __restrict__ xg, int M, _Float16* __restrict__ P, int Mpad, float inter_scale, float out_scale,
+    int n_tiles, int n_chunks) {
+  __shared__ __attribute__((aligned(16))) Fused128Smem<NPASS> sm;
+  __shared__ int tok[128];
+  const int bid = blockIdx.x;
+  const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
+  const int tile = rem >> 3;
+  const int chunk = grp * 8 + (rem & 7);
+  if (chunk >= n_chunks) return;
+  const int npan = I / 64;
+  const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
+  const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
+  if (threadIdx.x < 128) tok[threadIdx.x] = min(tile * 128 + (int)threadIdx.x, M);   // M: the zero token
+  __syncthreads();
+  const OutQuads out{P, Mpad, H, out_scale, chunk, tile * 128};
+  fused_unit128<NPASS>(wg, wu, wd, H, I, xg, tok, min(128, M - tile * 128), r0, r1, inter_scale, out, sm);
 }
 
 // The staged comparison baseline: the same units in two launches, phase 1
@@ -171,13 +195,17 @@ __global__ __launch_bounds__(256) void k_reduce_quads(const _Float16* __restrict
 }
 
 struct Plan {
-  char cfg;      // 'C' or 'D'
+  char cfg;      // 'C', 'D' or 'E'
   int MT, ICMAX;
   int n_tiles, n_chunks;
   int Mpad;
 };
 
 int round_up(int a, int b) { return (a + b - 1) / b * b; }
+
+// From this many tokens the 128-token unit E (two 128-row passes per chunk)
+// takes over from C.
+constexpr int kUnitEMinTokens = 512;
 
 // Units run one per CU, and the unit order below pins chunk c to XCD c % 8,
 // whose 32 CUs run that XCD's units: a plan takes the fewest rounds k for
@@ -195,12 +223,21 @@ Plan make_plan(int M, int H, int I, bool force_d) {
   (void)H;
   Plan p;
   const int tiles64 = (M + 63) / 64;
-  p.cfg = (tiles64 <= 4 || force_d) ? 'D' : 'C';
-  p.MT = 64;
-  p.ICMAX = (p.cfg == 'D') ? 192 : 384;
+  p.cfg = (tiles64 <= 4 || force_d) ? 'D' : (M >= kUnitEMinTokens ? 'E' : 'C');
+  p.MT = (p.cfg == 'E') ? 128 : 64;
+  p.ICMAX = (p.cfg == 'D') ? 192 : (p.cfg == 'E') ? 256 : 384;
   const int npan = I / 64;
   const int min_chunks = (npan + p.ICMAX / 64 - 1) / (p.ICMAX / 64);
   p.n_tiles = (M + p.MT - 1) / p.MT;
+  if (p.cfg == 'E') {
+    // whole 256-row chunks: the fewest partials.  Smaller chunks filling whole
+    // rounds (48 of 3-4 panels at M = 2048 instead of 43 of 4) measured no
+    // faster: the units are dispatched as CUs free up, so the total work sets
+    // the time, and the extra partials slowed the reduce.
+    p.n_chunks = min_chunks;
+    p.Mpad = round_up(p.n_tiles * p.MT, 64);
+    return p;
+  }
   const int k = (((min_chunks + 7) / 8) * p.n_tiles + 31) / 32;   // fewest rounds
   const int most = 8 * ((32 * k) / p.n_tiles);    // chunks that fit k rounds
   const int per = (npan + most - 1) / most;        // panels of the largest unit
@@ -236,7 +273,7 @@ void launch_cfg16(const Plan& p, const void* wg, const void* wu, const void* wd,
 size_t partial_bytes(const Plan& p, int H) { return ((size_t)p.n_chunks * H * p.Mpad * sizeof(_Float16) + 255) & ~(size_t)255; }
 
 size_t staged_x_bytes(const Plan& p, int H) {
-  return (p.cfg == 'D') ? x16_staged_bytes(p.n_tiles * p.MT, H) : 0;
+  return (p.cfg == 'D' || p.cfg == 'E') ? x16_staged_bytes(p.n_tiles * p.MT, H) : 0;
 }
 
 // A plan's own need is not monotone in M (adding a token tile can lower the
@@ -315,12 +352,17 @@ hipError_t launch_prefill(const void* wg, const void* wu, const void* wd, int hi
   const _Float16* rh = static_cast<const _Float16*>(res);
   _Float16* yh = static_cast<_Float16*>(y);
   uint8_t* xg = static_cast<uint8_t*>(ws) + partial_bytes(p, hidden);
-  if (p.cfg == 'D')
+  if (p.cfg == 'D' || p.cfg == 'E')
     hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream,
                        static_cast<const _Float16*>(x), hidden, M, xg);
   timing_begin(stream);   // the timed region is the fused kernel alone
   if (p.cfg == 'D')
     launch_cfg16<192>(p, wg, wu, wd, hidden, inter, x, M, P, xg, inter_scale, out_scale, stream);
+  else if (p.cfg == 'E')
+    hipLaunchKernelGGL((k_prefill_fused128<2>), dim3((p.n_chunks + 7) / 8 * 8 * p.n_tiles), dim3(512), 0, stream,
+                       static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
+                       static_cast<const uint8_t*>(wd), hidden, inter, xg, M, P, p.Mpad, inter_scale, out_scale,
+                       p.n_tiles, p.n_chunks);
   else
     launch_cfg<2, 1, 384>(p, wg, wu, wd, hidden, inter, x, M, P, inter_scale, out_scale, stream);
   timing_end(stream);

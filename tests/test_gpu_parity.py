@@ -96,7 +96,20 @@ def test_prefill_other_shapes(H, I):
     assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill H={H} I={I}")
 
 
-@pytest.mark.parametrize("M", [257, 320, 700])
+@pytest.mark.parametrize("H,I,M", [(512, 1536, 512), (512, 1536, 600), (768, 1280, 1000), (256, 2304, 530),
+                                   (512, 256, 640), (256, 2816, 2048)])
+def test_prefill_unit_e(H, I, M):
+    # from 512 tokens the plan takes the 128-token unit (two 128-row passes per
+    # chunk of at most 256 rows): several tiles and chunks, ragged token tails,
+    # chunks of two panels (one pass) and of two or three panels (the second
+    # pass half idle, 2816 / 64 = 44 panels in 16 chunks)
+    wg, wu, wd, x = _rand_mlp(300 + M + I, H, I, M)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
+    a, b = shifts_for(y_ref, h_ref)
+    assert_parity(prefill(wg, wu, wd, H, I, x, a, b), y_ref, f"prefill unit E H={H} I={I} M={M}")
+
+
+@pytest.mark.parametrize("M", [257, 320, 500])
 def test_prefill_unit_c(M):
     # past four 64-token tiles the plan takes the 32x32x16 unit with 384-row
     # chunks (unit C): several tiles, chunks and a ragged tail

@@ -14,8 +14,8 @@ stay inside the tolerance.  These inputs cannot hide one:
     cancellation, which tests the fp16 operands of the -dmin*m term and the
     fp16 split-K partials where the uniform recipe does not.
 Each probe runs on every unit the default plans use: the 64-token 16x16x32
-prefill unit (up to 256 tokens), the 32x32x16 unit with 384-row chunks (past
-256 tokens), the M = 1 row kernels, the 2 <= M <= 8 MFMA decode kernels and
+prefill unit (up to 256 tokens), the 32x32x16 unit with 384-row chunks (257 to
+511 tokens), the 128-token unit (from 512 tokens), the M = 1 row kernels, the 2 <= M <= 8 MFMA decode kernels and
 the MoE's 80-token unit (an expert with more than 80 routed rows)."""
 from __future__ import annotations
 
@@ -82,6 +82,7 @@ def _probe_inputs(probe, H, I, M, seed):
 PATHS = {
     "prefill_unit_d": ("prefill", 512, 1536, 200),    # 64-token 16x16x32 unit, 4 tiles, ragged tail
     "prefill_unit_c": ("prefill", 512, 1536, 330),    # 32x32x16 unit, 384-row chunks
+    "prefill_unit_e": ("prefill", 512, 1536, 600),    # 128-token unit, two 128-row passes per chunk
     "decode_rows_m1": ("decode", 1024, 2816, 1),      # row-streaming kernels
     "decode_mfma_m4": ("decode", 1024, 2816, 4),      # 16x16x32 MFMA decode
     "decode_mfma_m7": ("decode", 1024, 2816, 7),      # two token groups, the second ragged
