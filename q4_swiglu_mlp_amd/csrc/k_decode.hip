@@ -417,6 +417,145 @@ hipError_t launch_rows_k(const void* W0, const void* W1, int K, int N, const _Fl
   return launch_rows<MM, GATEUP, 4>(W0, W1, K, N, x, M, out, scale, res, res_scale, gamma, eps, stream);
 }
 
+// The down pass of one token with each row's contraction split over S waves
+// (S = ceil(chunks / 64), chunks = inter / 64), so a lane holds the activation
+// of one 64-weight chunk in registers and a wave's work per row is one chunk
+// per lane.  Twelve waves per workgroup take R = 12 / S rows at a time (wave w:
+// row slot w / S, segment w % S); the S partial sums of a row meet in LDS and
+// are added in segment order, so the result does not depend on scheduling.
+// Persistent workgroups walk the row groups grid-stride with the next group's
+// chunk loaded while the current one is computed.  Against whole rows per wave
+// (three chunks per lane at inter = 11008), a wave's latency chain per row is a
+// third as long and the kernel needs a third of the registers.
+template <int S>
+struct SplitShape {
+  static constexpr int R = 12 / S;                 // rows per group
+  static constexpr int WAVES = R * S;
+  static constexpr int THREADS = 64 * WAVES;
+};
+
+template <int S>
+__global__ __launch_bounds__(SplitShape<S>::THREADS) void k_decode_down_split(const uint8_t* __restrict__ W, int K,
+                                                                             int N, const _Float16* __restrict__ hin,
+                                                                             _Float16* out, float scale,
+                                                                             const _Float16* res, float res_scale) {
+  using SH = SplitShape<S>;
+  constexpr int R = SH::R, THREADS = SH::THREADS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char ds_smem[];
+  const int nb = K / QK;
+  const int Q = 4 * nb;                              // chunks per row
+  _Float16* xs = reinterpret_cast<_Float16*>(ds_smem);
+  float* X2 = reinterpret_cast<float*>(ds_smem + (size_t)K * 2);          // [2*Q] sub-block sums
+  float* part = X2 + 2 * Q;                                                 // [2][R][S] partial sums
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rs = wave / S, seg = wave - rs * S;
+  const NibbleK nk = nibble_consts();
+  const size_t row_bytes = (size_t)nb * BLOCK_BYTES;
+  const int q = 64 * seg + lane;                      // this lane's chunk
+  const bool has = q < Q;
+  const int qc = has ? q : 0;
+  const int cq = qc & 3;
+  const size_t boff = (size_t)(qc >> 2) * BLOCK_BYTES, qoff = boff + 16 + 32 * (qc & 3);
+  const int ngroups = (N + R - 1) / R;
+
+  auto load_row = [&](int g, Chunk& c) __attribute__((always_inline)) {
+    int j = g * R + rs;
+    j = j < N ? j : N - 1;                            // past the end: re-read the last row (never used)
+    const uint8_t* row = W + (size_t)j * row_bytes;
+    c.hdr = *reinterpret_cast<const uint4*>(row + boff);
+    c.q0 = *reinterpret_cast<const uint4*>(row + qoff);
+    c.q1 = *reinterpret_cast<const uint4*>(row + qoff + 16);
+  };
+  // the activation loads first, then the first group's weights
+  constexpr int NXG = (DR_KMAX / 8 + THREADS - 1) / THREADS;
+  const int nxg = K / 8;
+  uint4 xv[NXG];
+#pragma unroll
+  for (int u = 0; u < NXG; ++u) {
+    const int gi = tid + u * THREADS;
+    xv[u] = (gi < nxg) ? *reinterpret_cast<const uint4*>(hin + 8 * gi) : make_uint4(0, 0, 0, 0);
+  }
+  int g = blockIdx.x;
+  Chunk cur, nxt;
+  load_row(g < ngroups ? g : 0, cur);
+  // stage: groups of four with the middle two swapped; fp32 sums of every 32
+#pragma unroll
+  for (int u = 0; u < NXG; ++u) {
+    const int gi = tid + u * THREADS;
+    const uint4 v = xv[u];
+    if (gi < nxg)
+      *reinterpret_cast<uint4*>(xs + 8 * gi) =
+          make_uint4((v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
+                     (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u));
+    const half8 hv = __builtin_bit_cast(half8, v);
+    float s8 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8 += (float)hv[e];
+    s8 += dpp_f<0xB1>(s8);
+    s8 += dpp_f<0x4E>(s8);
+    if (gi < nxg && (gi & 3) == 0) X2[gi >> 2] = s8;
+  }
+  __syncthreads();
+  uint4 xr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const uint4*>(xs + 64 * qc + 8 * i);
+  const float xlo = X2[2 * qc], xhi = X2[2 * qc + 1];
+
+  for (int it = 0; g < ngroups; ++it, g += gridDim.x) {
+    load_row(g + (int)gridDim.x < ngroups ? g + (int)gridDim.x : g, nxt);
+    float acc = has ? chunk_dot_reg(cur, cq, xr, xlo, xhi, nk) : 0.0f;
+    acc = wave_sum_to_lane63(acc);
+    float* pb = part + (it & 1) * R * S;
+    if (lane == 63) pb[rs * S + seg] = acc;
+    __syncthreads();
+    if (tid < R) {
+      const int j = g * R + tid;
+      if (j < N) {
+        float v = 0.0f;
+#pragma unroll
+        for (int k = 0; k < S; ++k) v += pb[tid * S + k];
+        v *= scale;
+        if (res) v += (float)res[j] * res_scale;   // may be out itself: read, then written, here
+        out[j] = (_Float16)v;
+      }
+    }
+    cur = nxt;
+  }
+}
+
+template <int S>
+hipError_t launch_down_split(const void* W, int K, int N, const _Float16* h, _Float16* out, float scale,
+                             const _Float16* res, float res_scale, hipStream_t stream) {
+  using SH = SplitShape<S>;
+  const size_t smem = (size_t)K * 2 + (size_t)2 * (4 * (K / QK)) * 4 + (size_t)2 * SH::R * S * 4;
+  static size_t attr_set = 0;
+  if (smem > attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_down_split<S>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = smem;
+  }
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_down_split<S>, SH::THREADS, smem);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  const int ngroups = (N + SH::R - 1) / SH::R;
+  const int grid = std::max(1, std::min(cu_count() * per_cu, ngroups));
+  hipLaunchKernelGGL((k_decode_down_split<S>), dim3(grid), dim3(SH::THREADS), smem, stream,
+                     static_cast<const uint8_t*>(W), K, N, h, out, scale, res, res_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_split_k(const void* W, int K, int N, const _Float16* h, _Float16* out, float scale,
+                               const _Float16* res, float res_scale, hipStream_t stream) {
+  const int Q = 4 * (K / QK);
+  if (Q <= 64) return launch_down_split<1>(W, K, N, h, out, scale, res, res_scale, stream);
+  if (Q <= 128) return launch_down_split<2>(W, K, N, h, out, scale, res, res_scale, stream);
+  if (Q <= 192) return launch_down_split<3>(W, K, N, h, out, scale, res, res_scale, stream);
+  return launch_down_split<4>(W, K, N, h, out, scale, res, res_scale, stream);
+}
+
 }  // namespace
 
 size_t decode_workspace_bytes(int M, int hidden, int inter) {
@@ -449,8 +588,8 @@ hipError_t launch_decode(const void* wg, const void* wu, const void* wd, int hid
   timing_end(stream);
   if (e != hipSuccess) return e;
   timing_begin(stream);
-  e = launch_rows_k<1, false>(wd, nullptr, inter, hidden, hbuf, M, static_cast<_Float16*>(y), dn_scale,
-                              static_cast<const _Float16*>(res), res_scale, nullptr, 0.0f, stream);
+  e = launch_down_split_k(wd, inter, hidden, hbuf, static_cast<_Float16*>(y), dn_scale,
+                          static_cast<const _Float16*>(res), res_scale, stream);
   timing_end(stream);
   return e;
 }
