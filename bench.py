@@ -147,8 +147,12 @@ def measure_peaks(torch):
         t = timed(lambda: run(2048), 5, warm_s=0.3)
         out[f"mfma_f16_{shape}x{shape}_tflops_sustained"] = round(flops[0] / t / 1e12, 1)
         if shape == 16:
-            out["clock_during_mfma_loop"] = sample_clock(torch, lambda _i: run(2048), "the 16x16x32 MFMA-only loop",
-                                                         0.5)
+            out["clock_during_mfma_loop"] = sample_clock(torch, lambda _i: run(2048),
+                                                         "the 16x16x32 MFMA-only loop for 2 s, the last 0.8 s")
+            # the clock the sustained rate implies: one 16x16x32 MFMA (16384
+            # flops) per 16 cycles on each of the four SIMDs of every CU
+            out["clock_implied_by_mfma_rate_mhz"] = round(
+                out["mfma_f16_16x16_tflops_sustained"] * 1e12 / (ncu * 4 * 1024) / 1e6, 1)
     nbytes = 4 << 30
     src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
     dst = torch.empty(nbytes // 8, dtype=torch.int32, device=dev)
@@ -167,10 +171,83 @@ def measure_peaks(torch):
     return out
 
 
+def measure_issue_probes(torch):
+    """Two probes of what a SIMD can issue (libzinc_peaks.so), timed like the
+    peaks: (1) 16x16x32 MFMAs with kv independent packed-fp16 FMAs per MFMA,
+    issued by the same wave or by a second wave on the SIMD; (2) the fused
+    prefill unit's phase-1 loop (Q4_K decode in registers, B operands from
+    LDS, gate and up MFMAs) on L2-resident weights, whole and with parts
+    removed.  Times are per MFMA and SIMD, and as a fraction of the MFMA-only
+    rate of probe (1) at kv = 0."""
+    import ctypes
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.zinc_peak_mfma_valu.restype = ctypes.c_double
+    lib.zinc_peak_mfma_valu.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.zinc_peak_decode_loop.restype = ctypes.c_double
+    lib.zinc_peak_decode_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    import numpy as np
+    import q4k_synth as S
+    dev = torch.device("cuda:0")
+    cur = torch.cuda.current_stream()
+    sh = cur.cuda_stream
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(ncu * 768, dtype=torch.float32, device=dev)
+
+    def per_mfma_ns(fn, reps=5):
+        n = [0.0]
+
+        def run():
+            n[0] = fn()
+            if n[0] <= 0:
+                raise RuntimeError("probe launch failed")
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            run()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(reps):
+            e0.record(cur)
+            run()
+            e1.record(cur)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e6)
+        return best / n[0]
+
+    res = {"mfma_with_valu": {}, "phase1_loop": {}}
+    base = None
+    for same in (1, 0):
+        for kv in range(5):
+            ns = per_mfma_ns(lambda same=same, kv=kv: lib.zinc_peak_mfma_valu(same, kv, ncu, 4096, out.data_ptr(), sh))
+            base = ns if (same, kv) == (1, 0) else base
+            res["mfma_with_valu"][f"{'same_wave' if same else 'second_wave'}_kv{kv}"] = {
+                "ns_per_mfma": round(ns, 3), "mfma_rate_frac": round(base / ns, 3)}
+    rng = np.random.default_rng(11)
+    nblk = 16
+    wg = torch.from_numpy(S.gen_q4k_blob(rng, 192, nblk * 256)).to(dev)
+    wu = torch.from_numpy(S.gen_q4k_blob(rng, 192, nblk * 256)).to(dev)
+    names = {0: "whole", 2: "no_decode", 4: "no_weight_loads", 5: "no_loads_b_in_registers"}
+    for ng in (4, 8):
+        for var in (0, 2, 4, 5):
+            ns = per_mfma_ns(lambda ng=ng, var=var: lib.zinc_peak_decode_loop(
+                ng, var, wg.data_ptr(), wu.data_ptr(), nblk, 64, ncu, out.data_ptr(), sh))
+            res["phase1_loop"][f"{16 * ng}_tokens_{names[var]}"] = {"ns_per_mfma": round(ns, 3),
+                                                                   "mfma_rate_frac": round(base / ns, 3)}
+    res["method"] = ("one workgroup per CU (8 waves for probe 1; 12 waves for 64 tokens and 8 for 128 in probe 2); "
+                     "best of 5 launches after 0.2 s of back-to-back launches; ns per MFMA issued on one SIMD; "
+                     "mfma_rate_frac = the MFMA-only loop's ns per MFMA / this one's")
+    del out, wg, wu
+    return res
+
+
 class ClockSampler:
     """Samples the GPU's graphics clock and socket power through amdsmi in a
-    background thread while a timed region runs (every ~20 ms).  Any failure
-    leaves the record empty with the reason, and never stops the benchmark."""
+    background thread while a timed region runs (every ~10 ms).  Any failure
+    leaves the record empty with the reason, and never stops the benchmark.
+    The driver's figures lag the load by up to about a second (a sampler
+    started with the load has read the idle clock throughout), so record()
+    keeps only the samples taken after `settle_s`."""
 
     def __init__(self, torch):
         import threading
@@ -214,7 +291,7 @@ class ClockSampler:
         def loop():
             while not self._stop.is_set():
                 try:
-                    self.samples.append(self._read())
+                    self.samples.append((_t.perf_counter(), *self._read()))
                 except Exception as e:   # noqa: BLE001
                     self.error = f"{type(e).__name__}: {e}"
                     return
@@ -228,18 +305,21 @@ class ClockSampler:
         if self._thread:
             self._thread.join(timeout=2)
 
-    def record(self, where: str):
+    def record(self, where: str, settle_s: float = 0.0):
         if not self.samples:
             return {"samples": 0, "where": where, "error": self.error or "no sample taken"}
-        clk = sorted(c for c, _ in self.samples)
-        pw = [w for _, w in self.samples if w is not None]
-        return {"samples": len(clk), "where": where, "gfx_mhz_median": clk[len(clk) // 2],
+        t0 = self.samples[0][0]
+        kept = [(c, w) for t, c, w in self.samples if t - t0 >= settle_s] or [s[1:] for s in self.samples[-1:]]
+        clk = sorted(c for c, _ in kept)
+        pw = [w for _, w in kept if w is not None]
+        return {"samples": len(clk), "where": where, "after_s": settle_s, "gfx_mhz_median": clk[len(clk) // 2],
                 "gfx_mhz_min": clk[0], "gfx_mhz_max": clk[-1],
                 "power_w_median": (sorted(pw)[len(pw) // 2] if pw else None), "error": self.error}
 
 
-def sample_clock(torch, fn, where, seconds=1.0):
-    """The graphics clock and socket power while `fn` runs back to back."""
+def sample_clock(torch, fn, where, seconds=2.0, settle_s=1.2):
+    """The graphics clock and socket power while `fn` runs back to back, from
+    the samples taken after the first `settle_s` seconds."""
     sampler = ClockSampler(torch)
     with sampler:
         t0, i = time.perf_counter(), 0
@@ -249,7 +329,7 @@ def sample_clock(torch, fn, where, seconds=1.0):
             if i % 64 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
-    return sampler.record(where)
+    return sampler.record(where, settle_s)
 
 
 def call_percentiles(torch, fn, calls=50):
@@ -285,7 +365,7 @@ def headline(args, torch, peaks=None):
         Z.zinc_mlp_q4k_prefill(gwg, gwu, gwd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
 
     wall, ms = time_calls(call, args.steps, args.warmup, torch)
-    clock = sample_clock(torch, call, "back-to-back headline calls for 1 s, after the timed region")
+    clock = sample_clock(torch, call, "back-to-back headline calls for 2 s after the timed region, the last 0.8 s")
     kern_ms = sum(ms) / len(ms)
     pct = call_percentiles(torch, call)
     graph_us = prefill_graph_us(torch, call, y)
@@ -761,7 +841,8 @@ def main():
     import torch
 
     if args.only == "peaks":
-        print(json.dumps({"measured_peaks": measure_peaks(torch)}), flush=True)
+        print(json.dumps({"measured_peaks": measure_peaks(torch), "issue_probes": measure_issue_probes(torch)}),
+              flush=True)
         return
     if args.only == "cpu":
         import q4k_synth as S

@@ -9,16 +9,29 @@
 //   zinc_peak_hbm_read   streams a buffer with 16-byte loads, four in flight per
 //                        thread, grid-stride; one 4-byte result per thread
 //   zinc_peak_hbm_copy   the same loads, each stored to a second buffer
+//   zinc_peak_mfma_valu  how much independent VALU work hides behind 16x16x32
+//                        MFMAs: every step is one MFMA and `kv` packed fp16
+//                        FMAs, issued by the same wave, or by a second wave on
+//                        the same SIMD
+//   zinc_peak_decode_loop  the fused prefill unit's phase-1 inner loop (Q4_K
+//                        decode in registers, B operands from LDS, 16x16x32
+//                        MFMAs for gate and up) on L2-resident weights, with
+//                        4 or 8 token groups per decoded operand, and with
+//                        parts removed (the weight loads, the LDS reads, the
+//                        decode) to price each
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
 
+#include "../csrc/fused16.hpp"
+
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+using zinc::half8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half2p __attribute__((ext_vector_type(2)));
 
 // 768 threads (12 waves, three per SIMD): with a register budget of 168 the
 // accumulators stay in plain VGPRs (a 256-thread bound lets the compiler move
@@ -87,6 +100,168 @@ __global__ __launch_bounds__(256) void k_hbm_copy(const uint4* __restrict__ src,
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+// MODE 0: every step one MFMA and KV VALU in the same wave; MODE 1: waves
+// 0-3 of each 8-wave workgroup issue the MFMAs and waves 4-7 the VALU work
+// (one of each per SIMD).  Operands are registers only.
+template <int MODE, int KV>
+__global__ __launch_bounds__(512) void k_mfma_valu(int iters, float* __restrict__ out) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  half8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (_Float16)(0.001f * (float)((tid + e) & 7));
+    b[e] = (_Float16)(0.002f * (float)e);
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  half2p v[8];
+  const half2p sc = {(_Float16)0.999f, (_Float16)1.001f}, cc = {(_Float16)0.001f, (_Float16)-0.001f};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = half2p{(_Float16)(0.1f * k), (_Float16)(tid & 3)};
+  const bool do_mfma = MODE == 0 || wave < 4;
+  const bool do_valu = KV > 0 && (MODE == 0 || wave >= 4);
+  if (do_mfma && do_valu) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[k], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < KV; ++j) v[(k + j) & 7] = __builtin_elementwise_fma(v[(k + j) & 7], sc, cc);
+      }
+    }
+  } else if (do_mfma) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[k], 0, 0, 0);
+    }
+  } else if (do_valu) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int j = 0; j < KV; ++j) v[(k + j) & 7] = __builtin_elementwise_fma(v[(k + j) & 7], sc, cc);
+    }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r += acc[k][0] + (float)v[k][0] + (float)v[k][1];
+  out[(size_t)blockIdx.x * 512 + tid] = r;
+}
+
+// The phase-1 loop of the fused unit (the lane layout, decode, scales and
+// issue pattern of fused16.hpp) over nblk blocks, repeated `reps` times, with
+// NG 16-token groups per decoded operand and WAVES waves of 16 rows each.
+// Every workgroup reads the same rows (L2-resident); the activation column
+// sits in LDS unchanged.  VAR: 0 as in the kernel; 2 without the decode (a
+// fixed A operand); 4 without the weight loads (the quant words change in
+// registers); 5 as 4 and with the B operands held in registers.
+template <int NG, int WAVES, int VAR>
+__global__ __launch_bounds__(64 * WAVES) void k_decode_loop(const uint8_t* __restrict__ wg,
+                                                            const uint8_t* __restrict__ wu, int nblk, int reps,
+                                                            float* __restrict__ out) {
+  using namespace zinc;
+  constexpr int XS = 264;
+  __shared__ __attribute__((aligned(16))) _Float16 xs[NG * 16 * XS];
+  for (int i = threadIdx.x; i < NG * 16 * XS; i += 64 * WAVES) xs[i] = (_Float16)(0.001f * (float)(i & 15));
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, o = lane >> 4, sel = (o >> 1) & 1;
+  const NibbleK nk = nibble_consts_s();
+  const uint32_t rowb = (uint32_t)nblk * BLOCK_BYTES;
+  const uint32_t wrow_off = (uint32_t)(wave * 16 + r) * rowb;
+  f32x4_16 accg[NG], accu[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) accg[g][e] = accu[g][e] = 0.0f;
+  u32x4_16 hg = *reinterpret_cast<const u32x4_16*>(wg + wrow_off);
+  u32x4_16 hu = *reinterpret_cast<const u32x4_16*>(wu + wrow_off);
+  u32x4_16 qg0 = *reinterpret_cast<const u32x4_16*>(wg + (wrow_off + 16 + 16 * o));
+  u32x4_16 qu0 = *reinterpret_cast<const u32x4_16*>(wu + (wrow_off + 16 + 16 * o));
+  u32x4_16 qg1 = *reinterpret_cast<const u32x4_16*>(wg + (wrow_off + 80 + 16 * o));
+  u32x4_16 qu1 = *reinterpret_cast<const u32x4_16*>(wu + (wrow_off + 80 + 16 * o));
+  const int xlane = r * XS + o * 8;
+  half8 bfix[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) bfix[g] = *reinterpret_cast<const half8*>(xs + xlane + g * 16 * XS);
+  const half8 afix = bfix[0];
+  for (int rep = 0; rep < reps; ++rep) {
+    for (int kb = 0; kb < nblk; ++kb) {
+      const int kn = (kb + 1 < nblk) ? kb + 1 : 0;
+      const uint32_t noff = wrow_off + (uint32_t)kn * BLOCK_BYTES;
+      const Lane16S sg = lane16_scales(as_u4(hg), sel), su = lane16_scales(as_u4(hu), sel);
+      if constexpr (VAR < 4) {
+        hg = *reinterpret_cast<const u32x4_16*>(wg + noff);
+        hu = *reinterpret_cast<const u32x4_16*>(wu + noff);
+      } else {
+        const uint32_t d = (uint32_t)kb * 0x01010101u;
+        qg0 += d;
+        qu0 += d;
+        qg1 += d;
+        qu1 += d;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      auto load_b = [&](int i, half8 (&b)[NG]) {
+        if constexpr (VAR == 5) {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) b[g] = bfix[g];
+        } else {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) b[g] = *reinterpret_cast<const half8*>(xs + xlane + g * 16 * XS + i * 32);
+        }
+      };
+      auto decode = [&](int i, half8& ag, half8& au) {
+        const uint32_t qg = (i < 4) ? qg0[i & 3] : qg1[i & 3];
+        const uint32_t qu = (i < 4) ? qu0[i & 3] : qu1[i & 3];
+        ag = (i < 4) ? dequant_dword_sc(qg, sg.lo0, sg.hi0, nk) : dequant_dword_sc(qg, sg.lo1, sg.hi1, nk);
+        au = (i < 4) ? dequant_dword_sc(qu, su.lo0, su.hi0, nk) : dequant_dword_sc(qu, su.lo1, su.hi1, nk);
+      };
+      half8 bc[NG], bn[NG], agc, auc, agn, aun;
+      load_b(0, bc);
+      decode(0, agc, auc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < 7) {
+          load_b(i + 1, bn);
+          decode(i + 1, agn, aun);
+        }
+        if (VAR < 4 && i == 3) {
+          qg0 = *reinterpret_cast<const u32x4_16*>(wg + (noff + 16 + 16 * o));
+          qu0 = *reinterpret_cast<const u32x4_16*>(wu + (noff + 16 + 16 * o));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (VAR < 4 && i == 6) {
+          qg1 = *reinterpret_cast<const u32x4_16*>(wg + (noff + 80 + 16 * o));
+          qu1 = *reinterpret_cast<const u32x4_16*>(wu + (noff + 80 + 16 * o));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          accg[g] = mfma16x16(VAR == 2 ? afix : agc, bc[g], accg[g]);
+          accu[g] = mfma16x16(VAR == 2 ? afix : auc, bc[g], accu[g]);
+        }
+        if (i < 7) {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) bc[g] = bn[g];
+          agc = agn;
+          auc = aun;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, NG, 0);
+#pragma unroll
+        for (int k = 0; k < 2 * NG; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, NG >= 8 ? 2 : 3, 0);
+        }
+      }
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) sum += accg[g][0] + accu[g][1];
+  out[(size_t)blockIdx.x * 64 * WAVES + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,6 +297,51 @@ int zinc_peak_hbm_copy(const void* src, void* dst, size_t bytes, int blocks, voi
   hipLaunchKernelGGL(k_hbm_copy, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(src), static_cast<uint4*>(dst), bytes / 16);
   return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// blocks x 512 threads; `out` holds blocks * 512 floats.  Returns the MFMAs
+// issued per SIMD (the step count of the MFMA waves), 0 on an error.
+double zinc_peak_mfma_valu(int same_wave, int kv, int blocks, int iters, float* out, void* stream) {
+  if (blocks < 1 || iters < 1 || !out || kv < 0 || kv > 4) return 0.0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define ZP_MV(MODE, KV) hipLaunchKernelGGL((k_mfma_valu<MODE, KV>), dim3(blocks), dim3(512), 0, s, iters, out)
+  if (same_wave) {
+    switch (kv) { case 0: ZP_MV(0, 0); break; case 1: ZP_MV(0, 1); break; case 2: ZP_MV(0, 2); break;
+                  case 3: ZP_MV(0, 3); break; default: ZP_MV(0, 4); break; }
+  } else {
+    switch (kv) { case 0: ZP_MV(1, 0); break; case 1: ZP_MV(1, 1); break; case 2: ZP_MV(1, 2); break;
+                  case 3: ZP_MV(1, 3); break; default: ZP_MV(1, 4); break; }
+  }
+#undef ZP_MV
+  if (hipGetLastError() != hipSuccess) return 0.0;
+  // per SIMD (two waves of an 8-wave workgroup per SIMD, one workgroup per CU
+  // and round): MFMAs issued by its MFMA-issuing waves
+  return (double)iters * 8 * (same_wave ? 2 : 1);
+}
+
+// The phase-1 loop probe.  ng 4 (12 waves) or 8 (8 waves); var 0, 2, 4 or 5;
+// weights: 192 rows x nblk blocks of Q4_K for each of gate and up (every row
+// of both read); out holds blocks * 768 floats.  Returns the MFMAs per SIMD.
+double zinc_peak_decode_loop(int ng, int var, const void* wg, const void* wu, int nblk, int reps, int blocks,
+                             float* out, void* stream) {
+  if (!wg || !wu || !out || nblk < 1 || reps < 1 || blocks < 1) return 0.0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* g = static_cast<const uint8_t*>(wg);
+  const uint8_t* u = static_cast<const uint8_t*>(wu);
+#define ZP_DL(NG, W, V) hipLaunchKernelGGL((k_decode_loop<NG, W, V>), dim3(blocks), dim3(64 * W), 0, s, g, u, nblk, reps, out)
+  if (ng == 4) {
+    switch (var) { case 0: ZP_DL(4, 12, 0); break; case 2: ZP_DL(4, 12, 2); break; case 4: ZP_DL(4, 12, 4); break;
+                   case 5: ZP_DL(4, 12, 5); break; default: return 0.0; }
+  } else if (ng == 8) {
+    switch (var) { case 0: ZP_DL(8, 8, 0); break; case 2: ZP_DL(8, 8, 2); break; case 4: ZP_DL(8, 8, 4); break;
+                   case 5: ZP_DL(8, 8, 5); break; default: return 0.0; }
+  } else {
+    return 0.0;
+  }
+#undef ZP_DL
+  if (hipGetLastError() != hipSuccess) return 0.0;
+  const int waves = (ng == 4) ? 12 : 8;
+  return (double)waves / 4 * reps * nblk * 8 * ng * 2;
 }
 
 }  // extern "C"

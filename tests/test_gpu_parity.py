@@ -317,6 +317,18 @@ def test_decode_repeated_calls_reuse_workspace(M):
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
 
 
+# the MFMA decode kernels at hidden widths of one to three 4096-wide spans,
+# and one that is not a multiple of 4096 (the K split's last pass ragged)
+@pytest.mark.parametrize("H", [4096, 4352, 8192, 12288])
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_decode_mfma_hidden_widths(M, H):
+    I = 768
+    wg, wu, wd, x = _rand_mlp(4100 + M + H, H, I, M)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, H, I)
+    a, b = shifts_for(y_ref, h_ref)
+    assert_parity(decode(wg, wu, wd, H, I, x, a, b), y_ref, f"decode H={H} I={I} M={M}")
+
+
 def test_decode_and_prefill_agree_at_m8():
     w = S.WORKLOADS["tiny"]
     wg, wu, wd = S.layer_weights(w.seed, 0, w.hidden, w.inter)

@@ -84,7 +84,9 @@ PATHS = {
     "prefill_unit_c": ("prefill", 512, 1536, 330),    # 32x32x16 unit, 384-row chunks
     "prefill_unit_e": ("prefill", 512, 1536, 600),    # 128-token unit, two 128-row passes per chunk
     "decode_rows_m1": ("decode", 1024, 2816, 1),      # row-streaming kernels
+    "decode_rows_m1_w": ("decode", 4352, 1280, 1),    # two chunk slots per lane in the gate/up pass
     "decode_mfma_m4": ("decode", 1024, 2816, 4),      # 16x16x32 MFMA decode
+    "decode_mfma_m3_w": ("decode", 4352, 1280, 3),    # a hidden width that is not a multiple of 4096
     "decode_mfma_m7": ("decode", 1024, 2816, 7),      # two token groups, the second ragged
 }
 
