@@ -12,10 +12,12 @@
 //      (4 tiles x 58 chunks).  The default up to 4 token tiles (256 tokens).
 //   C: MT=64, ICMAX=384 -- the 32x32x16 unit of fused_core.hpp: half the
 //      chunks, so half the partial traffic and one round of units at 512
-//      tokens.  The default past 4 token tiles.
-// Both configurations store their partials in token quads, P[chunk][t/4][n][t%4],
-// which k_reduce_quads sums.  The plan is a function of (M, hidden, inter)
-// alone.
+//      tokens.  The default from 257 to 511 tokens.
+//   E: MT=128, ICMAX=256 -- the 128-token 16x16x32 unit (fused128.hpp, two
+//      128-row passes per chunk) on the staged activation: each decoded
+//      weight meets eight 16-token groups.  The default from 512 tokens.
+// All store their partials in token quads, P[chunk][t/4][n][t%4], which
+// k_reduce_quads sums.  The plan is a function of (M, hidden, inter) alone.
 #include "fused128.hpp"
 #include "fused16.hpp"
 #include "launch.hpp"
@@ -24,6 +26,37 @@
 namespace zinc {
 
 namespace {
+
+// Block id -> (token tile, chunk).  Workgroups go to the eight XCDs
+// round-robin by block id, so block b runs on XCD b % 8, and every XCD runs
+// all token tiles of its chunks, chunk-major (the units of one chunk read the
+// same gate/up rows and W_down columns, under one L2).  Which chunks:
+//   CONTIG (units D and C, one round of units): the contiguous range
+//     [x n / 8, (x + 1) n / 8), so neighbouring chunks, whose W_down column
+//     slices share cache lines at their boundary (a row's 144-byte Q4_K blocks
+//     do not align with 128-byte lines), share an L2 too;
+//   otherwise (unit E, several rounds): chunks x, x + 8, x + 16, ...
+// Measured on the 4096/11008 layer, alternating builds in one process: at
+// M = 256 the contiguous ranges take unit D from 97.4 to 94.8 us (its fetch
+// from 134.7 to 100.7 MB); at M = 2048 unit E takes 661.5 us interleaved and
+// 673.3 us with contiguous ranges (669.8 us tile-major, which cuts its fetch
+// from 946 to 563 MB but slows the reduce after it).  At most ceil(n / 8)
+// chunks per XCD either way, so a grid of 8 * tiles * ceil(n / 8) blocks
+// covers every unit.
+template <bool CONTIG>
+__device__ __forceinline__ bool unit_of_block(int bid, int n_tiles, int n_chunks, int& tile, int& chunk) {
+  const int x = bid & 7, s = bid >> 3;
+  const int q = s / n_tiles;
+  tile = s - q * n_tiles;
+  if constexpr (CONTIG) {
+    const int c0 = x * n_chunks / 8, nc = (x + 1) * n_chunks / 8 - c0;
+    chunk = c0 + q;
+    return q < nc;
+  } else {
+    chunk = 8 * q + x;
+    return chunk < n_chunks;
+  }
+}
 
 template <int TT, int RTW, int ICMAX>
 __global__ __launch_bounds__(64 * FuWaves<TT>::value) void k_prefill_fused(const uint8_t* __restrict__ wg,
@@ -37,13 +70,8 @@ __global__ __launch_bounds__(64 * FuWaves<TT>::value) void k_prefill_fused(const
   __shared__ int tok[C::MT];
   __shared__ float wrow[C::MT];
 
-  // Units of the same intermediate chunk share block id mod 8, so they land on
-  // the same XCD and its L2 serves that weight chunk to every token tile.
-  const int bid = blockIdx.x;
-  const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
-  const int tile = rem >> 3;
-  const int chunk = grp * 8 + (rem & 7);
-  if (chunk >= n_chunks) return;
+  int tile, chunk;
+  if (!unit_of_block<true>(blockIdx.x, n_tiles, n_chunks, tile, chunk)) return;
   const int npan = I / 64;
   const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
   const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
@@ -67,11 +95,8 @@ __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_fused
     int n_tiles, int n_chunks) {
   __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX> sm;
   __shared__ int tok[64];
-  const int bid = blockIdx.x;
-  const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
-  const int tile = rem >> 3;
-  const int chunk = grp * 8 + (rem & 7);
-  if (chunk >= n_chunks) return;
+  int tile, chunk;
+  if (!unit_of_block<true>(blockIdx.x, n_tiles, n_chunks, tile, chunk)) return;
   const int npan = I / 64;
   const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
   const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
@@ -90,11 +115,8 @@ __global__ __launch_bounds__(512) void k_prefill_fused128(
     int n_tiles, int n_chunks) {
   __shared__ __attribute__((aligned(16))) Fused128Smem<NPASS> sm;
   __shared__ int tok[128];
-  const int bid = blockIdx.x;
-  const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
-  const int tile = rem >> 3;
-  const int chunk = grp * 8 + (rem & 7);
-  if (chunk >= n_chunks) return;
+  int tile, chunk;
+  if (!unit_of_block<false>(blockIdx.x, n_tiles, n_chunks, tile, chunk)) return;
   const int npan = I / 64;
   const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
   const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
@@ -114,11 +136,8 @@ __global__ __launch_bounds__(64 * Fused16Cfg<ICMAX>::WAVES) void k_prefill_stage
     int n_chunks, _Float16* __restrict__ G, _Float16* __restrict__ U, const _Float16* __restrict__ Hm) {
   __shared__ __attribute__((aligned(16))) Fused16Smem<ICMAX> sm;
   __shared__ int tok[64];
-  const int bid = blockIdx.x;
-  const int grp = bid / (8 * n_tiles), rem = bid % (8 * n_tiles);
-  const int tile = rem >> 3;
-  const int chunk = grp * 8 + (rem & 7);
-  if (chunk >= n_chunks) return;
+  int tile, chunk;
+  if (!unit_of_block<true>(blockIdx.x, n_tiles, n_chunks, tile, chunk)) return;
   const int npan = I / 64;
   const int r0 = (int)((long long)chunk * npan / n_chunks) * 64;
   const int r1 = (int)((long long)(chunk + 1) * npan / n_chunks) * 64;
@@ -207,10 +226,10 @@ int round_up(int a, int b) { return (a + b - 1) / b * b; }
 // takes over from C.
 constexpr int kUnitEMinTokens = 512;
 
-// Units run one per CU, and the unit order below pins chunk c to XCD c % 8,
-// whose 32 CUs run that XCD's units: a plan takes the fewest rounds k for
-// which chunks = 8 * floor(32 k / tiles) reaches the unit's minimum, so every
-// XCD runs at most k rounds of 32 units, and the units are as small as k
+// Units run one per CU, and unit_of_block gives each XCD (32 CUs) at most
+// ceil(chunks / 8) chunks of every token tile: a plan takes the fewest rounds
+// k for which chunks = 8 * floor(32 k / tiles) reaches the unit's minimum, so
+// every XCD runs at most k rounds of 32 units, and the units are as small as k
 // rounds allow; of the chunk counts that give the same largest unit, the
 // smallest (fewest partials).  D (192-row chunks, at least 58) up to four
 // 64-token tiles, where one round fits; C (384-row chunks, at least 29) beyond.
