@@ -307,25 +307,23 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
   __shared__ int tok[MT_MOE];
   __shared__ int slot_of_row[MoeCfg::MTS];   // rows past MT_MOE (phase 2's last 32-token half): the junk row
 
-  // Units: n_chunks per tile of a 192-row-chunk expert (listed first), then
-  // n_chunks_small per tile of the others.  A tile's chunks have consecutive
-  // block ids and so go round-robin over the XCDs; the same chunk of an
-  // expert's consecutive tiles lands on the same pair of XCDs, whose L2s serve
-  // that slice of the expert's weights.
+  // Units: the chunks of the 192-row-chunk experts' tiles (listed first), then
+  // those of the others' tiles.  Workgroups go to the eight XCDs round-robin
+  // by block id, and every chunk of tile ti runs on XCD ti % 8: the chunks of
+  // one expert tile read neighbouring W_down column slices, which share cache
+  // lines at their boundary (144-byte Q4_K blocks do not align with 128-byte
+  // lines), and the tile's gathered activation rows, under one L2.  Each of
+  // the two segments takes 8 * chunks * ceil(tiles / 8) block ids.
   const int nbig = n_tiles[1];
-  const int units_big = nbig * n_chunks;
-  int ti, chunk, nc;
-  if ((int)blockIdx.x < units_big) {
-    ti = blockIdx.x / n_chunks;
-    chunk = blockIdx.x % n_chunks;
-    nc = n_chunks;
-  } else {
-    const int u = blockIdx.x - units_big;
-    ti = nbig + u / n_chunks_small;
-    chunk = u % n_chunks_small;
-    nc = n_chunks_small;
-  }
-  if (ti >= n_tiles[0]) return;
+  const int seg_big = 8 * n_chunks * ((nbig + 7) / 8);
+  const bool big = (int)blockIdx.x < seg_big;
+  const int nc = big ? n_chunks : n_chunks_small;
+  const int u = big ? (int)blockIdx.x : (int)blockIdx.x - seg_big;
+  const int x = u & 7, s = u >> 3;
+  const int q = s / nc;
+  const int chunk = s - q * nc;
+  const int ti = (big ? 0 : nbig) + 8 * q + x;
+  if (big ? ti >= nbig : ti >= n_tiles[0]) return;
   const int e = tile_expert[ti];
   const int start = tile_start[ti], rows = tile_rows[ti];
   if (threadIdx.x < MoeCfg::MTS) {
@@ -431,8 +429,12 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
                      hidden, M, pl.xtok);
   const int n_chunks = chunks_for(inter), n_chunks_small = chunks_small_for(inter);
   const int max_tiles = max_tiles_for(M, top_k, E);
+  // both unit segments (tile counts known on the device only) padded to whole
+  // groups of eight tiles: at most max_tiles * n_chunks_small + 8 * (n_chunks +
+  // n_chunks_small) block ids
+  const int grid = max_tiles * n_chunks_small + 8 * (n_chunks + n_chunks_small);
   auto fused = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(max_tiles * n_chunks_small), dim3(MoeCfg::THREADS), 0, stream,
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(MoeCfg::THREADS), 0, stream,
                        static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu),
                        static_cast<const uint8_t*>(wd), hidden, inter, M, pl.xtok, top_k, pl.n_tiles, pl.tile_expert,
                        pl.tile_start, pl.tile_rows, pl.slots, pl.Q, n_slots, ldexpf(1.0f, -inter_shift),
