@@ -19,11 +19,11 @@ staged baseline (the intermediate in device memory) at M=256 and M=2048.
 
 Also in the line: the measured peaks of this chip (an MFMA-only loop, HBM
 stream read and copy; libzinc_peaks.so), the graphics clock and socket power
-sampled through amdsmi during the headline's timed calls, and the headline
+sampled through amdsmi right after the headline's timed calls, and the headline
 fraction against the spec peak, the measured peak and the spec peak at the
 observed clock.
 
-usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-secondary] [--no-cpu-baseline] [--no-peaks]
+usage: python bench.py [--gpus 1] [--steps 200] [--warmup 300] [--no-secondary] [--no-cpu-baseline] [--no-peaks]
 """
 from __future__ import annotations
 
@@ -809,8 +809,10 @@ def moe_lines(args, torch, np, Z, S, dev, t):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the graphics clock climbs for the first ~200 calls (~25 ms) of back-to-back
+    # work after idle: the timed calls start once it has settled
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "moe", "block", "m2048", "staged", "peaks", "cpu"], default=None,

@@ -305,7 +305,9 @@ int zinc_moe_route_topk(const float* logits, int32_t M, int32_t n_experts, int32
  * MoE call records a HIP event pair on its stream immediately around its main
  * kernel -- the fused unit kernel for prefill and MoE; for decode, one pair
  * around the gate/up matvec and one around the down matvec -- for up to
- * `capacity` pairs.  zinc_timing_collect() waits for the recorded events,
+ * `capacity` pairs.  The events are recorded without a system-scope fence
+ * (hipEventDisableSystemFence), so they add no cache write-back of their own
+ * to the work they bracket.  zinc_timing_collect() waits for the recorded events,
  * writes each pair's elapsed milliseconds to ms[0..*n_out) in launch order and
  * restarts the recording; zinc_timing_disable() stops it and destroys the
  * events.  Not meant to be used while other threads call the library.

@@ -63,7 +63,11 @@ int zinc_timing_enable(int32_t capacity) {
   t.start.resize(capacity);
   t.stop.resize(capacity);
   for (int i = 0; i < capacity; ++i) {
-    if (hipEventCreate(&t.start[i]) != hipSuccess || hipEventCreate(&t.stop[i]) != hipSuccess) {
+    // timing only: no system-scope fence on record (a fence would write back
+    // and invalidate the caches between the timed kernel and its neighbours,
+    // adding its own cost to the call being measured)
+    if (hipEventCreateWithFlags(&t.start[i], hipEventDisableSystemFence) != hipSuccess ||
+        hipEventCreateWithFlags(&t.stop[i], hipEventDisableSystemFence) != hipSuccess) {
       t.start.resize(i);
       t.stop.resize(i);
       destroy_events(t);
