@@ -69,12 +69,19 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_calls(fn, steps: int, warmup: int, torch):
-    """Warmup, then time exactly `steps` calls bracketed by synchronize; returns
-    (wall seconds, per-call main-kernel durations in ms from the timing hook)."""
+def time_calls(fn, steps: int, warmup: int, torch, warm_s: float = 0.0):
+    """Warmup (`warmup` calls, and for the secondary workloads at least `warm_s`
+    seconds of calls, so the clock has settled after the host work that sets
+    each workload up), then time exactly `steps` calls bracketed by
+    synchronize; returns (wall seconds, per-call main-kernel durations in ms
+    from the timing hook)."""
     import q4_swiglu_mlp_amd as Z
-    for _ in range(warmup):
-        fn(0)
+    t0, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t0 < warm_s:
+        fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     Z.timing_enable(4 * steps)
     torch.cuda.synchronize()
@@ -557,7 +564,7 @@ def m2048_lines(args, torch, np, Z, S, dev, t):
         Z.zinc_mlp_q4k_prefill(lg, lu, ld, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
 
     steps = 3 * n_layers
-    wall, ms = time_calls(call, steps, n_layers, torch)
+    wall, ms = time_calls(call, steps, n_layers, torch, warm_s=0.05)
     per = wall / steps
     kern = sum(ms) / len(ms)   # the fused kernel of each call (HIP events on its stream)
     flops = 6.0 * w.M * w.hidden * w.inter
@@ -594,8 +601,8 @@ def block_lines(args, torch, np, Z, S, dev, t):
         def plain(_i):
             fplain(wg, wu, wd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=wsb)
 
-        tb = min(time_calls(blk, steps, 5, torch)[0] for _ in range(2)) / steps
-        tp = min(time_calls(plain, steps, 5, torch)[0] for _ in range(2)) / steps
+        tb = min(time_calls(blk, steps, 5, torch, warm_s=0.05)[0] for _ in range(2)) / steps
+        tp = min(time_calls(plain, steps, 5, torch, warm_s=0.05)[0] for _ in range(2)) / steps
         out.append({
             "workload": f"MLP block (RMS norm + MLP + residual) vs plain MLP call, {name} (4096/11008, M={w.M})",
             "block_us": round(tb * 1e6, 2),
@@ -645,8 +652,8 @@ def _staged_lines_d(torch, Z, S, dev, t):
         # alternate the two a few times (same thermal state), keep each one's best round
         best_f, best_s = float("inf"), float("inf")
         for _ in range(3):
-            best_f = min(best_f, time_calls(fused, steps, 3, torch)[0] / steps)
-            best_s = min(best_s, time_calls(staged, steps, 3, torch)[0] / steps)
+            best_f = min(best_f, time_calls(fused, steps, 3, torch, warm_s=0.05)[0] / steps)
+            best_s = min(best_s, time_calls(staged, steps, 3, torch, warm_s=0.05)[0] / steps)
         crossing = 6 * w.M * w.inter * 2
         out.append({
             "workload": f"fused vs staged prefill 4096/11008 M={w.M} (seed {w.seed}, layer 0)",
@@ -703,7 +710,7 @@ def decode_lines(args, torch, np, Z, S, dev, t):
             Z.zinc_mlp_q4k_decode(lg, lu, ld, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
 
         steps = len(layers) * 10
-        wall, ms = time_calls(call, steps, len(layers), torch)
+        wall, ms = time_calls(call, steps, len(layers), torch, warm_s=0.05)
         per_layer = wall / steps
         kern_ms = sum(ms) / steps   # the timed kernels of one call (gate+up and down)
         graph_us = decode_graph_us(torch, Z, layers, w, gx, y, ws)
@@ -742,7 +749,7 @@ def moe_lines(args, torch, np, Z, S, dev, t):
                                y=y, workspace=ws)
 
     steps = 100
-    wall, ms = time_calls(mcall, steps, 10, torch)
+    wall, ms = time_calls(mcall, steps, 10, torch, warm_s=0.05)
     per = wall / steps
     kern = sum(ms) / len(ms)
     wbytes = w.n_experts * (2 * q4k_bytes(w.inter, w.hidden) + q4k_bytes(w.hidden, w.inter))
@@ -783,7 +790,7 @@ def moe_lines(args, torch, np, Z, S, dev, t):
             Z.zinc_moe_experts_fmt(eg, eu, wd5, fmt, w.n_experts, w.hidden, w.inter, gx, gids, gp, w.inter_shift,
                                    w.out_shift, y=y, workspace=ws)
 
-        fwall, fms = time_calls(fcall, steps, 10, torch)
+        fwall, fms = time_calls(fcall, steps, 10, torch, warm_s=0.05)
         out.append({
             "workload": f"MoE E=64 top-8, 2048->768, M=512, down projections in {fmt.upper()}",
             "tokens_per_s": round(w.M / (fwall / steps), 1),
@@ -793,8 +800,8 @@ def moe_lines(args, torch, np, Z, S, dev, t):
         log(f"[bench] {out[-1]}")
         del wd5
 
-    rwall, rms = time_calls(rcall, steps, 10, torch)
-    lwall, _ = time_calls(lcall, steps, 10, torch)
+    rwall, rms = time_calls(rcall, steps, 10, torch, warm_s=0.05)
+    lwall, _ = time_calls(lcall, steps, 10, torch, warm_s=0.05)
     out.append({
         "workload": "MoE router, top-8 of 64 fp32 logits, M=512; then router + experts as one block",
         "router_us_per_call": round(rwall / steps * 1e6, 3),
