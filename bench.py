@@ -248,6 +248,55 @@ def measure_issue_probes(torch):
     return res
 
 
+def measure_stream_layouts(torch):
+    """Bandwidth of three ways to read a 4096 x 11008 gate/up pair of Q4_K
+    matrices (50.7 MB), over 32 rotating pairs so that every launch reads from
+    HBM (libzinc_peaks.so): a row per wave with the lanes along the row (the
+    decode row kernels); 16-row tiles per wave in the MFMA lane layout, walked
+    one block column at a time (the fused units and the MFMA decode); the same
+    tiles two block columns long, so that a tile is 4.6 KB of contiguous
+    memory."""
+    import ctypes
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.zinc_peak_q4k_stream.restype = ctypes.c_int
+    lib.zinc_peak_q4k_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    cur = torch.cuda.current_stream()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    rows, nb = 11008, 16
+    nbytes = rows * nb * 144
+    pairs = [(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev),
+              torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev)) for _ in range(32)]
+    out = torch.empty(ncu * 2 * 256, dtype=torch.int32, device=dev)
+    res = {}
+    for name, layout, lnb, lrows in (("row_per_wave", 0, nb, rows), ("mfma_tiles_16_blocks", 1, nb, rows),
+                                     ("mfma_tiles_2_blocks", 1, 2, rows * nb // 2)):
+        def run(i):
+            g, u = pairs[i % 32]
+            if lib.zinc_peak_q4k_stream(layout, g.data_ptr(), u.data_ptr(), lnb, lrows, 2 * ncu, out.data_ptr(),
+                                        cur.cuda_stream) != 0:
+                raise RuntimeError("stream probe launch failed")
+        for i in range(64):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(3):
+            e0.record(cur)
+            for i in range(32):
+                run(i)
+            e1.record(cur)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3 / 32)
+        res[name] = {"us": round(best * 1e6, 2), "GBs": round(2 * nbytes / best / 1e9, 1)}
+    res["method"] = ("loads only (folded into a sink), two 4-wave workgroups per CU, best of three sweeps of 32 "
+                     "launches over 32 rotating pairs")
+    del pairs, out
+    torch.cuda.empty_cache()
+    return res
+
+
 class ClockSampler:
     """Samples the GPU's graphics clock and socket power through amdsmi in a
     background thread while a timed region runs (every ~10 ms).  Any failure
@@ -850,8 +899,8 @@ def main():
     import torch
 
     if args.only == "peaks":
-        print(json.dumps({"measured_peaks": measure_peaks(torch), "issue_probes": measure_issue_probes(torch)}),
-              flush=True)
+        print(json.dumps({"measured_peaks": measure_peaks(torch), "issue_probes": measure_issue_probes(torch),
+                          "q4k_stream_layouts": measure_stream_layouts(torch)}), flush=True)
         return
     if args.only == "cpu":
         import q4k_synth as S

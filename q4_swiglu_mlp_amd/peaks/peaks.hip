@@ -19,6 +19,12 @@
 //                        4 or 8 token groups per decoded operand, and with
 //                        parts removed (the weight loads, the LDS reads, the
 //                        decode) to price each
+//   zinc_peak_q4k_stream   the bandwidth of three ways to read a gate/up pair
+//                        of Q4_K matrices: one row per wave with the lanes
+//                        along the row (the decode row kernels), 16-row tiles
+//                        per wave in the MFMA lane layout walked block column
+//                        by block column (the fused units, the MFMA decode),
+//                        and 16-row tiles of one block column each
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -262,6 +268,67 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode_loop(const uint8_t* __res
   out[(size_t)blockIdx.x * 64 * WAVES + threadIdx.x] = sum;
 }
 
+
+// Q4_K stream layouts (loads only, folded into a sink).  LAYOUT 0: wave per
+// row, lane l = 64-weight chunk l of the row (block header + its 32 quant
+// bytes); LAYOUT 1: wave per 16-row tile, lane (r, o) = row r, quant pieces
+// [16o, +16) and [64 + 16o, +16) and the header of every block in turn, two
+// blocks ahead.
+template <int LAYOUT>
+__global__ __launch_bounds__(256) void k_q4k_stream(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+                                                    int nb, int nrows, uint32_t* __restrict__ out) {
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  const uint32_t rowb = (uint32_t)nb * 144u;
+  u4v sink = {0u, 0u, 0u, 0u};
+  if constexpr (LAYOUT == 0) {
+    const uint32_t boff = (uint32_t)(lane >> 2) * 144u, qoff = boff + 16u + 32u * (uint32_t)(lane & 3);
+    const bool has = (lane >> 2) < nb;
+    for (int j = wave; j < nrows; j += nw) {
+      if (!has) break;
+      const uint32_t b = (uint32_t)j * rowb;
+      sink ^= *reinterpret_cast<const u4v*>(wg + b + boff);
+      sink ^= *reinterpret_cast<const u4v*>(wg + b + qoff);
+      sink ^= *reinterpret_cast<const u4v*>(wg + b + qoff + 16);
+      sink ^= *reinterpret_cast<const u4v*>(wu + b + boff);
+      sink ^= *reinterpret_cast<const u4v*>(wu + b + qoff);
+      sink ^= *reinterpret_cast<const u4v*>(wu + b + qoff + 16);
+    }
+  } else {
+    const int r = lane & 15, o = lane >> 4;
+    for (int t = wave; t < nrows / 16; t += nw) {
+      const uint32_t base = (uint32_t)(t * 16 + r) * rowb;
+      u4v buf[2][6];
+      auto ld = [&](int a, int kb) __attribute__((always_inline)) {
+        const uint32_t off = base + (uint32_t)(kb < nb ? kb : nb - 1) * 144u;
+        buf[a][0] = *reinterpret_cast<const u4v*>(wg + off);
+        buf[a][1] = *reinterpret_cast<const u4v*>(wg + off + 16 + 16 * o);
+        buf[a][2] = *reinterpret_cast<const u4v*>(wg + off + 80 + 16 * o);
+        buf[a][3] = *reinterpret_cast<const u4v*>(wu + off);
+        buf[a][4] = *reinterpret_cast<const u4v*>(wu + off + 16 + 16 * o);
+        buf[a][5] = *reinterpret_cast<const u4v*>(wu + off + 80 + 16 * o);
+      };
+      ld(0, 0);
+      ld(1, 1);
+      for (int kb = 0; kb < nb; kb += 2) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+          for (int m = 0; m < 6; ++m) sink ^= buf[a][m];
+          ld(a, kb + a + 2);
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int m = 0; m < 6; ++m) sink ^= buf[a][m];
+    }
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = sink.x ^ sink.y ^ sink.z ^ sink.w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -342,6 +409,27 @@ double zinc_peak_decode_loop(int ng, int var, const void* wg, const void* wu, in
   if (hipGetLastError() != hipSuccess) return 0.0;
   const int waves = (ng == 4) ? 12 : 8;
   return (double)waves / 4 * reps * nblk * 8 * ng * 2;
+}
+
+// One launch of a Q4_K stream layout over a gate/up pair of nrows x (256 nb)
+// matrices: layout 0 (row per wave, nb <= 16), 1 (16-row tiles, nrows a
+// multiple of 16, nb even).  blocks x 256 threads; `out` holds blocks * 256
+// words.  Returns 0, or -1 on an invalid argument.
+int zinc_peak_q4k_stream(int layout, const void* wg, const void* wu, int nb, int nrows, int blocks, uint32_t* out,
+                         void* stream) {
+  if (!wg || !wu || !out || nb < 1 || nrows < 16 || blocks < 1) return -1;
+  if (layout == 0 && nb > 16) return -1;
+  if (layout == 1 && ((nrows % 16) != 0 || (nb % 2) != 0)) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* g = static_cast<const uint8_t*>(wg);
+  const uint8_t* u = static_cast<const uint8_t*>(wu);
+  if (layout == 0)
+    hipLaunchKernelGGL(k_q4k_stream<0>, dim3(blocks), dim3(256), 0, s, g, u, nb, nrows, out);
+  else if (layout == 1)
+    hipLaunchKernelGGL(k_q4k_stream<1>, dim3(blocks), dim3(256), 0, s, g, u, nb, nrows, out);
+  else
+    return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // extern "C"
