@@ -663,25 +663,11 @@ def block_lines(args, torch, np, Z, S, dev, t):
 
 
 def staged_lines(args, torch, np, Z, S, dev, t):
-    """The fused prefill against its staged comparison baseline (the same
-    units with G, U and the intermediate in device memory), whole calls."""
-    out = []
-    # the fused call runs the staged baseline's unit (configuration D) at
-    # every M, so the two differ only in where the intermediate lives; the
-    # override is in place before the workspace size query, which follows it
-    saved = os.environ.get("ZINC_PREFILL_CFG")
-    os.environ["ZINC_PREFILL_CFG"] = "D"
-    try:
-        out = _staged_lines_d(torch, Z, S, dev, t)
-    finally:
-        if saved is None:
-            os.environ.pop("ZINC_PREFILL_CFG", None)
-        else:
-            os.environ["ZINC_PREFILL_CFG"] = saved
-    return out
-
-
-def _staged_lines_d(torch, Z, S, dev, t):
+    """The fused prefill against its staged comparison baseline (unit D's
+    units with G, U and the intermediate in device memory), whole calls.  At
+    M=256 both calls run unit D, so they differ only in where the intermediate
+    lives; at M=2048 the fused call runs its default unit (the 128-token unit
+    E) and the staged call unit D."""
     out = []
     for name, steps in (("prefill_m256", 50), ("prefill_m2048", 10)):
         w = S.WORKLOADS[name]
@@ -706,6 +692,7 @@ def _staged_lines_d(torch, Z, S, dev, t):
         crossing = 6 * w.M * w.inter * 2
         out.append({
             "workload": f"fused vs staged prefill 4096/11008 M={w.M} (seed {w.seed}, layer 0)",
+            "units": "fused D, staged D" if w.M <= 256 else "fused E, staged D",
             "fused_us": round(best_f * 1e6, 2),
             "staged_us": round(best_s * 1e6, 2),
             "staged_over_fused": round(best_s / best_f, 3),
