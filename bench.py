@@ -24,6 +24,7 @@ fraction against the spec peak, the measured peak and the spec peak at the
 observed clock.
 
 usage: python bench.py [--gpus 1] [--steps 200] [--warmup 300] [--no-secondary] [--no-cpu-baseline] [--no-peaks]
+                      [--no-extras]
 """
 from __future__ import annotations
 
@@ -421,10 +422,12 @@ def headline(args, torch, peaks=None):
         Z.zinc_mlp_q4k_prefill(gwg, gwu, gwd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
 
     wall, ms = time_calls(call, args.steps, args.warmup, torch)
-    clock = sample_clock(torch, call, "back-to-back headline calls for 2 s after the timed region, the last 0.8 s")
+    extras = not getattr(args, "no_extras", False)
+    clock = (sample_clock(torch, call, "back-to-back headline calls for 2 s after the timed region, the last 0.8 s")
+             if extras else {"samples": 0, "error": "not sampled (--no-extras)"})
     kern_ms = sum(ms) / len(ms)
-    pct = call_percentiles(torch, call)
-    graph_us = prefill_graph_us(torch, call, y)
+    pct = call_percentiles(torch, call) if extras else None
+    graph_us = prefill_graph_us(torch, call, y) if extras else None
     flops = 6.0 * w.M * w.hidden * w.inter
     achieved = flops / (kern_ms * 1e-3) / 1e12
     traffic = None
@@ -449,7 +452,8 @@ def headline(args, torch, peaks=None):
         "ms_per_step": wall / args.steps * 1e3,
         "roofline": roofline,
         "whole_call_tflops": round(flops / (wall / args.steps) / 1e12, 2),
-        "graph_replay": {"us_per_call": round(graph_us, 3), "tokens_per_s": round(w.M / (graph_us * 1e-6), 1)},
+        "graph_replay": ({"us_per_call": round(graph_us, 3), "tokens_per_s": round(w.M / (graph_us * 1e-6), 1)}
+                         if graph_us else None),
         "call_us": pct,
         "clock": clock,
     }
@@ -862,6 +866,9 @@ def main():
                     help="development and profiling runs: skip the headline and run one part (a secondary line, "
                          "the measured peaks, or the full CPU oracle table including one-thread figures)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline: only the warmup and timed calls (no clock sampling, percentile calls or graph "
+                         "replay), for counter collection")
     ap.add_argument("--layers", type=int, default=32,
                     help="layers of the 32-layer sweeps (decode, 2048-token prefill); fewer for profiling runs")
     ap.add_argument("--copy-calibration", action="store_true",
