@@ -225,12 +225,14 @@ __device__ __forceinline__ float x16_dpp(float v) {
 // column, the 34 pieces described at X16_TP.  Grid ((M + 8) / 8, H / 256),
 // 256 threads = 8 tokens x 32 pieces; piece (c, j) of a token is
 // x[64c + 4j + {0..3}] and x[64c + 32 + 4j + {0..3}] of the column.
-__global__ __launch_bounds__(256) void k_stage_x16(const _Float16* __restrict__ x, int H, int M,
-                                                   uint8_t* __restrict__ xtok) {
-  const int kb = blockIdx.y, nbH = H / QK;
-  const int token = blockIdx.x * 8 + (threadIdx.x >> 5);
+// One 256-thread group of the staging: tokens 8 bx .. 8 bx + 7 of column kb,
+// thread t of the group.
+__device__ __forceinline__ void stage_x16_group(const _Float16* __restrict__ x, int H, int M,
+                                                uint8_t* __restrict__ xtok, int bx, int kb, int t) {
+  const int nbH = H / QK;
+  const int token = bx * 8 + (t >> 5);
   if (token > M) return;   // whole 32-lane groups (the DPP sums below stay within one)
-  const int p = threadIdx.x & 31, c = p >> 3, j = p & 7;
+  const int p = t & 31, c = p >> 3, j = p & 7;
   _Float16* col = reinterpret_cast<_Float16*>(xtok + ((size_t)token * nbH + kb) * X16_TP_BYTES);
   uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
   if (token < M) {
@@ -259,6 +261,11 @@ __global__ __launch_bounds__(256) void k_stage_x16(const _Float16* __restrict__ 
     m[sb_slot(2 * c)] = (_Float16)(sl * 0.03125f);
     m[sb_slot(2 * c + 1)] = (_Float16)(sh * 0.03125f);
   }
+}
+
+__global__ __launch_bounds__(256) void k_stage_x16(const _Float16* __restrict__ x, int H, int M,
+                                                   uint8_t* __restrict__ xtok) {
+  stage_x16_group(x, H, M, xtok, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 }  // namespace

@@ -222,11 +222,22 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__
 // (build_tile_table's order), then the scatter with LDS cursors.
 constexpr int kRouteOneBlockSlots = 1 << 16;
 
+// Block 0 routes (the one-workgroup path); every other block stages the
+// activation, four 256-thread staging groups per block (group g = 4 (b - 1) +
+// threadIdx.x / 256 of the grid ((M + 8) / 8) x (H / 256)), so the two run side
+// by side in one launch.
 __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ ids, int n_slots, int E,
                                                    int32_t* __restrict__ dev_error, int* __restrict__ offsets,
                                                    int* __restrict__ tile_expert, int* __restrict__ tile_start,
                                                    int* __restrict__ tile_rows, int* __restrict__ n_tiles,
-                                                   int* __restrict__ slots, int* __restrict__ pos, int MT) {
+                                                   int* __restrict__ slots, int* __restrict__ pos, int MT,
+                                                   const _Float16* __restrict__ x, int H, int M,
+                                                   uint8_t* __restrict__ xtok) {
+  if (blockIdx.x > 0) {
+    const int gx = (M + 8) / 8, g = 4 * ((int)blockIdx.x - 1) + ((int)threadIdx.x >> 8);
+    if (g < gx * (H / QK)) stage_x16_group(x, H, M, xtok, g % gx, g / gx, threadIdx.x & 255);
+    return;
+  }
   __shared__ int cnt[1024];
   __shared__ int s0[1024], s1[1024], s2[1024], s3[1024], s4[1024];
   const int e = threadIdx.x;
@@ -411,9 +422,13 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
   const int n_slots = M * top_k;
   MoePlan pl = carve(ws, M, top_k, E, hidden, inter, nullptr);
   const bool one_block = n_slots <= kRouteOneBlockSlots;
+  const _Float16* xh = static_cast<const _Float16*>(x);
   if (one_block) {
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), 0, stream, ids, n_slots, E, dev_error, pl.offsets,
-                       pl.tile_expert, pl.tile_start, pl.tile_rows, pl.n_tiles, pl.slots, pl.pos, MT_MOE);
+    // routing and staging in one launch (block 0 routes)
+    const int groups = ((M + 8) / 8) * (hidden / QK);
+    hipLaunchKernelGGL(k_moe_route, dim3(1 + (groups + 3) / 4), dim3(1024), 0, stream, ids, n_slots, E, dev_error,
+                       pl.offsets, pl.tile_expert, pl.tile_start, pl.tile_rows, pl.n_tiles, pl.slots, pl.pos, MT_MOE,
+                       xh, hidden, M, pl.xtok);
   } else {
     // counts and cursor are adjacent 256-byte-aligned arrays; zero both
     launch_fill_zero(reinterpret_cast<float*>(pl.counts),
@@ -424,9 +439,8 @@ hipError_t launch_moe(const void* wg, const void* wu, const void* wd, int n_expe
                        pl.tile_start, pl.tile_rows, pl.n_tiles, MT_MOE);
     hipLaunchKernelGGL(k_moe_scatter, dim3(sblocks), dim3(256), 0, stream, ids, n_slots, E, MT_MOE, pl.offsets, pl.cursor,
                        pl.slots, pl.pos);
+    hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream, xh, hidden, M, pl.xtok);
   }
-  hipLaunchKernelGGL(k_stage_x16, dim3(M / 8 + 1, hidden / QK), dim3(256), 0, stream, static_cast<const _Float16*>(x),
-                     hidden, M, pl.xtok);
   const int n_chunks = chunks_for(inter), n_chunks_small = chunks_small_for(inter);
   const int max_tiles = max_tiles_for(M, top_k, E);
   // both unit segments (tile counts known on the device only) padded to whole
