@@ -271,7 +271,7 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
     if (lane == 0) part[wave] = ss;
-    __syncthreads();
+    lds_barrier();
     float tot = 0.0f;
 #pragma unroll
     for (int w = 0; w < DR_WAVES; ++w) tot += part[w];
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
     s8 += dpp_f<0x4E>(s8);
     if (g < ngroups && (a & 3) == 0) X2[t * 2 * Q + (a >> 2)] = s8;
   }
-  __syncthreads();
+  lds_barrier();
   if constexpr (XREG) {
 #pragma unroll
     for (int k = 0; k < KQ; ++k) {
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(SplitShape<S>::THREADS) void k_decode_down_split(co
     s8 += dpp_f<0x4E>(s8);
     if (gi < nxg && (gi & 3) == 0) X2[gi >> 2] = s8;
   }
-  __syncthreads();
+  lds_barrier();
   uint4 xr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const uint4*>(xs + 64 * qc + 8 * i);
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(SplitShape<S>::THREADS) void k_decode_down_split(co
     acc = wave_sum_to_lane63(acc);
     float* pb = part + (it & 1) * R * S;
     if (lane == 63) pb[rs * S + seg] = acc;
-    __syncthreads();
+    lds_barrier();
     if (tid < R) {
       const int j = g * R + tid;
       if (j < N) {

@@ -96,6 +96,13 @@ __device__ __forceinline__ LaneChunkS lane_chunk_scales(uint4 hdr, int sel) {
   return r;
 }
 
+// Orders one wave's LDS accesses for the compiler (the hardware already runs
+// them in program order); emits no instruction.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 struct DecBlock {
   uint4 hdr, q0, q1;
 };
@@ -162,43 +169,43 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
     // 1. activation loads first (the staging below waits only for them), then
     //    every weight load of the pass, then the headers of the min correction
     //    (octet o of group g takes block 4g+o)
+    //    Every load is issued, whatever cnt is: a block past the wave's range
+    //    reads the wave's last block (or block 0 when the range is empty)
+    //    instead, and its result is discarded below.  With a fixed number of
+    //    loads in flight the compiler can wait for the activations alone.
+    const int blast = max(b1 - 1, 0);
     uint2 xl[NPIT], xh[NPIT];
 #pragma unroll
     for (int it = 0; it < NPIT; ++it) {
       const int p = lane + 64 * it;
       const int j = p & 7, c = (p >> 3) & 3, bl = (p >> 5) % NBW, n = p / (32 * NBW);
-      xl[it] = xh[it] = make_uint2(0, 0);
-      if (p < NPIECE && bl < cnt && n < M) {
-        const _Float16* src = xin + (size_t)n * K + (size_t)(pb + bl) * QK + 64 * c + 4 * j;
-        xl[it] = *reinterpret_cast<const uint2*>(src);
-        xh[it] = *reinterpret_cast<const uint2*>(src + 32);
-      }
+      const _Float16* src = xin + (size_t)min(n, M - 1) * K + (size_t)min(pb + bl, blast) * QK + 64 * c + 4 * j;
+      xl[it] = *reinterpret_cast<const uint2*>(src);
+      xh[it] = *reinterpret_cast<const uint2*>(src + 32);
     }
     u32x4 w0[NBW][3], w1[NBW][3];   // raw pieces k = 0, 1, 2 of the coalesced loads
     uint4 ch0[NG], ch1[NG];
-    static_for<NBW>([&](auto blc) {
-      constexpr int bl = decltype(blc)::value;
-      if (bl < cnt) {
-        const size_t boff = (size_t)(pb + bl) * BLOCK_BYTES;
-        // lanes 16..63 of the third load re-read piece 143 (in bounds, unused)
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          w0[bl][k] = *reinterpret_cast<const u32x4*>(W0 + poff[k] + boff);
-          if (GATEUP) w1[bl][k] = *reinterpret_cast<const u32x4*>(W1 + poff[k] + boff);
-        }
-      }
-    });
+    for (int bl = 0; bl < NBW; ++bl) {
+      const size_t boff = (size_t)min(pb + bl, blast) * BLOCK_BYTES;
+      // lanes 16..63 of the third load re-read piece 143 (in bounds, unused)
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const int bl = 4 * g + o;
-      ch0[g] = ch1[g] = make_uint4(0, 0, 0, 0);
-      if (bl < cnt) {
-        ch0[g] = *reinterpret_cast<const uint4*>(row0 + (size_t)(pb + bl) * BLOCK_BYTES);
-        if (GATEUP) ch1[g] = *reinterpret_cast<const uint4*>(row1 + (size_t)(pb + bl) * BLOCK_BYTES);
+      for (int k = 0; k < 3; ++k) {
+        w0[bl][k] = *reinterpret_cast<const u32x4*>(W0 + poff[k] + boff);
+        if (GATEUP) w1[bl][k] = *reinterpret_cast<const u32x4*>(W1 + poff[k] + boff);
       }
     }
-    // 2. stage this pass's activation pieces and sub-block means
-    if (pass > 0) __syncthreads();   // every wave is done reading the previous pass
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const size_t boff = (size_t)min(pb + 4 * g + o, blast) * BLOCK_BYTES;
+      ch0[g] = *reinterpret_cast<const uint4*>(row0 + boff);
+      if (GATEUP) ch1[g] = *reinterpret_cast<const uint4*>(row1 + boff);
+    }
+    // 2. stage this pass's activation pieces and sub-block means.  The LDS
+    //    areas of the pass loop belong to one wave each, whose LDS accesses
+    //    complete in program order, so no workgroup barrier is needed; the
+    //    fence below only keeps the compiler from moving accesses across it.
+    wave_lds_order();
 #pragma unroll
     for (int it = 0; it < NPIT; ++it) {
       const int p = lane + 64 * it;
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
         xm[(n * NBW + bl) * 8 + sb_slot(2 * c + 1)] = (_Float16)(sh * 0.03125f);
       }
     }
-    __syncthreads();
+    wave_lds_order();
 
     // 3. MFMAs: 8 per block and matrix, then the min correction per 4 blocks
     const _Float16* xb = xs + tb * TSTRIDE + o * 8;
@@ -273,11 +280,13 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
     for (int g = 0; g < NG; ++g) {
       if (4 * g >= cnt) continue;   // wave-uniform
       const int bl = 4 * g + o;
-      // octets past the pass's blocks carry a zero header, hence a zero A
+      // octets past the pass's blocks take a zero header, hence a zero A
       // operand; they read the means of a staged block (finite) instead
+      const bool live = bl < cnt;
+      const uint4 z = make_uint4(0, 0, 0, 0);
       const half8 b = *reinterpret_cast<const half8*>(xm + (tb * NBW + min(bl, cnt - 1)) * 8);
-      acc0 = mfma16(block_neg_dm32(ch0[g]), b, acc0);
-      if (GATEUP) acc1 = mfma16(block_neg_dm32(ch1[g]), b, acc1);
+      acc0 = mfma16(block_neg_dm32(live ? ch0[g] : z), b, acc0);
+      if (GATEUP) acc1 = mfma16(block_neg_dm32(live ? ch1[g] : z), b, acc1);
     }
   }
 
@@ -290,7 +299,7 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
         if (GATEUP) red[wave - 1][(4 + e) * 64 + lane] = acc1[e];
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave > 0) return;
     for (int w = 0; w < KS - 1; ++w) {
 #pragma unroll
