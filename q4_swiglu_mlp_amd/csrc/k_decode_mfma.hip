@@ -1,4 +1,5 @@
-// Decode for 2 <= M <= 8 tokens: the two HBM-bound Q4_K passes on 16x16x32
+// Decode for 2 <= M <= 8 tokens (one launch per pass, up to eight token
+// columns of the MFMA): the two HBM-bound Q4_K passes on 16x16x32
 // MFMAs, so the Q4_K decode work (the VALU cost) does not grow with M.
 //
 //   k_decode<GATEUP=true>  streams W_gate and W_up once against one staging of
@@ -60,9 +61,15 @@ constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_SHR4 = 0x114;   // row_shr:4 (lanes 0-3 of each row of 16 read 0)
 
-// Launch shapes: KS waves per workgroup, at most NBW super-blocks per wave per pass.
-constexpr int KS_GU = 4, NBW_GU = 4;
-constexpr int KS_DN = 11, NBW_DN = 4;
+// Launch shapes: KS waves per workgroup, at most NBW super-blocks per wave per
+// pass.  Eight tokens take half the blocks per pass, so that their staged
+// activation still fits LDS (60 KB for gate/up, two workgroups per CU; 134 KB
+// for down).
+template <int MM, bool GATEUP>
+struct DecShape {
+  static constexpr int KS = GATEUP ? 4 : 11;
+  static constexpr int NBW = MM > 4 ? 2 : 4;
+};
 
 // Scales of the two chunks a lane decodes in every block: chunk c0 = sel and
 // c1 = 2 + sel (sel = (o >> 1) & 1).  s = RNE16(d*sc) exactly, as
@@ -325,12 +332,14 @@ template <int MM>
 void launch_group_mfma(const void* wg, const void* wu, const void* wd, int hidden, int inter, const _Float16* x,
                        _Float16* y, _Float16* h, int M, float gu_scale, float dn_scale, const _Float16* res,
                        float res_scale, int stage, hipStream_t stream) {
+  typedef DecShape<MM, true> GU;
+  typedef DecShape<MM, false> DN;
   if (stage == 0) {
-    hipLaunchKernelGGL((k_decode<MM, true, KS_GU, NBW_GU>), dim3(inter / 16), dim3(64 * KS_GU), 0, stream,
+    hipLaunchKernelGGL((k_decode<MM, true, GU::KS, GU::NBW>), dim3(inter / 16), dim3(64 * GU::KS), 0, stream,
                        static_cast<const uint8_t*>(wg), static_cast<const uint8_t*>(wu), hidden, inter, x, M, h,
                        gu_scale, (const _Float16*)nullptr, 0.0f);
   } else {
-    hipLaunchKernelGGL((k_decode<MM, false, KS_DN, NBW_DN>), dim3(hidden / 16), dim3(64 * KS_DN), 0, stream,
+    hipLaunchKernelGGL((k_decode<MM, false, DN::KS, DN::NBW>), dim3(hidden / 16), dim3(64 * DN::KS), 0, stream,
                        static_cast<const uint8_t*>(wd), static_cast<const uint8_t*>(nullptr), inter, hidden, h, M,
                        y, dn_scale, res, res_scale);
   }
@@ -343,8 +352,10 @@ void launch_tokens_mfma(const void* wg, const void* wu, const void* wd, int hidd
     launch_group_mfma<1>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, res, res_scale, stage, stream);
   else if (M <= 2)
     launch_group_mfma<2>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, res, res_scale, stage, stream);
-  else
+  else if (M <= 4)
     launch_group_mfma<4>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, res, res_scale, stage, stream);
+  else
+    launch_group_mfma<8>(wg, wu, wd, hidden, inter, x, y, h, M, gu_scale, dn_scale, res, res_scale, stage, stream);
 }
 
 }  // namespace
@@ -358,11 +369,12 @@ hipError_t launch_decode_mfma(const void* wg, const void* wu, const void* wd, in
   _Float16* hbuf = static_cast<_Float16*>(ws);
   const float gu_scale = ldexpf(1.0f, -inter_shift);
   const float dn_scale = ldexpf(1.0f, inter_shift - out_shift) * mlp_scale, res_scale = ldexpf(1.0f, -out_shift);
-  // groups of at most four tokens (the staged activation of one group fits LDS)
+  // groups of at most eight tokens (the 16 columns of the MFMA hold them all,
+  // so each weight is read once per call)
   for (int stage = 0; stage < 2; ++stage) {
     timing_begin(stream);
-    for (int t0 = 0; t0 < M; t0 += 4) {
-      const int mg = min(4, M - t0);
+    for (int t0 = 0; t0 < M; t0 += 8) {
+      const int mg = min(8, M - t0);
       launch_tokens_mfma(wg, wu, wd, hidden, inter, xh + (size_t)t0 * hidden, yh + (size_t)t0 * hidden,
                          hbuf + (size_t)t0 * inter, mg, gu_scale, dn_scale, rh ? rh + (size_t)t0 * hidden : nullptr,
                          res_scale, stage, stream);
