@@ -124,7 +124,10 @@ __device__ __forceinline__ int piece_slot(int bl, int c, int j) {
 }
 
 template <int MM, bool GATEUP, int KS, int NBW>
-__global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
+// Three waves per SIMD (at most 168 VGPRs): with 53 KB of LDS, three 4-wave
+// gate/up workgroups share a CU, so the 688 tiles of an 11,008-row pass are
+// all resident at once instead of 512 and a second round of 176.
+__global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
                                                     int K, int N, const _Float16* __restrict__ xin, int M,
                                                     _Float16* out, float scale, const _Float16* res,
                                                     float res_scale) {
@@ -133,12 +136,16 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
   constexpr int NPIECE = MM * NBW * 32;       // pieces of 8 halves per pass
   constexpr int NPIT = (NPIECE + 63) / 64;
   constexpr int NG = (NBW + 3) / 4;           // min-correction groups per pass
+  constexpr int NPC = NBW * 144;              // 16-byte weight pieces per matrix and pass
+  constexpr int NLD = (NPC + 63) / 64;        // coalesced loads per matrix and pass
   __shared__ __attribute__((aligned(16))) _Float16 xs_all[KS][MM * TSTRIDE];
   __shared__ __attribute__((aligned(16))) _Float16 xm_all[KS][MM * NBW * 8];
-  __shared__ float red[KS > 1 ? KS - 1 : 1][NMAT * 4 * 64];
   // per wave and matrix: one block column of the tile (16 rows x 9 pieces of
-  // 16 B), written in load order and read back in the MFMA lane layout
+  // 16 B), written in load order and read back in the MFMA lane layout.  After
+  // its last block a wave leaves its partial sums for wave 0 in its own area
+  // (NMAT x 4 x 64 floats), which no other wave touches.
   __shared__ __attribute__((aligned(16))) u32x4 wt_all[KS][NMAT][16 * 9];
+  static_assert(sizeof(wt_all[0]) >= NMAT * 4 * 64 * sizeof(float), "partial sums fit a wave's weight area");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches below
@@ -151,17 +158,9 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
   const int b0 = (int)((long long)wave * nb / KS), b1 = (int)((long long)(wave + 1) * nb / KS);
   const int per_wave_max = (nb + KS - 1) / KS;
   const int npass = (per_wave_max + NBW - 1) / NBW;   // the same for every wave of the block
-  const size_t row_bytes = (size_t)nb * BLOCK_BYTES;
-  const uint8_t* row0 = W0 + (size_t)(tile * 16 + r) * row_bytes;
-  const uint8_t* row1 = GATEUP ? W1 + (size_t)(tile * 16 + r) * row_bytes : nullptr;
-  // coalesced weight loads: piece p = 64k + lane (k < 3, p < 144) of a block
-  // column is row p/9, bytes [16*(p%9), +16) of that row's block
-  size_t poff[3];
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int p = min(64 * k + lane, 143);
-    poff[k] = (size_t)(tile * 16 + p / 9) * row_bytes + 16 * (p % 9);
-  }
+  const uint32_t row_bytes = (uint32_t)nb * BLOCK_BYTES;
+  const uint8_t* tile0 = W0 + (size_t)tile * 16 * row_bytes;
+  const uint8_t* tile1 = GATEUP ? W1 + (size_t)tile * 16 * row_bytes : nullptr;
   u32x4* wt0 = wt_all[wave][0];
   u32x4* wt1 = wt_all[wave][NMAT - 1];
   _Float16* xs = xs_all[wave];
@@ -190,24 +189,26 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
       xl[it] = *reinterpret_cast<const uint2*>(src);
       xh[it] = *reinterpret_cast<const uint2*>(src + 32);
     }
-    u32x4 w0[NBW][3], w1[NBW][3];   // raw pieces k = 0, 1, 2 of the coalesced loads
+    // The NBW block columns of a pass are NPC pieces of 16 B per matrix, read
+    // by NLD coalesced loads: piece p = 64k + lane is block p/144 of the pass,
+    // row (p%144)/9, bytes [16*(p%9), +16) of that row's block.  Pieces past
+    // NPC re-read the last one (in bounds, unused).
+    u32x4 w0[NLD], w1[NLD];
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int pc = min(64 * k + lane, NPC - 1);
+      const int bl = pc / 144, q = pc - 144 * bl;
+      const uint32_t off = (uint32_t)(q / 9) * row_bytes + 16u * (uint32_t)(q % 9) +
+                           (uint32_t)min(pb + bl, blast) * BLOCK_BYTES;
+      w0[k] = *reinterpret_cast<const u32x4*>(tile0 + off);
+      if (GATEUP) w1[k] = *reinterpret_cast<const u32x4*>(tile1 + off);
+    }
+    // headers of the min correction (octet o of group g takes block 4g+o),
+    // picked from the LDS copy of each block column as it is read below; an
+    // octet past the pass's blocks keeps a zero header, hence a zero A operand
     uint4 ch0[NG], ch1[NG];
 #pragma unroll
-    for (int bl = 0; bl < NBW; ++bl) {
-      const size_t boff = (size_t)min(pb + bl, blast) * BLOCK_BYTES;
-      // lanes 16..63 of the third load re-read piece 143 (in bounds, unused)
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        w0[bl][k] = *reinterpret_cast<const u32x4*>(W0 + poff[k] + boff);
-        if (GATEUP) w1[bl][k] = *reinterpret_cast<const u32x4*>(W1 + poff[k] + boff);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const size_t boff = (size_t)min(pb + 4 * g + o, blast) * BLOCK_BYTES;
-      ch0[g] = *reinterpret_cast<const uint4*>(row0 + boff);
-      if (GATEUP) ch1[g] = *reinterpret_cast<const uint4*>(row1 + boff);
-    }
+    for (int g = 0; g < NG; ++g) ch0[g] = ch1[g] = make_uint4(0, 0, 0, 0);
     // 2. stage this pass's activation pieces and sub-block means.  The LDS
     //    areas of the pass loop belong to one wave each, whose LDS accesses
     //    complete in program order, so no workgroup barrier is needed; the
@@ -248,14 +249,14 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
       if (bl >= cnt) return;   // wave-uniform
       // through LDS into the MFMA layout: lane (r, o) takes row r's header and
       // quant runs [16o, +16) and [64+16o, +16)
-      wt0[lane] = w0[bl][0];
-      wt0[64 + lane] = w0[bl][1];
-      if (lane < 16) wt0[128 + lane] = w0[bl][2];
-      if (GATEUP) {
-        wt1[lane] = w1[bl][0];
-        wt1[64 + lane] = w1[bl][1];
-        if (lane < 16) wt1[128 + lane] = w1[bl][2];
-      }
+      static_for<(144 * bl + 143) / 64 - (144 * bl) / 64 + 1>([&](auto kc) {
+        constexpr int k = (144 * bl) / 64 + decltype(kc)::value;
+        const int q = 64 * k + lane - 144 * bl;
+        if (q >= 0 && q < 144) {
+          wt0[q] = w0[k];
+          if (GATEUP) wt1[q] = w1[k];
+        }
+      });
       DecBlock db0, db1;
       db0.hdr = as_uint4(wt0[9 * r]);
       db0.q0 = as_uint4(wt0[9 * r + 1 + o]);
@@ -264,6 +265,10 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
         db1.hdr = as_uint4(wt1[9 * r]);
         db1.q0 = as_uint4(wt1[9 * r + 1 + o]);
         db1.q1 = as_uint4(wt1[9 * r + 5 + o]);
+      }
+      if (o == (bl & 3)) {
+        ch0[bl >> 2] = db0.hdr;
+        if (GATEUP) ch1[bl >> 2] = db1.hdr;
       }
       const LaneChunkS s0 = lane_chunk_scales(db0.hdr, sel);
       LaneChunkS s1;
@@ -287,32 +292,33 @@ __global__ __launch_bounds__(64 * KS) void k_decode(const uint8_t* __restrict__ 
     for (int g = 0; g < NG; ++g) {
       if (4 * g >= cnt) continue;   // wave-uniform
       const int bl = 4 * g + o;
-      // octets past the pass's blocks take a zero header, hence a zero A
-      // operand; they read the means of a staged block (finite) instead
-      const bool live = bl < cnt;
-      const uint4 z = make_uint4(0, 0, 0, 0);
+      // octets past the pass's blocks (zero headers) read the means of a staged
+      // block (finite)
       const half8 b = *reinterpret_cast<const half8*>(xm + (tb * NBW + min(bl, cnt - 1)) * 8);
-      acc0 = mfma16(block_neg_dm32(live ? ch0[g] : z), b, acc0);
-      if (GATEUP) acc1 = mfma16(block_neg_dm32(live ? ch1[g] : z), b, acc1);
+      acc0 = mfma16(block_neg_dm32(ch0[g]), b, acc0);
+      if (GATEUP) acc1 = mfma16(block_neg_dm32(ch1[g]), b, acc1);
     }
   }
 
   // 4. the KS partial sums meet in wave 0
   if (KS > 1) {
+    wave_lds_order();   // the wave's last weight reads stay before these writes
     if (wave > 0) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        red[wave - 1][e * 64 + lane] = acc0[e];
-        if (GATEUP) red[wave - 1][(4 + e) * 64 + lane] = acc1[e];
+        float* red = reinterpret_cast<float*>(wt_all[wave]);
+        red[e * 64 + lane] = acc0[e];
+        if (GATEUP) red[(4 + e) * 64 + lane] = acc1[e];
       }
     }
     lds_barrier();
     if (wave > 0) return;
-    for (int w = 0; w < KS - 1; ++w) {
+    for (int w = 1; w < KS; ++w) {
+      const float* red = reinterpret_cast<const float*>(wt_all[w]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc0[e] += red[w][e * 64 + lane];
-        if (GATEUP) acc1[e] += red[w][(4 + e) * 64 + lane];
+        acc0[e] += red[e * 64 + lane];
+        if (GATEUP) acc1[e] += red[(4 + e) * 64 + lane];
       }
     }
   }
