@@ -172,13 +172,10 @@ __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict
   for (int pass = 0; pass < npass; ++pass) {
     const int pb = b0 + pass * NBW;                   // first block of this pass
     const int cnt = max(0, min(NBW, b1 - pb));        // wave-uniform
-    // 1. activation loads first (the staging below waits only for them), then
-    //    every weight load of the pass, then the headers of the min correction
-    //    (octet o of group g takes block 4g+o)
-    //    Every load is issued, whatever cnt is: a block past the wave's range
-    //    reads the wave's last block (or block 0 when the range is empty)
-    //    instead, and its result is discarded below.  With a fixed number of
-    //    loads in flight the compiler can wait for the activations alone.
+    // 1. the activation loads of the pass.  Every load of a pass is issued,
+    //    whatever cnt is: a block past the wave's range reads the wave's last
+    //    block (or block 0 when the range is empty) instead, and its result is
+    //    discarded below, so the compiler can count the loads in flight.
     const int blast = max(b1 - 1, 0);
     uint2 xl[NPIT], xh[NPIT];
 #pragma unroll
@@ -189,26 +186,6 @@ __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict
       xl[it] = *reinterpret_cast<const uint2*>(src);
       xh[it] = *reinterpret_cast<const uint2*>(src + 32);
     }
-    // The NBW block columns of a pass are NPC pieces of 16 B per matrix, read
-    // by NLD coalesced loads: piece p = 64k + lane is block p/144 of the pass,
-    // row (p%144)/9, bytes [16*(p%9), +16) of that row's block.  Pieces past
-    // NPC re-read the last one (in bounds, unused).
-    u32x4 w0[NLD], w1[NLD];
-#pragma unroll
-    for (int k = 0; k < NLD; ++k) {
-      const int pc = min(64 * k + lane, NPC - 1);
-      const int bl = pc / 144, q = pc - 144 * bl;
-      const uint32_t off = (uint32_t)(q / 9) * row_bytes + 16u * (uint32_t)(q % 9) +
-                           (uint32_t)min(pb + bl, blast) * BLOCK_BYTES;
-      w0[k] = *reinterpret_cast<const u32x4*>(tile0 + off);
-      if (GATEUP) w1[k] = *reinterpret_cast<const u32x4*>(tile1 + off);
-    }
-    // headers of the min correction (octet o of group g takes block 4g+o),
-    // picked from the LDS copy of each block column as it is read below; an
-    // octet past the pass's blocks keeps a zero header, hence a zero A operand
-    uint4 ch0[NG], ch1[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) ch0[g] = ch1[g] = make_uint4(0, 0, 0, 0);
     // 2. stage this pass's activation pieces and sub-block means.  The LDS
     //    areas of the pass loop belong to one wave each, whose LDS accesses
     //    complete in program order, so no workgroup barrier is needed; the
@@ -242,7 +219,34 @@ __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict
     }
     wave_lds_order();
 
-    // 3. MFMAs: 8 per block and matrix, then the min correction per 4 blocks
+    // 3. the weight loads, issued only once the activation is staged: issued
+    //    beside a flood of weight loads, the activation loads wait in the same
+    //    queues, and a wave could not start on a block column that has
+    //    arrived (per-wave timestamps: 4 to 14 us after the start).  The
+    //    scheduling barriers keep the loads here.
+    __builtin_amdgcn_sched_barrier(0);
+    // The NBW block columns of a pass are NPC pieces of 16 B per matrix, read
+    // by NLD coalesced loads: piece p = 64k + lane is block p/144 of the pass,
+    // row (p%144)/9, bytes [16*(p%9), +16) of that row's block.  Pieces past
+    // NPC re-read the last one (in bounds, unused).
+    u32x4 w0[NLD], w1[NLD];
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int pc = min(64 * k + lane, NPC - 1);
+      const int bl = pc / 144, q = pc - 144 * bl;
+      const uint32_t off = (uint32_t)(q / 9) * row_bytes + 16u * (uint32_t)(q % 9) +
+                           (uint32_t)min(pb + bl, blast) * BLOCK_BYTES;
+      w0[k] = *reinterpret_cast<const u32x4*>(tile0 + off);
+      if (GATEUP) w1[k] = *reinterpret_cast<const u32x4*>(tile1 + off);
+    }
+    // headers of the min correction (octet o of group g takes block 4g+o),
+    // picked from the LDS copy of each block column as it is read below; an
+    // octet past the pass's blocks keeps a zero header, hence a zero A operand
+    uint4 ch0[NG], ch1[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) ch0[g] = ch1[g] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // 4. MFMAs: 8 per block and matrix, then the min correction per 4 blocks
     const _Float16* xb = xs + tb * TSTRIDE + o * 8;
     static_for<NBW>([&](auto blc) {
       constexpr int bl = decltype(blc)::value;
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict
     }
   }
 
-  // 4. the KS partial sums meet in wave 0
+  // 5. the KS partial sums meet in wave 0
   if (KS > 1) {
     wave_lds_order();   // the wave's last weight reads stay before these writes
     if (wave > 0) {
