@@ -298,6 +298,18 @@ def test_decode_workloads(name, layer):
     assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift), y_ref, f"{name} layer {layer}")
 
 
+@pytest.mark.parametrize("M", [6, 8])
+def test_decode_eight_token_group_full_size(M):
+    # five to eight tokens share one launch per pass (two blocks per wave and
+    # pass), here at the 4096/11008 shape: the down pass takes two passes
+    w = S.WORKLOADS["decode_m4"]
+    wg, wu, wd = S.layer_weights(w.seed, 5, w.hidden, w.inter)
+    x = S.gen_x(np.random.default_rng(880 + M), M, w.hidden)
+    y_ref, h_ref = O.mlp(x, wg, wu, wd, w.hidden, w.inter)
+    a, b = shifts_for(y_ref, h_ref)
+    assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, a, b), y_ref, f"decode 4096/11008 M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 4])
 def test_decode_repeated_calls_reuse_workspace(M):
     # back-to-back calls on one workspace (filled with garbage first) give the
@@ -320,7 +332,7 @@ def test_decode_repeated_calls_reuse_workspace(M):
 # the MFMA decode kernels at hidden widths of one to three 4096-wide spans,
 # and one that is not a multiple of 4096 (the K split's last pass ragged)
 @pytest.mark.parametrize("H", [4096, 4352, 8192, 12288])
-@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8])
 def test_decode_mfma_hidden_widths(M, H):
     I = 768
     wg, wu, wd, x = _rand_mlp(4100 + M + H, H, I, M)
