@@ -41,13 +41,14 @@ def test_noalloc_limit_rejected_on_the_host():
 
 @pytest.mark.gpu
 def test_noalloc_matches_decode_on_two_calls_in_a_row():
-    # first call: 4096/11008, M = 4 (88 KB of intermediate); second: a smaller
-    # layer and M = 1, reading the array the first call left behind
+    # first call: 4096/11008, M = 8 (176 KB of intermediate, the eight-token
+    # kernels); second: a smaller layer and M = 1, reading the array the first
+    # call left behind
     cases = []
     w = S.WORKLOADS["decode_m4"]
     wg, wu, wd = S.layer_weights(w.seed, 5, w.hidden, w.inter)
-    cases.append((wg, wu, wd, w.hidden, w.inter, S.workload_x(w)))
     rng = np.random.default_rng(17)
+    cases.append((wg, wu, wd, w.hidden, w.inter, S.gen_x(rng, 8, w.hidden)))
     H, I = 1024, 2816
     cases.append((S.gen_q4k_blob(rng, I, H), S.gen_q4k_blob(rng, I, H), S.gen_q4k_blob(rng, H, I), H, I,
                   S.gen_x(rng, 1, H)))
