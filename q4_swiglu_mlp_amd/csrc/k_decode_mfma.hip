@@ -9,10 +9,12 @@
 //   k_decode<GATEUP=false> streams W_down against it and writes y.
 //
 // Shape.  A workgroup owns one 16-row tile of the output and KS waves; wave w
-// takes an even share of the tile's super-block columns, loads all of them at
-// once (consecutive lanes read consecutive 16-byte pieces of a row) and passes
-// each block column through LDS into the MFMA lane layout; the KS partial sums
-// meet through LDS at the end.
+// takes an even share of the tile's super-block columns and walks them in
+// passes of NBW columns.  Per pass it stages its slice of the activation in
+// its own LDS area, then issues the pass's weight loads (consecutive lanes read
+// consecutive 16-byte pieces of the rows' blocks, packed across the pass's
+// columns) and passes each block column through LDS into the MFMA lane layout
+// as it arrives; the KS partial sums meet through LDS at the end.
 //
 // Arithmetic.  Lane l holds row l%16 of the weight tile and token l%16 of the
 // activation, eight K values each (octet o = l/16); token columns beyond M are
@@ -123,10 +125,10 @@ __device__ __forceinline__ int piece_slot(int bl, int c, int j) {
   return (bl * 8 + i) * 4 + o;
 }
 
-template <int MM, bool GATEUP, int KS, int NBW>
 // Three waves per SIMD (at most 168 VGPRs): with 53 KB of LDS, three 4-wave
 // gate/up workgroups share a CU, so the 688 tiles of an 11,008-row pass are
 // all resident at once instead of 512 and a second round of 176.
+template <int MM, bool GATEUP, int KS, int NBW>
 __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
                                                     int K, int N, const _Float16* __restrict__ xin, int M,
                                                     _Float16* out, float scale, const _Float16* res,
