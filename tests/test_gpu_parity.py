@@ -277,7 +277,7 @@ def test_decode_tiny_workload(M):
     assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift), y_ref, f"decode tiny M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("M", [1, 4, 8])
 def test_decode_long_down_contraction(M):
     # inter = 16640 > 16384: longer than the M = 1 row kernels cover, so both M
     # take the MFMA passes; the prefill kernel runs the same shape
