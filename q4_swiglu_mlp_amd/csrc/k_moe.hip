@@ -136,7 +136,7 @@ __device__ int build_tile_table(int e, int E, int c, int MT, int* s0, int* s1, i
   s2[e] = ra;
   s3[e] = fb;
   s4[e] = rb;
-  __syncthreads();
+  lds_barrier();
   // inclusive Hillis-Steele scans over the first P entries, P the power of
   // two at or above E (the entries from E on are zero, so entry P - 1 holds
   // the totals and later entries are never read)
@@ -148,13 +148,13 @@ __device__ int build_tile_table(int e, int E, int c, int MT, int* s0, int* s1, i
     const int a2 = (e >= d) ? s2[e - d] : 0;
     const int a3 = (e >= d) ? s3[e - d] : 0;
     const int a4 = (e >= d) ? s4[e - d] : 0;
-    __syncthreads();
+    lds_barrier();
     s0[e] += a0;
     s1[e] += a1;
     s2[e] += a2;
     s3[e] += a3;
     s4[e] += a4;
-    __syncthreads();
+    lds_barrier();
   }
   const int off = s0[e] - c;   // exclusive
   const int tfa = s1[P - 1], tra = s2[P - 1], tfb = s3[P - 1], trb = s4[P - 1];
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
   __shared__ int s0[1024], s1[1024], s2[1024], s3[1024], s4[1024];
   const int e = threadIdx.x;
   cnt[e] = 0;
-  __syncthreads();
+  lds_barrier();
   bool bad = false;
   for (int i = threadIdx.x; i < n_slots; i += 1024) {
     const int x = ids[i];
@@ -252,15 +252,15 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
       bad = true;
   }
   if (bad && dev_error) atomicOr(dev_error, 1);
-  __syncthreads();
+  lds_barrier();
   const int c = (e < E) ? cnt[e] : 0;
   const int off = build_tile_table(e, E, c, MT, s0, s1, s2, s3, s4, offsets, tile_expert, tile_start, tile_rows,
                                    n_tiles);
-  __syncthreads();
+  lds_barrier();
   s1[e] = small_expert(c, MT) ? kPosSmall : 0;   // the expert's position flag
-  __syncthreads();
+  lds_barrier();
   cnt[e] = off;   // the expert's cursor
-  __syncthreads();
+  lds_barrier();
   for (int i = threadIdx.x; i < n_slots; i += 1024) {
     const int x = ids[i];
     if (x >= 0 && x < E) {
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(MoeCfg::THREADS) void k_moe_fused16(
     if (threadIdx.x < MT_MOE) tok[threadIdx.x] = t;
     slot_of_row[threadIdx.x] = sl;
   }
-  __syncthreads();
+  lds_barrier();
   const int npan = I / 64;
   const int r0 = (int)((long long)chunk * npan / nc) * 64;
   const int r1 = (int)((long long)(chunk + 1) * npan / nc) * 64;
