@@ -221,10 +221,10 @@ __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict
     }
     wave_lds_order();
 
-    // 3. the weight loads, issued only once the activation is staged: issued
-    //    beside a flood of weight loads, the activation loads wait in the same
-    //    queues, and a wave could not start on a block column that has
-    //    arrived (per-wave timestamps: 4 to 14 us after the start).  The
+    // 3. the weight loads, issued only once the activation is staged.  Issued
+    //    together, the activation loads queue behind every tile's weight
+    //    loads (they landed 4 to 14 us after a wave's start), and a wave
+    //    cannot start on block columns that have already arrived.  The
     //    scheduling barriers keep the loads here.
     __builtin_amdgcn_sched_barrier(0);
     // The NBW block columns of a pass are NPC pieces of 16 B per matrix, read
