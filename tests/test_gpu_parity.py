@@ -329,9 +329,10 @@ def test_decode_repeated_calls_reuse_workspace(M):
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
 
 
-# the MFMA decode kernels at hidden widths of one to three 4096-wide spans,
-# and one that is not a multiple of 4096 (the K split's last pass ragged)
-@pytest.mark.parametrize("H", [4096, 4352, 8192, 12288])
+# the MFMA decode kernels at hidden widths of one to four 4096-wide spans (the
+# library's maximum, eight passes per wave at eight tokens), and one that is
+# not a multiple of 4096 (the K split's last pass ragged)
+@pytest.mark.parametrize("H", [4096, 4352, 8192, 12288, 16384])
 @pytest.mark.parametrize("M", [2, 3, 4, 5, 8])
 def test_decode_mfma_hidden_widths(M, H):
     I = 768
