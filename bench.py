@@ -716,9 +716,10 @@ def staged_lines(args, torch, np, Z, S, dev, t):
     return out
 
 
-def decode_graph_us(torch, Z, layers, w, gx, y, ws, replays=10):
+def decode_graph_us(torch, Z, layers, w, gx, y, ws, replays=30, warm_s=0.1):
     """Per-layer time of the 32-layer sweep captured once in a HIP graph and
-    replayed: the device-side rate without the host's per-call launch cost."""
+    replayed: the device-side rate without the host's per-call launch cost,
+    timed after at least warm_s seconds of back-to-back replays."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -730,8 +731,10 @@ def decode_graph_us(torch, Z, layers, w, gx, y, ws, replays=10):
     with torch.cuda.graph(g):
         for lg, lu, ld in layers:
             Z.zinc_mlp_q4k_decode(lg, lu, ld, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
-    g.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        g.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(replays):
         g.replay()
