@@ -87,7 +87,8 @@ PATHS = {
     "decode_rows_m1_w": ("decode", 4352, 1280, 1),    # two chunk slots per lane in the gate/up pass
     "decode_mfma_m4": ("decode", 1024, 2816, 4),      # 16x16x32 MFMA decode
     "decode_mfma_m3_w": ("decode", 4352, 1280, 3),    # a hidden width that is not a multiple of 4096
-    "decode_mfma_m7": ("decode", 1024, 2816, 7),      # two token groups, the second ragged
+    "decode_mfma_m7": ("decode", 1024, 2816, 7),      # the eight-token kernels, one token column unused
+    "decode_mfma_m8": ("decode", 4352, 1280, 8),      # all eight columns, two blocks per wave and pass
 }
 
 
@@ -228,11 +229,11 @@ def test_centred_prefill_m2048_sampled_tokens():
     assert_parity(y[rows], y_ref, f"centred prefill M=2048, {len(rows)} sampled tokens")
 
 
-@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("M", [1, 4, 8])
 def test_centred_decode_full_shape(M):
     w = S.WORKLOADS["decode_m4"]
     wg, wu, wd = _centred_layer(2)
-    x = S.workload_x(w)[:M]
+    x = S.workload_x(w)[:M] if M <= 4 else S.gen_x(np.random.default_rng(990), M, w.hidden)
     y_ref, h_ref = O.mlp(x, wg, wu, wd, w.hidden, w.inter)
     a, b = shifts_for(y_ref, h_ref)
     assert_parity(decode(wg, wu, wd, w.hidden, w.inter, x, a, b), y_ref, f"centred decode 4096/11008 M={M}")
