@@ -89,6 +89,7 @@ __device__ __forceinline__ void fused_unit128(const uint8_t* __restrict__ wg, co
   constexpr int NG = C::NGMAX, XSH = C::XSH, HS = C::HS, HSS = C::HSS, MT = C::MT, NC = C::NCOPY;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, o = lane >> 4, sel = (o >> 1) & 1;
+  const uint32_t psel = sc_pair_sel(2 * sel);   // lane16_scales
   const int tid = threadIdx.x;
   const int nbH = H / QK;
   const uint32_t rowb = (uint32_t)nbH * BLOCK_BYTES;
@@ -166,7 +167,7 @@ __device__ __forceinline__ void fused_unit128(const uint8_t* __restrict__ wg, co
       const int kn = (kb + 1 < nbH) ? kb + 1 : kb;
       const uint32_t noff = wrow_off + (uint32_t)kn * BLOCK_BYTES;
       if (act) {
-        const Lane16S sg = lane16_scales(as_u4(hg), sel), su = lane16_scales(as_u4(hu), sel);
+        const Lane16S sg = lane16_scales(as_u4(hg), psel), su = lane16_scales(as_u4(hu), psel);
         const bool mine = o == (kb & 3);
         cg = mine ? hg : cg;
         cu = mine ? hu : cu;
@@ -182,8 +183,8 @@ __device__ __forceinline__ void fused_unit128(const uint8_t* __restrict__ wg, co
         auto decode = [&](int i, half8& ag, half8& au) {
           const uint32_t qg = (i < 4) ? qg0[i & 3] : qg1[i & 3];
           const uint32_t qu = (i < 4) ? qu0[i & 3] : qu1[i & 3];
-          ag = (i < 4) ? dequant_dword_sc(qg, sg.lo0, sg.hi0, nk) : dequant_dword_sc(qg, sg.lo1, sg.hi1, nk);
-          au = (i < 4) ? dequant_dword_sc(qu, su.lo0, su.hi0, nk) : dequant_dword_sc(qu, su.lo1, su.hi1, nk);
+          ag = dequant_dword_sc(qg, (i < 4) ? sg.r0 : sg.r1, nk);
+          au = dequant_dword_sc(qu, (i < 4) ? su.r0 : su.r1, nk);
         };
         // Eight token groups leave no room for a second set of B operands:
         // each group's B is refilled in place right after its two MFMAs, a

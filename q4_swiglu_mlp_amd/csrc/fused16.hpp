@@ -106,49 +106,77 @@ struct Fused16Smem {
   int p2_next;                          // phase 2: next unclaimed output tile
 };
 
-// Scales of the two chunks a lane decodes per block (chunk c0 = sel, c1 =
-// 2 + sel): s = RNE16(d*sc) as (1024 + sc)*d - 1024*d, rounded once, each
-// packed with its offset constant (-1024*s for the low-nibble sub-block, -64*s
-// for the high one) as (s, c): one register per sub-block.
+// Scale registers of the decode below.  A sub-block's s = RNE16(d*sc) is
+// taken as (1024 + sc)*d - 1024*d, rounded once, and then scaled exactly by a
+// power of two: a register holds (1024*s_a, 64*s_b) for a low-nibble
+// sub-block a and the high-nibble sub-block b of the same 64-weight chunk.
+// The input is the fp16 pair (1024 + sc_a, 1024 + sc_b) as bits.
+__device__ __forceinline__ half2v scale_pair(uint32_t bits, half2v d2, half2v nd2) {
+  const half2v s = __builtin_elementwise_fma(bits_h2(bits), d2, nd2);
+  return s * half2v{(_Float16)1024.0f, (_Float16)64.0f};
+}
+
+// d of a block header (its low half) in both halves of a register.
+__device__ __forceinline__ half2v splat_d(uint32_t x) { return bits_h2(__builtin_amdgcn_perm(x, x, 0x01000100u)); }
+
+// Six-bit scales 0..3 (masked) and 4..7 (low four bits from word 3, top two
+// from bits 6..7 of word 1), one per byte.
+__device__ __forceinline__ uint32_t sc03_bytes(uint4 hdr) { return hdr.y & 0x3F3F3F3Fu; }
+__device__ __forceinline__ uint32_t sc47_bytes(uint4 hdr) {
+  return (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
+}
+
+// v_perm selector that turns bytes j and j + 1 of a word (src1) into the fp16
+// pair (1024 + byte_j, 1024 + byte_j+1): each half's high byte is 0x64, taken
+// from byte 0 of src0 = 0x64646464.
+__host__ __device__ constexpr uint32_t sc_pair_sel(int j) {
+  return 0x04000400u | ((uint32_t)(j + 1) << 16) | (uint32_t)j;
+}
+
+// The two chunks a lane decodes per block (chunk c0 = sel, c1 = 2 + sel):
+// r0 for sub-blocks (2 sel, 2 sel + 1), r1 for (4 + 2 sel, 5 + 2 sel);
+// psel = sc_pair_sel(2 sel).
 struct Lane16S {
-  half2v lo0, hi0, lo1, hi1;
+  half2v r0, r1;
 };
 
-__device__ __forceinline__ Lane16S lane16_scales(uint4 hdr, int sel) {
-  const SixBit sb = unpack_sixbit(hdr.y, hdr.z, hdr.w);
-  const uint32_t a = sb.sc03 >> (16 * sel);
-  const uint32_t b = sb.sc47 >> (16 * sel);
-  const uint32_t pl = (a & 0xFFu) | ((b & 0xFFu) << 16);
-  const uint32_t ph = ((a >> 8) & 0xFFu) | (((b >> 8) & 0xFFu) << 16);
-  const half2v d2 = splat_lo(hdr.x);
+__device__ __forceinline__ Lane16S lane16_scales(uint4 hdr, uint32_t psel) {
+  const half2v d2 = splat_d(hdr.x);
   const half2v nd = d2 * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const half2v slo = __builtin_elementwise_fma(bits_h2(pl | 0x64006400u), d2, nd);   // (s_2c0, s_2c1)
-  const half2v shi = __builtin_elementwise_fma(bits_h2(ph | 0x64006400u), d2, nd);   // (s_2c0+1, s_2c1+1)
-  const half2v klo = {(_Float16)1.0f, (_Float16)-1024.0f};
-  const half2v khi = {(_Float16)1.0f, (_Float16)-64.0f};
   Lane16S r;
-  r.lo0 = half2v{slo[0], slo[0]} * klo;
-  r.lo1 = half2v{slo[1], slo[1]} * klo;
-  r.hi0 = half2v{shi[0], shi[0]} * khi;
-  r.hi1 = half2v{shi[1], shi[1]} * khi;
+  r.r0 = scale_pair(__builtin_amdgcn_perm(0x64646464u, sc03_bytes(hdr), psel), d2, nd);
+  r.r1 = scale_pair(__builtin_amdgcn_perm(0x64646464u, sc47_bytes(hdr), psel), d2, nd);
   return r;
 }
 
-// dequant_dword_scaled with the packed (s, c) registers.
-__device__ __forceinline__ half8 dequant_dword_sc(uint32_t Q, half2v sc_lo, half2v sc_hi, const NibbleK& k) {
-  const half2v s_lo = __builtin_shufflevector(sc_lo, sc_lo, 0, 0), c_lo = __builtin_shufflevector(sc_lo, sc_lo, 1, 1);
-  const half2v s_hi = __builtin_shufflevector(sc_hi, sc_hi, 0, 0), c_hi = __builtin_shufflevector(sc_hi, sc_hi, 1, 1);
-  return dequant_dword_scaled(Q, s_lo, c_lo, s_hi, c_hi, k);
+// w' = q*s for the eight operand slots of one quant dword (the slot order of
+// dequant_dword_f16), from the register R = (1024*s_a, 64*s_b).  The nibble
+// becomes an fp16 in [1, 2) by OR-ing in the exponent of 1.0: a low nibble
+// reads 1 + q/1024, a high one (bits 4..7) 1 + q/64; fma(v, S, -S) is then
+// q*s exactly before its single rounding, with -S taken by a negation
+// modifier of the same register.
+__device__ __forceinline__ half8 dequant_dword_sc(uint32_t Q, half2v R, const NibbleK& k) {
+  const half2v S_lo = __builtin_shufflevector(R, R, 0, 0), S_hi = __builtin_shufflevector(R, R, 1, 1);
+  const uint32_t Q8 = Q >> 8;
+  const half2v p0 = __builtin_elementwise_fma(bits_h2((Q & k.lo_mask) | k.lo_magic), S_lo, -S_lo);
+  const half2v p1 = __builtin_elementwise_fma(bits_h2((Q8 & k.lo_mask) | k.lo_magic), S_lo, -S_lo);
+  const half2v p2 = __builtin_elementwise_fma(bits_h2((Q & k.hi_mask) | k.hi_magic), S_hi, -S_hi);
+  const half2v p3 = __builtin_elementwise_fma(bits_h2((Q8 & k.hi_mask) | k.hi_magic), S_hi, -S_hi);
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
 }
 
 // The nibble masks in SGPRs (a VALU operation may read one), the exponent
 // patterns in VGPRs: (q & mask) | magic stays one v_and_or_b32.
+// Both exponent patterns are 1.0 here (dequant_dword_sc).
 __device__ __forceinline__ NibbleK nibble_consts_s() {
   NibbleK k;
   asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(k.lo_mask));
   asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(k.hi_mask));
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.lo_magic));
-  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(k.hi_magic));
+  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(k.lo_magic));
+  k.hi_magic = k.lo_magic;
   return k;
 }
 
@@ -272,24 +300,14 @@ __global__ __launch_bounds__(256) void k_stage_x16(const _Float16* __restrict__ 
 
 inline size_t x16_staged_bytes(int M, int H) { return (size_t)(M + 1) * (H / QK) * X16_TP_BYTES; }
 
-// Scales of chunk CH (0..3) of a W_down block: sub-blocks 2*CH (low nibbles)
-// and 2*CH+1 (high), packed as (s, -1024*s) and (s, -64*s).
-struct PanelS {
-  half2v lo, hi;
-};
-
+// Scale register of chunk CH (0..3) of a W_down block: (1024*s_2CH,
+// 64*s_2CH+1), as in lane16_scales.
 template <int CH>
-__device__ __forceinline__ PanelS panel_scales(uint4 hdr) {
-  const SixBit sb = unpack_sixbit(hdr.y, hdr.z, hdr.w);
-  const uint32_t w = ((CH < 2) ? sb.sc03 : sb.sc47) >> (16 * (CH & 1));   // bytes sc_2CH, sc_2CH+1
-  const uint32_t v = (w & 0xFFu) | ((w & 0xFF00u) << 8);
-  const half2v d2 = splat_lo(hdr.x);
-  const half2v sp = __builtin_elementwise_fma(bits_h2(v | 0x64006400u), d2,
-                                              d2 * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f});
-  PanelS r;
-  r.lo = half2v{sp[0], sp[0]} * half2v{(_Float16)1.0f, (_Float16)-1024.0f};
-  r.hi = half2v{sp[1], sp[1]} * half2v{(_Float16)1.0f, (_Float16)-64.0f};
-  return r;
+__device__ __forceinline__ half2v panel_scales(uint4 hdr) {
+  const uint32_t w = (CH < 2) ? sc03_bytes(hdr) : sc47_bytes(hdr);
+  const half2v d2 = splat_d(hdr.x);
+  return scale_pair(__builtin_amdgcn_perm(0x64646464u, w, sc_pair_sel(2 * (CH & 1))), d2,
+                    d2 * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f});
 }
 
 // Output policies of phase 2.  store<NTT>() receives the 32-row accumulator
@@ -328,15 +346,13 @@ struct OutQuads {
 enum : int { kDownQ4K = 0, kDownQ5K = 1, kDownQ51 = 2 };
 
 // w' = q*s for one quant dword and its fifth bits: the Q4_K operand slots of
-// dequant_dword_scaled, with the fifth bit of each low nibble taken from bit
+// dequant_dword_sc, with the fifth bit of each low nibble taken from bit
 // 2*CH of the same byte of QH and that of each high nibble from bit 2*CH + 1,
-// OR'ed into the exponent patterns (1024 + q and 64 + q stay within one fp16
-// binade for q < 32).
+// OR'ed in above the nibble (1 + q/1024 and 1 + q/64 stay in [1, 2) for
+// q < 32).
 template <int CH>
-__device__ __forceinline__ half8 dequant5_dword_sc(uint32_t Q, uint32_t QH, half2v sc_lo, half2v sc_hi,
-                                                   const NibbleK& k) {
-  const half2v s_lo = __builtin_shufflevector(sc_lo, sc_lo, 0, 0), c_lo = __builtin_shufflevector(sc_lo, sc_lo, 1, 1);
-  const half2v s_hi = __builtin_shufflevector(sc_hi, sc_hi, 0, 0), c_hi = __builtin_shufflevector(sc_hi, sc_hi, 1, 1);
+__device__ __forceinline__ half8 dequant5_dword_sc(uint32_t Q, uint32_t QH, half2v R, const NibbleK& k) {
+  const half2v S_lo = __builtin_shufflevector(R, R, 0, 0), S_hi = __builtin_shufflevector(R, R, 1, 1);
   const uint32_t Q8 = Q >> 8, QH8 = QH >> 8;
   // bytes 0 and 2 (QH) and 1 and 3 (QH8): the low-nibble bit to 4 / 20, the
   // high-nibble bit to 8 / 24 (shifting the odd bytes down first keeps byte
@@ -344,13 +360,13 @@ __device__ __forceinline__ half8 dequant5_dword_sc(uint32_t Q, uint32_t QH, half
   auto lo_bits = [](uint32_t v) { return (4 - 2 * CH >= 0) ? (v << (4 - 2 * CH)) : (v >> (2 * CH - 4)); };
   auto hi_bits = [](uint32_t v) { return v << (7 - 2 * CH); };
   const half2v p0 =
-      __builtin_elementwise_fma(bits_h2((Q & k.lo_mask) | k.lo_magic | (lo_bits(QH) & 0x00100010u)), s_lo, c_lo);
+      __builtin_elementwise_fma(bits_h2((Q & k.lo_mask) | k.lo_magic | (lo_bits(QH) & 0x00100010u)), S_lo, -S_lo);
   const half2v p1 =
-      __builtin_elementwise_fma(bits_h2((Q8 & k.lo_mask) | k.lo_magic | (lo_bits(QH8) & 0x00100010u)), s_lo, c_lo);
+      __builtin_elementwise_fma(bits_h2((Q8 & k.lo_mask) | k.lo_magic | (lo_bits(QH8) & 0x00100010u)), S_lo, -S_lo);
   const half2v p2 =
-      __builtin_elementwise_fma(bits_h2((Q & k.hi_mask) | k.hi_magic | (hi_bits(QH) & 0x01000100u)), s_hi, c_hi);
+      __builtin_elementwise_fma(bits_h2((Q & k.hi_mask) | k.hi_magic | (hi_bits(QH) & 0x01000100u)), S_hi, -S_hi);
   const half2v p3 =
-      __builtin_elementwise_fma(bits_h2((Q8 & k.hi_mask) | k.hi_magic | (hi_bits(QH8) & 0x01000100u)), s_hi, c_hi);
+      __builtin_elementwise_fma(bits_h2((Q8 & k.hi_mask) | k.hi_magic | (hi_bits(QH8) & 0x01000100u)), S_hi, -S_hi);
   half8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
@@ -504,10 +520,10 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
     auto panel = [&](auto pc) {
       constexpr int P = decltype(pc)::value;
       if (P < NP && P < npan) {
-        const PanelS ps = panel_scales<(P + OFF) & 3>(dt.hdr[(P + OFF) >> 2]);
+        const half2v ps = panel_scales<(P + OFF) & 3>(dt.hdr[(P + OFF) >> 2]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const half8 b = dequant_dword_sc(dword_of(dt.qs[P], s), ps.lo, ps.hi, nk);
+          const half8 b = dequant_dword_sc(dword_of(dt.qs[P], s), ps, nk);
 #pragma unroll
           for (int tt = 0; tt < NTT; ++tt) {
             const half8 a = *reinterpret_cast<const half8*>(hs + (tt * 32 + l32) * HS + P * 64 + (2 * s + h) * 8);
@@ -560,10 +576,10 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
         constexpr int P = decltype(pc)::value;
         constexpr int CH = (P + OFF) & 3, K = (P + OFF) >> 2;
         if (P < NP && P < npan) {
-          const PanelS ps = panel_scales<CH>(dt.hdr[K]);
+          const half2v ps = panel_scales<CH>(dt.hdr[K]);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const half8 b = dequant5_dword_sc<CH>(dword_of(dt.qs[P], s), dword_of(dt.qh[K], s), ps.lo, ps.hi, nk);
+            const half8 b = dequant5_dword_sc<CH>(dword_of(dt.qs[P], s), dword_of(dt.qh[K], s), ps, nk);
             strip_mfma(acc, P, s, b);
           }
           dt.qs[P] = *reinterpret_cast<const uint4*>(nq + K * BB + 32 * CH);
@@ -603,9 +619,9 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
       auto panel = [&](auto pc) {
         constexpr int P = decltype(pc)::value;
         if (P < NP && P < npan) {
-          const half2v da = splat_lo(dt.ha[P].x), db = splat_lo(dt.hb[P].x);
-          const half2v slo = da * half2v{(_Float16)1.0f, (_Float16)-1024.0f};
-          const half2v shi = db * half2v{(_Float16)1.0f, (_Float16)-64.0f};
+          // (1024 * d_A, 64 * d_B): the scale register of dequant5_dword_sc
+          const half2v sab = bits_h2((dt.ha[P].x & 0xFFFFu) | (dt.hb[P].x << 16)) *
+                             half2v{(_Float16)1024.0f, (_Float16)64.0f};
           const uint32_t fa = dt.ha[P].y >> (16 * h), fb = dt.hb[P].y >> (16 * h);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
@@ -615,7 +631,7 @@ __device__ __forceinline__ void fu16_phase2(const uint8_t* __restrict__ wd, int 
             // four fifth bits to bit 0 of four bytes: x * 0x204081 puts bit e at 8e
             const uint32_t QH = ((((fa >> (4 * s)) & 0xFu) * 0x00204081u) & 0x01010101u) |
                                 (((((fb >> (4 * s)) & 0xFu) * 0x00204081u) & 0x01010101u) << 1);
-            strip_mfma(acc, P, s, dequant5_dword_sc<0>(Q, QH, slo, shi, nk));
+            strip_mfma(acc, P, s, dequant5_dword_sc<0>(Q, QH, sab, nk));
           }
           const uint8_t* nb = nxt + (size_t)(2 * (P + OFF)) * Q5_1_BLOCK_BYTES;
           dt.qa[P] = load_q51_quants(nb);
@@ -726,6 +742,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
   constexpr int XS = C::XS, HS = C::HS, HSS = C::HSS, MT = C::MT;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, o = lane >> 4, sel = (o >> 1) & 1;
+  const uint32_t psel = sc_pair_sel(2 * sel);   // lane16_scales
   const int nbH = H / QK;
   const size_t rowb = (size_t)nbH * BLOCK_BYTES;
   const NibbleK nk = nibble_consts_s();
@@ -816,7 +833,7 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
       _Float16* const xs_next = sm.u.xs[(kb + AHEAD) % SLOTS];
       _Float16* const xm_next = sm.xm[kx & (C::XRING - 1)];
       if constexpr (ACT) {
-        const Lane16S sg = lane16_scales(as_u4(hg), sel), su = lane16_scales(as_u4(hu), sel);
+        const Lane16S sg = lane16_scales(as_u4(hg), psel), su = lane16_scales(as_u4(hu), psel);
         // octet o keeps block (kb & ~3) + o's headers for the correction
         const bool mine = o == (kb & 3);
         cg = mine ? hg : cg;
@@ -834,8 +851,8 @@ __device__ __forceinline__ void fused_unit16(const uint8_t* __restrict__ wg, con
         auto decode = [&](int i, half8& ag, half8& au) {
           const uint32_t qg = (i < 4) ? qg0[i & 3] : qg1[i & 3];
           const uint32_t qu = (i < 4) ? qu0[i & 3] : qu1[i & 3];
-          ag = (i < 4) ? dequant_dword_sc(qg, sg.lo0, sg.hi0, nk) : dequant_dword_sc(qg, sg.lo1, sg.hi1, nk);
-          au = (i < 4) ? dequant_dword_sc(qu, su.lo0, su.hi0, nk) : dequant_dword_sc(qu, su.lo1, su.hi1, nk);
+          ag = dequant_dword_sc(qg, (i < 4) ? sg.r0 : sg.r1, nk);
+          au = dequant_dword_sc(qu, (i < 4) ? su.r0 : su.r1, nk);
         };
         // Five token groups leave no room for a second set of B operands:
         // there each group's B is refilled in place right after its two

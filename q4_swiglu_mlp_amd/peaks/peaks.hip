@@ -173,6 +173,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode_loop(const uint8_t* __res
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, o = lane >> 4, sel = (o >> 1) & 1;
+  const uint32_t psel = sc_pair_sel(2 * sel);
   const NibbleK nk = nibble_consts_s();
   const uint32_t rowb = (uint32_t)nblk * BLOCK_BYTES;
   const uint32_t wrow_off = (uint32_t)(wave * 16 + r) * rowb;
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode_loop(const uint8_t* __res
     for (int kb = 0; kb < nblk; ++kb) {
       const int kn = (kb + 1 < nblk) ? kb + 1 : 0;
       const uint32_t noff = wrow_off + (uint32_t)kn * BLOCK_BYTES;
-      const Lane16S sg = lane16_scales(as_u4(hg), sel), su = lane16_scales(as_u4(hu), sel);
+      const Lane16S sg = lane16_scales(as_u4(hg), psel), su = lane16_scales(as_u4(hu), psel);
       if constexpr (VAR < 4) {
         hg = *reinterpret_cast<const u32x4_16*>(wg + noff);
         hu = *reinterpret_cast<const u32x4_16*>(wu + noff);
@@ -220,8 +221,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode_loop(const uint8_t* __res
       auto decode = [&](int i, half8& ag, half8& au) {
         const uint32_t qg = (i < 4) ? qg0[i & 3] : qg1[i & 3];
         const uint32_t qu = (i < 4) ? qu0[i & 3] : qu1[i & 3];
-        ag = (i < 4) ? dequant_dword_sc(qg, sg.lo0, sg.hi0, nk) : dequant_dword_sc(qg, sg.lo1, sg.hi1, nk);
-        au = (i < 4) ? dequant_dword_sc(qu, su.lo0, su.hi0, nk) : dequant_dword_sc(qu, su.lo1, su.hi1, nk);
+        ag = dequant_dword_sc(qg, (i < 4) ? sg.r0 : sg.r1, nk);
+        au = dequant_dword_sc(qu, (i < 4) ? su.r0 : su.r1, nk);
       };
       half8 bc[NG], bn[NG], agc, auc, agn, aun;
       load_b(0, bc);
