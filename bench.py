@@ -191,6 +191,8 @@ def measure_issue_probes(torch):
     lib = ctypes.CDLL(PEAKS_LIB)
     lib.zinc_peak_mfma_valu.restype = ctypes.c_double
     lib.zinc_peak_mfma_valu.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.zinc_peak_mfma32_valu.restype = ctypes.c_double
+    lib.zinc_peak_mfma32_valu.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.zinc_peak_decode_loop.restype = ctypes.c_double
     lib.zinc_peak_decode_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
@@ -231,6 +233,13 @@ def measure_issue_probes(torch):
             base = ns if (same, kv) == (1, 0) else base
             res["mfma_with_valu"][f"{'same_wave' if same else 'second_wave'}_kv{kv}"] = {
                 "ns_per_mfma": round(ns, 3), "mfma_rate_frac": round(base / ns, 3)}
+    res["mfma32_with_valu"] = {}
+    base32 = None
+    for kv in (0, 1, 2, 3, 4, 6, 8, 12):
+        ns = per_mfma_ns(lambda kv=kv: lib.zinc_peak_mfma32_valu(kv, ncu, 4096, out.data_ptr(), sh))
+        base32 = ns if kv == 0 else base32
+        res["mfma32_with_valu"][f"same_wave_kv{kv}"] = {"ns_per_mfma": round(ns, 3),
+                                                        "time_vs_mfma_only": round(ns / base32, 3)}
     rng = np.random.default_rng(11)
     nblk = 16
     wg = torch.from_numpy(S.gen_q4k_blob(rng, 192, nblk * 256)).to(dev)
@@ -242,7 +251,8 @@ def measure_issue_probes(torch):
                 ng, var, wg.data_ptr(), wu.data_ptr(), nblk, 64, ncu, out.data_ptr(), sh))
             res["phase1_loop"][f"{16 * ng}_tokens_{names[var]}"] = {"ns_per_mfma": round(ns, 3),
                                                                    "mfma_rate_frac": round(base / ns, 3)}
-    res["method"] = ("one workgroup per CU (8 waves for probe 1; 12 waves for 64 tokens and 8 for 128 in probe 2); "
+    res["method"] = ("one workgroup per CU (8 waves for probe 1 and its 32x32x16 form; 12 waves for 64 tokens and 8 "
+                     "for 128 in probe 2); "
                      "best of 5 launches after 0.2 s of back-to-back launches; ns per MFMA issued on one SIMD; "
                      "mfma_rate_frac = the MFMA-only loop's ns per MFMA / this one's")
     del out, wg, wu

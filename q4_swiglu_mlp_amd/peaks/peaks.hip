@@ -13,6 +13,9 @@
 //                        MFMAs: every step is one MFMA and `kv` packed fp16
 //                        FMAs, issued by the same wave, or by a second wave on
 //                        the same SIMD
+//   zinc_peak_mfma32_valu  the same-wave form of zinc_peak_mfma_valu with
+//                        32x32x16 MFMAs (four accumulators of 16 registers),
+//                        kv up to 12
 //   zinc_peak_decode_loop  the fused prefill unit's phase-1 inner loop (Q4_K
 //                        decode in registers, B operands from LDS, 16x16x32
 //                        MFMAs for gate and up) on L2-resident weights, with
@@ -152,6 +155,42 @@ __global__ __launch_bounds__(512) void k_mfma_valu(int iters, float* __restrict_
   float r = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) r += acc[k][0] + (float)v[k][0] + (float)v[k][1];
+  out[(size_t)blockIdx.x * 512 + tid] = r;
+}
+
+// Every step one 32x32x16 MFMA and KV packed fp16 FMAs of the same wave;
+// registers only.
+template <int KV>
+__global__ __launch_bounds__(512) void k_mfma32_valu(int iters, float* __restrict__ out) {
+  const int tid = threadIdx.x;
+  half8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (_Float16)(0.001f * (float)((tid + e) & 7));
+    b[e] = (_Float16)(0.002f * (float)e);
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[k][e] = 0.f;
+  half2p v[8];
+  const half2p sc = {(_Float16)0.999f, (_Float16)1.001f}, cc = {(_Float16)0.001f, (_Float16)-0.001f};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = half2p{(_Float16)(0.1f * k), (_Float16)(tid & 3)};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[k], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < KV; ++j) v[(k + j) & 7] = __builtin_elementwise_fma(v[(k + j) & 7], sc, cc);
+    }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r += acc[k][0];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r += (float)v[k][0] + (float)v[k][1];
   out[(size_t)blockIdx.x * 512 + tid] = r;
 }
 
@@ -385,6 +424,28 @@ double zinc_peak_mfma_valu(int same_wave, int kv, int blocks, int iters, float* 
   // per SIMD (two waves of an 8-wave workgroup per SIMD, one workgroup per CU
   // and round): MFMAs issued by its MFMA-issuing waves
   return (double)iters * 8 * (same_wave ? 2 : 1);
+}
+
+// blocks x 512 threads; `out` holds blocks * 512 floats; kv in {0..4, 6, 8,
+// 12}.  Returns the 32x32x16 MFMAs issued per SIMD, 0 on an error.
+double zinc_peak_mfma32_valu(int kv, int blocks, int iters, float* out, void* stream) {
+  if (blocks < 1 || iters < 1 || !out) return 0.0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define ZP_M32(KV) hipLaunchKernelGGL((k_mfma32_valu<KV>), dim3(blocks), dim3(512), 0, s, iters, out)
+  switch (kv) {
+    case 0: ZP_M32(0); break;
+    case 1: ZP_M32(1); break;
+    case 2: ZP_M32(2); break;
+    case 3: ZP_M32(3); break;
+    case 4: ZP_M32(4); break;
+    case 6: ZP_M32(6); break;
+    case 8: ZP_M32(8); break;
+    case 12: ZP_M32(12); break;
+    default: return 0.0;
+  }
+#undef ZP_M32
+  if (hipGetLastError() != hipSuccess) return 0.0;
+  return (double)iters * 4 * 2;   // two waves per SIMD, four MFMAs per iteration each
 }
 
 // The phase-1 loop probe.  ng 4 (12 waves) or 8 (8 waves); var 0, 2, 4 or 5;
