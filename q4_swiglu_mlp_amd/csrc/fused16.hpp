@@ -106,80 +106,6 @@ struct Fused16Smem {
   int p2_next;                          // phase 2: next unclaimed output tile
 };
 
-// Scale registers of the decode below.  A sub-block's s = RNE16(d*sc) is
-// taken as (1024 + sc)*d - 1024*d, rounded once, and then scaled exactly by a
-// power of two: a register holds (1024*s_a, 64*s_b) for a low-nibble
-// sub-block a and the high-nibble sub-block b of the same 64-weight chunk.
-// The input is the fp16 pair (1024 + sc_a, 1024 + sc_b) as bits.
-__device__ __forceinline__ half2v scale_pair(uint32_t bits, half2v d2, half2v nd2) {
-  const half2v s = __builtin_elementwise_fma(bits_h2(bits), d2, nd2);
-  return s * half2v{(_Float16)1024.0f, (_Float16)64.0f};
-}
-
-// d of a block header (its low half) in both halves of a register.
-__device__ __forceinline__ half2v splat_d(uint32_t x) { return bits_h2(__builtin_amdgcn_perm(x, x, 0x01000100u)); }
-
-// Six-bit scales 0..3 (masked) and 4..7 (low four bits from word 3, top two
-// from bits 6..7 of word 1), one per byte.
-__device__ __forceinline__ uint32_t sc03_bytes(uint4 hdr) { return hdr.y & 0x3F3F3F3Fu; }
-__device__ __forceinline__ uint32_t sc47_bytes(uint4 hdr) {
-  return (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
-}
-
-// v_perm selector that turns bytes j and j + 1 of a word (src1) into the fp16
-// pair (1024 + byte_j, 1024 + byte_j+1): each half's high byte is 0x64, taken
-// from byte 0 of src0 = 0x64646464.
-__host__ __device__ constexpr uint32_t sc_pair_sel(int j) {
-  return 0x04000400u | ((uint32_t)(j + 1) << 16) | (uint32_t)j;
-}
-
-// The two chunks a lane decodes per block (chunk c0 = sel, c1 = 2 + sel):
-// r0 for sub-blocks (2 sel, 2 sel + 1), r1 for (4 + 2 sel, 5 + 2 sel);
-// psel = sc_pair_sel(2 sel).
-struct Lane16S {
-  half2v r0, r1;
-};
-
-__device__ __forceinline__ Lane16S lane16_scales(uint4 hdr, uint32_t psel) {
-  const half2v d2 = splat_d(hdr.x);
-  const half2v nd = d2 * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f};
-  Lane16S r;
-  r.r0 = scale_pair(__builtin_amdgcn_perm(0x64646464u, sc03_bytes(hdr), psel), d2, nd);
-  r.r1 = scale_pair(__builtin_amdgcn_perm(0x64646464u, sc47_bytes(hdr), psel), d2, nd);
-  return r;
-}
-
-// w' = q*s for the eight operand slots of one quant dword (the slot order of
-// dequant_dword_f16), from the register R = (1024*s_a, 64*s_b).  The nibble
-// becomes an fp16 in [1, 2) by OR-ing in the exponent of 1.0: a low nibble
-// reads 1 + q/1024, a high one (bits 4..7) 1 + q/64; fma(v, S, -S) is then
-// q*s exactly before its single rounding, with -S taken by a negation
-// modifier of the same register.
-__device__ __forceinline__ half8 dequant_dword_sc(uint32_t Q, half2v R, const NibbleK& k) {
-  const half2v S_lo = __builtin_shufflevector(R, R, 0, 0), S_hi = __builtin_shufflevector(R, R, 1, 1);
-  const uint32_t Q8 = Q >> 8;
-  const half2v p0 = __builtin_elementwise_fma(bits_h2((Q & k.lo_mask) | k.lo_magic), S_lo, -S_lo);
-  const half2v p1 = __builtin_elementwise_fma(bits_h2((Q8 & k.lo_mask) | k.lo_magic), S_lo, -S_lo);
-  const half2v p2 = __builtin_elementwise_fma(bits_h2((Q & k.hi_mask) | k.hi_magic), S_hi, -S_hi);
-  const half2v p3 = __builtin_elementwise_fma(bits_h2((Q8 & k.hi_mask) | k.hi_magic), S_hi, -S_hi);
-  half8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-// The nibble masks in SGPRs (a VALU operation may read one), the exponent
-// patterns in VGPRs: (q & mask) | magic stays one v_and_or_b32.
-// Both exponent patterns are 1.0 here (dequant_dword_sc).
-__device__ __forceinline__ NibbleK nibble_consts_s() {
-  NibbleK k;
-  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(k.lo_mask));
-  asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(k.hi_mask));
-  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(k.lo_magic));
-  k.hi_magic = k.lo_magic;
-  return k;
-}
-
 // Copy plan of one thread: NCOPY 16-byte pieces per column, piece p = the
 // thread's slot = (token row t = p / 34, piece j = p % 34).  src = byte offset
 // of the piece in column 0 of the staged activation, dst = its offset (halves)

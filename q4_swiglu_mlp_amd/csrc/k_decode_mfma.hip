@@ -73,38 +73,6 @@ struct DecShape {
   static constexpr int NBW = MM > 4 ? 2 : 4;
 };
 
-// Scales of the two chunks a lane decodes in every block: chunk c0 = sel and
-// c1 = 2 + sel (sel = (o >> 1) & 1).  s = RNE16(d*sc) exactly, as
-// (1024 + sc)*d - 1024*d before its single rounding.
-struct LaneChunkS {
-  half2v s_lo0, c_lo0, s_hi0, c_hi0;   // chunk c0: sub-blocks 2*c0 (low nibbles), 2*c0+1 (high)
-  half2v s_lo1, c_lo1, s_hi1, c_hi1;   // chunk c1
-};
-
-__device__ __forceinline__ LaneChunkS lane_chunk_scales(uint4 hdr, int sel) {
-  const SixBit sb = unpack_sixbit(hdr.y, hdr.z, hdr.w);
-  const uint32_t a = sb.sc03 >> (16 * sel);   // bytes: sc_{2c0}, sc_{2c0+1}
-  const uint32_t b = sb.sc47 >> (16 * sel);   // bytes: sc_{2c1}, sc_{2c1+1}
-  const uint32_t pl = (a & 0xFFu) | ((b & 0xFFu) << 16);
-  const uint32_t ph = ((a >> 8) & 0xFFu) | (((b >> 8) & 0xFFu) << 16);
-  const half2v d2 = splat_lo(hdr.x);
-  const half2v nd = d2 * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const half2v slo = __builtin_elementwise_fma(bits_h2(pl | 0x64006400u), d2, nd);   // (s_{2c0}, s_{2c1})
-  const half2v shi = __builtin_elementwise_fma(bits_h2(ph | 0x64006400u), d2, nd);   // (s_{2c0+1}, s_{2c1+1})
-  LaneChunkS r;
-  r.s_lo0 = half2v{slo[0], slo[0]};
-  r.s_lo1 = half2v{slo[1], slo[1]};
-  r.s_hi0 = half2v{shi[0], shi[0]};
-  r.s_hi1 = half2v{shi[1], shi[1]};
-  const half2v k1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const half2v k64 = {(_Float16)-64.0f, (_Float16)-64.0f};
-  r.c_lo0 = r.s_lo0 * k1024;
-  r.c_lo1 = r.s_lo1 * k1024;
-  r.c_hi0 = r.s_hi0 * k64;
-  r.c_hi1 = r.s_hi1 * k64;
-  return r;
-}
-
 // Orders one wave's LDS accesses for the compiler (the hardware already runs
 // them in program order); emits no instruction.
 __device__ __forceinline__ void wave_lds_order() {
@@ -152,6 +120,7 @@ __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches below
   const int r = lane & 15, o = lane >> 4, sel = (o >> 1) & 1;
+  const uint32_t psel = sc_pair_sel(2 * sel);   // lane16_scales: chunks sel and 2 + sel
   // B-operand column: token r.  Columns r >= M are computed and discarded, so
   // they may read any staged token's (finite) data.
   const int tb = r & (MM - 1);
@@ -167,7 +136,7 @@ __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict
   u32x4* wt1 = wt_all[wave][NMAT - 1];
   _Float16* xs = xs_all[wave];
   _Float16* xm = xm_all[wave];
-  const NibbleK nk = nibble_consts();
+  const NibbleK nk = nibble_consts_s();
 
   float4v_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 
@@ -276,20 +245,18 @@ __global__ __launch_bounds__(64 * KS, 3) void k_decode(const uint8_t* __restrict
         ch0[bl >> 2] = db0.hdr;
         if (GATEUP) ch1[bl >> 2] = db1.hdr;
       }
-      const LaneChunkS s0 = lane_chunk_scales(db0.hdr, sel);
-      LaneChunkS s1;
-      if (GATEUP) s1 = lane_chunk_scales(db1.hdr, sel);
+      const Lane16S s0 = lane16_scales(db0.hdr, psel);
+      Lane16S s1;
+      if (GATEUP) s1 = lane16_scales(db1.hdr, psel);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const half8 b = *reinterpret_cast<const half8*>(xb + (bl * 8 + i) * 32);
         const uint32_t q = (i < 4) ? dword_of(db0.q0, i & 3) : dword_of(db0.q1, i & 3);
-        const half8 a = (i < 4) ? dequant_dword_scaled(q, s0.s_lo0, s0.c_lo0, s0.s_hi0, s0.c_hi0, nk)
-                                : dequant_dword_scaled(q, s0.s_lo1, s0.c_lo1, s0.s_hi1, s0.c_hi1, nk);
+        const half8 a = dequant_dword_sc(q, (i < 4) ? s0.r0 : s0.r1, nk);
         acc0 = mfma16(a, b, acc0);
         if (GATEUP) {
           const uint32_t qu = (i < 4) ? dword_of(db1.q0, i & 3) : dword_of(db1.q1, i & 3);
-          const half8 au = (i < 4) ? dequant_dword_scaled(qu, s1.s_lo0, s1.c_lo0, s1.s_hi0, s1.c_hi0, nk)
-                                   : dequant_dword_scaled(qu, s1.s_lo1, s1.c_lo1, s1.s_hi1, s1.c_hi1, nk);
+          const half8 au = dequant_dword_sc(qu, (i < 4) ? s1.r0 : s1.r1, nk);
           acc1 = mfma16(au, b, acc1);
         }
       }
