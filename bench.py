@@ -616,6 +616,39 @@ def secondary(args, torch):
         out += m2048_lines(args, torch, np, Z, S, dev, t)
     if args.only == "staged":   # its own run: its fused calls at M=2048 would mix into the headline kernel's trace
         out += staged_lines(args, torch, np, Z, S, dev, t)
+    if args.only == "m384":     # its own run, for the counters of the 257-511-token unit
+        out += m384_lines(args, torch, np, Z, S, dev, t)
+    return out
+
+
+def m384_lines(args, torch, np, Z, S, dev, t):
+    """A mid-size prefill that the plan gives to the 64-token unit with
+    384-row chunks (257-511 tokens): 384 tokens through layer 0 of the M=256
+    workload's weights (seed 1, its shifts), x ~ N(0, 1) of its own seed;
+    whole-call time and the fused kernel by HIP events."""
+    w = S.WORKLOADS["prefill_m256"]
+    M = 384
+    wg, wu, wd = (t(a) for a in S.layer_weights(w.seed, 0, w.hidden, w.inter))
+    gx = t(S.gen_x(np.random.default_rng([w.seed, 384]), M, w.hidden))
+    y = torch.empty((M, w.hidden), dtype=torch.float16, device=dev)
+    ws = torch.empty(Z.prefill_workspace_size(M, w.hidden, w.inter), dtype=torch.uint8, device=dev)
+
+    def call(_i):
+        Z.zinc_mlp_q4k_prefill(wg, wu, wd, w.hidden, w.inter, gx, w.inter_shift, w.out_shift, y=y, workspace=ws)
+
+    steps = 50
+    wall, ms = time_calls(call, steps, 10, torch, warm_s=0.1)
+    per = wall / steps
+    kern = sum(ms) / len(ms)
+    flops = 6.0 * M * w.hidden * w.inter
+    out = [{
+        "workload": "prefill 4096/11008 M=384 (layer 0 of seed 1), the 257-511-token unit",
+        "tokens_per_s": round(M / per, 1),
+        "us_per_call": round(per * 1e6, 2),
+        "fused_kernel_us": round(kern * 1e3, 2),
+        "fused_kernel_mfma_frac": round(flops / (kern * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+    }]
+    log(f"[bench] {out[-1]}")
     return out
 
 
@@ -902,7 +935,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "moe", "block", "m2048", "staged", "peaks", "cpu"], default=None,
+    ap.add_argument("--only", choices=["decode", "moe", "block", "m2048", "staged", "m384", "peaks", "cpu"],
+                    default=None,
                     help="development and profiling runs: skip the headline and run one part (a secondary line, "
                          "the measured peaks, or the full CPU oracle table including one-thread figures)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
