@@ -200,6 +200,22 @@ def test_prefill_m2048_workload_sampled_tokens(layer):
     assert_parity(y[rows], y_ref, f"prefill M=2048 layer {layer}, {len(rows)} sampled tokens")
 
 
+def test_prefill_large_m_sampled_tokens():
+    # 8200 tokens (a ragged last 128-token tile) put the split-K partials at
+    # 43 x 8200 x 4096 x 2 B = 2.9 GB, past 2^31 bytes: every partial and
+    # workspace offset must be 64-bit
+    w = S.WORKLOADS["prefill_m2048"]
+    M = 8200
+    wg, wu, wd = S.layer_weights(w.seed, 0, w.hidden, w.inter)
+    x = S.gen_x(np.random.default_rng([w.seed, M]), M, w.hidden, w.x_sd)
+    assert Z.prefill_workspace_size(M, w.hidden, w.inter) > 2**31
+    y = prefill(wg, wu, wd, w.hidden, w.inter, x, w.inter_shift, w.out_shift)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 4096, 8191, 8192, M - 1], rng.choice(M, 23, replace=False)]))
+    y_ref, _ = O.mlp(x[rows], wg, wu, wd, w.hidden, w.inter)   # tokens are independent rows
+    assert_parity(y[rows], y_ref, f"prefill M={M}, {len(rows)} sampled tokens")
+
+
 def test_prefill_intermediate_near_fp16_limit():
     # the shift is one less than the 4x-headroom choice, so the fp16 strip holds
     # values up to 2^14: sums of 32 such values would overflow fp16, the kernel's
