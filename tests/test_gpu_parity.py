@@ -397,6 +397,19 @@ def test_moe_tiny():
     assert_parity(_moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, 8), y_ref, "moe E=4 top-2")
 
 
+@pytest.mark.parametrize("E,k,M", [(1024, 16, 40), (3, 3, 50)])
+def test_moe_expert_count_limits(E, k, M):
+    # the most experts the boundary takes (1024: most of them get no slot and
+    # the rest one or two, so nearly every tile holds a row or two), and every
+    # token routed to all of its experts (top_k == E)
+    H, I = 256, 256
+    wg, wu, wd, x, ids, p = _moe_inputs(E, H, I, M, k, 23)
+    y_ref, bad = O.moe(x, wg, wu, wd, ids, p, H, I)
+    assert bad == 0
+    print(f"[moe limits] E={E} k={k} M={M}: {len(np.unique(ids))} experts used", flush=True)
+    assert_parity(_moe_gpu(wg, wu, wd, E, H, I, x, ids, p, 0, 8), y_ref, f"moe E={E} top-{k} M={M}")
+
+
 @pytest.mark.parametrize("M", [32768, 32769])
 def test_moe_routing_paths_around_the_switch(M):
     # up to 65536 slots the routing runs in one workgroup, past it as three
