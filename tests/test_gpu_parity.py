@@ -482,6 +482,20 @@ def test_moe_invalid_ids_flag_and_contribute_nothing():
     assert_parity(y, y_ref, "moe with invalid ids")
 
 
+@pytest.mark.parametrize("M", [1, 3])
+def test_moe_decode_sized_batches(M):
+    # the E=64 top-8 2048 -> 768 experts with one or three tokens (MoE decode):
+    # every tile then holds one to three rows
+    w = S.WORKLOADS["moe_e64"]
+    wg, wu, wd = S.expert_weights(w.seed, w.n_experts, w.hidden, w.inter)
+    x = S.workload_x(w, M)
+    ids, p = S.workload_routing(w, M)
+    y = _moe_gpu(wg, wu, wd, w.n_experts, w.hidden, w.inter, x, ids, p, w.inter_shift, w.out_shift)
+    y_ref, bad = O.moe(x, wg, wu, wd, ids, p, w.hidden, w.inter)
+    assert bad == 0
+    assert_parity(y, y_ref, f"moe E=64 top-8 M={M}")
+
+
 def test_moe_workload_full():
     w = S.WORKLOADS["moe_e64"]
     wg, wu, wd = S.expert_weights(w.seed, w.n_experts, w.hidden, w.inter)
