@@ -233,6 +233,13 @@ def measure_issue_probes(torch):
             base = ns if (same, kv) == (1, 0) else base
             res["mfma_with_valu"][f"{'same_wave' if same else 'second_wave'}_kv{kv}"] = {
                 "ns_per_mfma": round(ns, 3), "mfma_rate_frac": round(base / ns, 3)}
+    lib.zinc_peak_mfma_valu_agpr.restype = ctypes.c_double
+    lib.zinc_peak_mfma_valu_agpr.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
+    res["mfma_with_valu_agpr_acc"] = {}
+    for kv in range(5):
+        ns = per_mfma_ns(lambda kv=kv: lib.zinc_peak_mfma_valu_agpr(kv, ncu, 4096, out.data_ptr(), sh))
+        res["mfma_with_valu_agpr_acc"][f"same_wave_kv{kv}"] = {"ns_per_mfma": round(ns, 3),
+                                                             "mfma_rate_frac": round(base / ns, 3)}
     res["mfma32_with_valu"] = {}
     base32 = None
     for kv in (0, 1, 2, 3, 4, 6, 8, 12):
@@ -256,6 +263,55 @@ def measure_issue_probes(torch):
                      "best of 5 launches after 0.2 s of back-to-back launches; ns per MFMA issued on one SIMD; "
                      "mfma_rate_frac = the MFMA-only loop's ns per MFMA / this one's")
     del out, wg, wu
+    return res
+
+
+def measure_partial_sinks(torch):
+    """Where the fused prefill unit's split-K partials could go, at the M = 256
+    unit's shape (232 workgroups of 12 waves, each a 64-token x 4096-row partial
+    written in 32-row tiles, libzinc_peaks.so): fp16 stores to a region per
+    workgroup (what the unit does, 121.6 MB), fp32 stores (243 MB), or fp32
+    atomic adds into one accumulator per (XCD, token tile), chosen by the
+    hardware XCC id so that each accumulator is updated from one XCD (32 MB).
+    Best of five launches; the atomic form is checked element by element."""
+    import ctypes
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.zinc_peak_partial_sink.restype = ctypes.c_int
+    lib.zinc_peak_partial_sink.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    cur = torch.cuda.current_stream()
+    n_wg, tok, H = 232, 64, 4096
+    acc = torch.zeros(8 * 4 * tok * H, dtype=torch.float32, device=dev)
+    part = torch.empty(n_wg * tok * H, dtype=torch.float32, device=dev)
+    xcc = torch.zeros(n_wg, dtype=torch.int32, device=dev)
+    res = {}
+    for mode, name, mb in ((0, "fp16_stores_per_unit", n_wg * tok * H * 2 / 1e6),
+                           (1, "fp32_stores_per_unit", n_wg * tok * H * 4 / 1e6),
+                           (2, "fp32_atomics_per_xcd_accumulator", 8 * 4 * tok * H * 4 / 1e6)):
+        best = float("inf")
+        for r in range(6):
+            acc.zero_()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            if lib.zinc_peak_partial_sink(mode, n_wg, acc.data_ptr(), part.data_ptr(), xcc.data_ptr(),
+                                          cur.cuda_stream) != 0:
+                raise RuntimeError("partial-sink probe launch failed")
+            e1.record(cur)
+            e1.synchronize()
+            if r:
+                best = min(best, e0.elapsed_time(e1) * 1e3)
+        res[name] = {"us": round(best, 2), "MB_written": round(mb, 1)}
+        if mode == 2:
+            x = xcc.cpu().numpy() & 7
+            counts = torch.zeros(8, 4, dtype=torch.float32)
+            for b in range(n_wg):
+                counts[x[b], b % 4] += 1
+            want = counts.to(dev).reshape(8, 4, 1).expand(8, 4, tok * H).reshape(-1)
+            res[name]["wrong_elements"] = int((acc != want).sum().item())
+            res[name]["workgroups_off_block_id_mod_8"] = int(sum(int(x[b]) != b % 8 for b in range(n_wg)))
+    del acc, part, xcc
     return res
 
 
@@ -968,7 +1024,8 @@ def main():
 
     if args.only == "peaks":
         print(json.dumps({"measured_peaks": measure_peaks(torch), "issue_probes": measure_issue_probes(torch),
-                          "q4k_stream_layouts": measure_stream_layouts(torch)}), flush=True)
+                          "q4k_stream_layouts": measure_stream_layouts(torch),
+                          "partial_sinks": measure_partial_sinks(torch)}), flush=True)
         return
     if args.only == "cpu":
         import q4k_synth as S

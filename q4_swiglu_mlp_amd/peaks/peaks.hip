@@ -111,9 +111,12 @@ __global__ __launch_bounds__(256) void k_hbm_copy(const uint4* __restrict__ src,
 
 // MODE 0: every step one MFMA and KV VALU in the same wave; MODE 1: waves
 // 0-3 of each 8-wave workgroup issue the MFMAs and waves 4-7 the VALU work
-// (one of each per SIMD).  Operands are registers only.
-template <int MODE, int KV>
+// (one of each per SIMD).  Operands are registers only.  AG: the accumulators
+// live in AGPRs (an AGPR clobber makes the compiler select the MFMAs' AGPR
+// form) instead of VGPRs.
+template <int MODE, int KV, bool AG = false>
 __global__ __launch_bounds__(512) void k_mfma_valu(int iters, float* __restrict__ out) {
+  if constexpr (AG) asm volatile("" ::: "a0");
   const int tid = threadIdx.x, wave = tid >> 6;
   half8 a, b;
 #pragma unroll
@@ -192,6 +195,48 @@ __global__ __launch_bounds__(512) void k_mfma32_valu(int iters, float* __restric
 #pragma unroll
   for (int k = 0; k < 8; ++k) r += (float)v[k][0] + (float)v[k][1];
   out[(size_t)blockIdx.x * 512 + tid] = r;
+}
+
+// Split-K partial sinks of the fused prefill unit's phase 2, at its shape (n_wg
+// workgroups of 12 waves, each writing a 64-token x 4096-row partial in 32-row
+// tiles, lanes along the rows):
+//   MODE 0: fp16 stores, each workgroup to its own region (the unit's partials)
+//   MODE 1: fp32 stores, each workgroup to its own region
+//   MODE 2: fp32 atomic adds into one accumulator per (XCD, token tile of
+//           blockIdx % 4), the XCD taken from the hardware XCC id, so every
+//           accumulator is updated from one XCD only
+// acc: 8 * 4 * 64 * 4096 floats (zeroed by the caller for MODE 2); part:
+// n_wg * 64 * 4096 floats; wg_xcc: n_wg ints (the XCC id each workgroup ran on).
+constexpr int PS_TOK = 64, PS_H = 4096;
+__device__ __forceinline__ int hw_xcc_id() {
+  int v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 15;
+}
+template <int MODE>
+__global__ __launch_bounds__(768) void k_partial_sink(float* __restrict__ acc, void* __restrict__ part,
+                                                      int* __restrict__ wg_xcc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int xcc = hw_xcc_id();
+  if (threadIdx.x == 0) wg_xcc[blockIdx.x] = xcc;
+  const int l32 = lane & 31, h = lane >> 5;
+  float* const abase = acc + ((size_t)(xcc & 7) * 4 + blockIdx.x % 4) * PS_TOK * PS_H;
+  _Float16* const pb = static_cast<_Float16*>(part) + (size_t)blockIdx.x * PS_TOK * PS_H;
+  float* const fb = static_cast<float*>(part) + (size_t)blockIdx.x * PS_TOK * PS_H;
+  for (int nt = wave; nt < PS_H / 32; nt += 12) {
+    const int n = nt * 32 + l32;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const size_t off = (size_t)(32 * t2 + 8 * q + 4 * h + e) * PS_H + n;
+          if constexpr (MODE == 0) pb[off] = (_Float16)1.0f;
+          else if constexpr (MODE == 1) fb[off] = 1.0f;
+          else __hip_atomic_fetch_add(abase + off, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+  }
 }
 
 // The phase-1 loop of the fused unit (the lane layout, decode, scales and
@@ -424,6 +469,32 @@ double zinc_peak_mfma_valu(int same_wave, int kv, int blocks, int iters, float* 
   // per SIMD (two waves of an 8-wave workgroup per SIMD, one workgroup per CU
   // and round): MFMAs issued by its MFMA-issuing waves
   return (double)iters * 8 * (same_wave ? 2 : 1);
+}
+
+// Probe 1's same-wave form with the accumulators in AGPRs; kv 0..4.
+double zinc_peak_mfma_valu_agpr(int kv, int blocks, int iters, float* out, void* stream) {
+  if (blocks < 1 || iters < 1 || !out || kv < 0 || kv > 4) return 0.0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define ZP_MA(KV) hipLaunchKernelGGL((k_mfma_valu<0, KV, true>), dim3(blocks), dim3(512), 0, s, iters, out)
+  switch (kv) { case 0: ZP_MA(0); break; case 1: ZP_MA(1); break; case 2: ZP_MA(2); break;
+                case 3: ZP_MA(3); break; default: ZP_MA(4); break; }
+#undef ZP_MA
+  if (hipGetLastError() != hipSuccess) return 0.0;
+  return (double)iters * 8 * 2;
+}
+
+// One launch of the partial-sink probe (k_partial_sink) over n_wg workgroups;
+// mode 0..2.  Returns 0, or -1 on an invalid argument or a launch error.
+int zinc_peak_partial_sink(int mode, int n_wg, float* acc, void* part, int* wg_xcc, void* stream) {
+  if (!acc || !part || !wg_xcc || n_wg < 1 || mode < 0 || mode > 2) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == 0)
+    hipLaunchKernelGGL(k_partial_sink<0>, dim3(n_wg), dim3(768), 0, s, acc, part, wg_xcc);
+  else if (mode == 1)
+    hipLaunchKernelGGL(k_partial_sink<1>, dim3(n_wg), dim3(768), 0, s, acc, part, wg_xcc);
+  else
+    hipLaunchKernelGGL(k_partial_sink<2>, dim3(n_wg), dim3(768), 0, s, acc, part, wg_xcc);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 // blocks x 512 threads; `out` holds blocks * 512 floats; kv in {0..4, 6, 8,
