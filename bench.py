@@ -258,6 +258,15 @@ def measure_issue_probes(torch):
                 ng, var, wg.data_ptr(), wu.data_ptr(), nblk, 64, ncu, out.data_ptr(), sh))
             res["phase1_loop"][f"{16 * ng}_tokens_{names[var]}"] = {"ns_per_mfma": round(ns, 3),
                                                                    "mfma_rate_frac": round(base / ns, 3)}
+    lib.zinc_peak_decode_loop32.restype = ctypes.c_double
+    lib.zinc_peak_decode_loop32.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    res["phase1_loop_32x32x16"] = {}
+    for var in (0, 2, 4, 5):
+        ns = per_mfma_ns(lambda var=var: lib.zinc_peak_decode_loop32(
+            var, wg.data_ptr(), wu.data_ptr(), nblk, 64, ncu, out.data_ptr(), sh))
+        res["phase1_loop_32x32x16"][f"64_tokens_{names[var]}"] = {"ns_per_16x16x32_equivalent": round(ns, 3),
+                                                                  "mfma_rate_frac": round(base / ns, 3)}
     res["method"] = ("one workgroup per CU (8 waves for probe 1 and its 32x32x16 form; 12 waves for 64 tokens and 8 "
                      "for 128 in probe 2); "
                      "best of 5 launches after 0.2 s of back-to-back launches; ns per MFMA issued on one SIMD; "

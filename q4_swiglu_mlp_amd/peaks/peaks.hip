@@ -354,6 +354,94 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode_loop(const uint8_t* __res
 }
 
 
+// The same phase-1 work as k_decode_loop<4, 12, VAR> (64 tokens, gate and up
+// of 192 rows) on 32x32x16 MFMAs: wave w owns one matrix (gate for even w, up
+// for odd) of the 32-row tile w / 2, for both 32-token halves.  Lane (r, h) =
+// (lane % 32, lane / 32) decodes row r's quant bytes [64h, 64h + 64) of each
+// block, one dword per MFMA step (sixteen steps per block; chunk 2h for steps
+// 0-7, 2h + 1 for 8-15), and the B operand of step s is token lane % 32's
+// activation piece of that dword.  Same VAR meanings as k_decode_loop.
+template <int VAR>
+__global__ __launch_bounds__(768) void k_decode_loop32(const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+                                                       int nblk, int reps, float* __restrict__ out) {
+  using namespace zinc;
+  constexpr int XS = 264;
+  __shared__ __attribute__((aligned(16))) _Float16 xs[64 * XS];
+  for (int i = threadIdx.x; i < 64 * XS; i += 768) xs[i] = (_Float16)(0.001f * (float)(i & 15));
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  const NibbleK nk = nibble_consts_s();
+  const uint8_t* const w = (wave & 1) ? wu : wg;
+  const uint32_t rowb = (uint32_t)nblk * BLOCK_BYTES;
+  const uint32_t wrow_off = (uint32_t)((wave >> 1) * 32 + r) * rowb;
+  float16v acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+  u32x4_16 hd = *reinterpret_cast<const u32x4_16*>(w + wrow_off);
+  u32x4_16 q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = *reinterpret_cast<const u32x4_16*>(w + (wrow_off + 16 + 64 * h + 16 * i));
+  const _Float16* const xl = xs + r * XS + 64 * h;   // token r of half 0; chunk 2h's first piece
+  const half8 afix = *reinterpret_cast<const half8*>(xl);
+  const uint32_t psel0 = sc_pair_sel(0), psel1 = sc_pair_sel(2);
+  for (int rep = 0; rep < reps; ++rep) {
+    for (int kb = 0; kb < nblk; ++kb) {
+      const int kn = (kb + 1 < nblk) ? kb + 1 : 0;
+      const uint32_t noff = wrow_off + (uint32_t)kn * BLOCK_BYTES;
+      const uint4 hh = as_u4(hd);
+      const half2v d2 = splat_d(hh.x);
+      const half2v nd = d2 * half2v{(_Float16)-1024.0f, (_Float16)-1024.0f};
+      const uint32_t scw = h ? sc47_bytes(hh) : sc03_bytes(hh);
+      const half2v s0 = scale_pair(__builtin_amdgcn_perm(0x64646464u, scw, psel0), d2, nd);
+      const half2v s1 = scale_pair(__builtin_amdgcn_perm(0x64646464u, scw, psel1), d2, nd);
+      u32x4_16 qn[4];
+      if constexpr (VAR < 4) {
+        hd = *reinterpret_cast<const u32x4_16*>(w + noff);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qn[i] = *reinterpret_cast<const u32x4_16*>(w + (noff + 16 + 64 * h + 16 * i));
+      } else {
+        const uint32_t d = (uint32_t)kb * 0x01010101u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qn[i] = q[i] + d;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      auto load_b = [&](int st, half8 (&b)[2]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) b[t] = (VAR == 5) ? afix : *reinterpret_cast<const half8*>(xl + t * 32 * XS + st * 8);
+      };
+      auto decode = [&](int st) -> half8 { return dequant_dword_sc(q[st >> 2][st & 3], (st < 8) ? s0 : s1, nk); };
+      half8 bc[2], bn[2], ac, an;
+      load_b(0, bc);
+      ac = decode(0);
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        if (st < 15) {
+          load_b(st + 1, bn);
+          an = decode(st + 1);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma32(VAR == 2 ? afix : ac, bc[t], acc[t]);
+        if (st < 15) {
+          bc[0] = bn[0];
+          bc[1] = bn[1];
+          ac = an;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = qn[i];
+    }
+  }
+  out[(size_t)blockIdx.x * 768 + threadIdx.x] = acc[0][0] + acc[1][1];
+}
+
 // Q4_K stream layouts (loads only, folded into a sink).  LAYOUT 0: wave per
 // row, lane l = 64-weight chunk l of the row (block header + its 32 quant
 // bytes); LAYOUT 1: wave per 16-row tile, lane (r, o) = row r, quant pieces
@@ -542,6 +630,26 @@ double zinc_peak_decode_loop(int ng, int var, const void* wg, const void* wu, in
   if (hipGetLastError() != hipSuccess) return 0.0;
   const int waves = (ng == 4) ? 12 : 8;
   return (double)waves / 4 * reps * nblk * 8 * ng * 2;
+}
+
+// The phase-1 loop probe on 32x32x16 MFMAs (k_decode_loop32); var 0, 2, 4 or
+// 5; weights as zinc_peak_decode_loop.  Returns the MFMAs per SIMD counted as
+// 16x16x32 equivalents (two per 32x32x16), so rates compare with that probe.
+double zinc_peak_decode_loop32(int var, const void* wg, const void* wu, int nblk, int reps, int blocks, float* out,
+                               void* stream) {
+  if (!wg || !wu || !out || nblk < 1 || reps < 1 || blocks < 1) return 0.0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* g = static_cast<const uint8_t*>(wg);
+  const uint8_t* u = static_cast<const uint8_t*>(wu);
+  switch (var) {
+    case 0: hipLaunchKernelGGL(k_decode_loop32<0>, dim3(blocks), dim3(768), 0, s, g, u, nblk, reps, out); break;
+    case 2: hipLaunchKernelGGL(k_decode_loop32<2>, dim3(blocks), dim3(768), 0, s, g, u, nblk, reps, out); break;
+    case 4: hipLaunchKernelGGL(k_decode_loop32<4>, dim3(blocks), dim3(768), 0, s, g, u, nblk, reps, out); break;
+    case 5: hipLaunchKernelGGL(k_decode_loop32<5>, dim3(blocks), dim3(768), 0, s, g, u, nblk, reps, out); break;
+    default: return 0.0;
+  }
+  if (hipGetLastError() != hipSuccess) return 0.0;
+  return 3.0 * reps * nblk * 16 * 2 * 2;
 }
 
 // One launch of a Q4_K stream layout over a gate/up pair of nrows x (256 nb)
