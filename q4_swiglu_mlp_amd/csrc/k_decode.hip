@@ -39,6 +39,7 @@
 #include "util_kernels.hpp"
 
 #include <algorithm>
+#include <atomic>
 
 namespace zinc {
 
@@ -344,16 +345,31 @@ __global__ __launch_bounds__(DrShape<NW>::THREADS) void k_decode_rows(const uint
   }
 }
 
+// Per-device CU count, looked up once per device (atomics: calls may come from
+// several host threads).
 int cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  int& c = cache[dev & 63];
-  if (c == 0) {
-    int n = 0;
-    c = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  std::atomic<int>& c = cache[dev & 63];
+  int n = c.load(std::memory_order_relaxed);
+  if (n == 0) {
+    n = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    c.store(n, std::memory_order_relaxed);
   }
-  return c;
+  return n;
+}
+
+// Raises a kernel's dynamic-LDS limit to at least `smem` bytes; `set` holds the
+// largest limit set so far for that kernel (shared by host threads).
+hipError_t raise_lds_limit(const void* kernel, size_t smem, std::atomic<size_t>& set) {
+  if (smem <= set.load(std::memory_order_relaxed)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  size_t cur = set.load(std::memory_order_relaxed);
+  while (cur < smem && !set.compare_exchange_weak(cur, smem, std::memory_order_relaxed)) {
+  }
+  return hipSuccess;
 }
 
 // Persistent grid: as many workgroups as are resident at once (occupancy of
@@ -371,22 +387,21 @@ hipError_t launch_rows_cfg(const void* W0, const void* W1, int K, int N, const _
                            float scale, const _Float16* res, float res_scale, const _Float16* gamma, float eps,
                            int wg_per_cu, hipStream_t stream) {
   const size_t smem = (size_t)MM * (K + 8) * 2 + (size_t)MM * 2 * (4 * (K / QK)) * 4;
-  static size_t attr_set = 0;   // largest dynamic LDS size allowed so far
-  if (smem > attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_rows<MM, GATEUP, KQ, DEPTH, NW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = smem;
-  }
-  static size_t occ_smem = 0;
-  static int occ = 0;
-  if (occ == 0 || occ_smem != smem) {
+  static std::atomic<size_t> attr_set{0};   // largest dynamic LDS size allowed so far
+  hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&k_decode_rows<MM, GATEUP, KQ, DEPTH, NW>), smem,
+                                 attr_set);
+  if (e != hipSuccess) return e;
+  // occupancy at the last LDS size asked for, cached as (smem << 8) | occupancy
+  static std::atomic<uint64_t> occ_key{0};
+  uint64_t key = occ_key.load(std::memory_order_relaxed);
+  int occ = (int)(key & 0xFFu);
+  if (occ == 0 || (key >> 8) != (uint64_t)smem) {
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_rows<MM, GATEUP, KQ, DEPTH, NW>,
-                                                                DrShape<NW>::THREADS, smem);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_rows<MM, GATEUP, KQ, DEPTH, NW>,
+                                                     DrShape<NW>::THREADS, smem);
     if (e != hipSuccess) return e;
-    occ = per_cu < 1 ? 1 : per_cu;
-    occ_smem = smem;
+    occ = per_cu < 1 ? 1 : (per_cu > 255 ? 255 : per_cu);
+    occ_key.store(((uint64_t)smem << 8) | (uint64_t)occ, std::memory_order_relaxed);
   }
   const int per_cu = (wg_per_cu > 0 && wg_per_cu < occ) ? wg_per_cu : occ;
   const int grid = std::max(1, std::min(cu_count() * per_cu, (N + NW - 1) / NW));
@@ -529,15 +544,11 @@ hipError_t launch_down_split(const void* W, int K, int N, const _Float16* h, _Fl
                              const _Float16* res, float res_scale, hipStream_t stream) {
   using SH = SplitShape<S>;
   const size_t smem = (size_t)K * 2 + (size_t)2 * (4 * (K / QK)) * 4 + (size_t)2 * SH::R * S * 4;
-  static size_t attr_set = 0;
-  if (smem > attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_down_split<S>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = smem;
-  }
+  static std::atomic<size_t> attr_set{0};
+  hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&k_decode_down_split<S>), smem, attr_set);
+  if (e != hipSuccess) return e;
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_down_split<S>, SH::THREADS, smem);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_down_split<S>, SH::THREADS, smem);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   const int ngroups = (N + SH::R - 1) / SH::R;
