@@ -131,17 +131,41 @@ __device__ int build_tile_table(int e, int E, int c, int MT, int* s0, int* s1, i
   const bool sm = small_expert(c, MT);
   const int fa = sm ? 0 : nf, ra = (!sm && rem > 0) ? 1 : 0;   // 192-row-chunk expert
   const int fb = sm ? nf : 0, rb = sm ? 1 : 0;                 // 128-row-chunk expert
+  // inclusive scans over the first P entries, P the power of two at or above
+  // E (the entries from E on are zero, so entry P - 1 holds the totals and
+  // later entries are never read)
+  int P = 1;
+  while (P < E) P <<= 1;
+  if (P <= 64) {
+    // one wave holds every entry: scan in registers, then publish
+    if (e < 64) {
+      int v0 = c, v1 = fa, v2 = ra, v3 = fb, v4 = rb;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int a0 = __shfl_up(v0, d, 64), a1 = __shfl_up(v1, d, 64), a2 = __shfl_up(v2, d, 64);
+        const int a3 = __shfl_up(v3, d, 64), a4 = __shfl_up(v4, d, 64);
+        if (e >= d) {
+          v0 += a0;
+          v1 += a1;
+          v2 += a2;
+          v3 += a3;
+          v4 += a4;
+        }
+      }
+      s0[e] = v0;
+      s1[e] = v1;
+      s2[e] = v2;
+      s3[e] = v3;
+      s4[e] = v4;
+    }
+    lds_barrier();
+  } else {
   s0[e] = c;
   s1[e] = fa;
   s2[e] = ra;
   s3[e] = fb;
   s4[e] = rb;
   lds_barrier();
-  // inclusive Hillis-Steele scans over the first P entries, P the power of
-  // two at or above E (the entries from E on are zero, so entry P - 1 holds
-  // the totals and later entries are never read)
-  int P = 1;
-  while (P < E) P <<= 1;
   for (int d = 1; d < P; d <<= 1) {
     const int a0 = (e >= d) ? s0[e - d] : 0;
     const int a1 = (e >= d) ? s1[e - d] : 0;
@@ -155,6 +179,7 @@ __device__ int build_tile_table(int e, int E, int c, int MT, int* s0, int* s1, i
     s3[e] += a3;
     s4[e] += a4;
     lds_barrier();
+  }
   }
   const int off = s0[e] - c;   // exclusive
   const int tfa = s1[P - 1], tra = s2[P - 1], tfb = s3[P - 1], trb = s4[P - 1];
@@ -244,7 +269,25 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
   cnt[e] = 0;
   lds_barrier();
   bool bad = false;
-  for (int i = threadIdx.x; i < n_slots; i += 1024) {
+  // the first four ids of this thread stay in registers for the scatter pass
+  constexpr int KEEP = 4;
+  int idk[KEEP];
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k) {
+    const int i = (int)threadIdx.x + 1024 * k;
+    idk[k] = (i < n_slots) ? ids[i] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k) {
+    if ((int)threadIdx.x + 1024 * k < n_slots) {
+      const int x = idk[k];
+      if (x >= 0 && x < E)
+        atomicAdd(&cnt[x], 1);
+      else
+        bad = true;
+    }
+  }
+  for (int i = threadIdx.x + 1024 * KEEP; i < n_slots; i += 1024) {
     const int x = ids[i];
     if (x >= 0 && x < E)
       atomicAdd(&cnt[x], 1);
@@ -261,8 +304,7 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
   lds_barrier();
   cnt[e] = off;   // the expert's cursor
   lds_barrier();
-  for (int i = threadIdx.x; i < n_slots; i += 1024) {
-    const int x = ids[i];
+  auto scatter = [&](int i, int x) {
     if (x >= 0 && x < E) {
       const int q = atomicAdd(&cnt[x], 1);
       slots[q] = i;
@@ -270,7 +312,13 @@ __global__ __launch_bounds__(1024) void k_moe_route(const int32_t* __restrict__ 
     } else {
       pos[i] = -1;
     }
+  };
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k) {
+    const int i = (int)threadIdx.x + 1024 * k;
+    if (i < n_slots) scatter(i, idk[k]);
   }
+  for (int i = threadIdx.x + 1024 * KEEP; i < n_slots; i += 1024) scatter(i, ids[i]);
 }
 
 // MoE output of the 80-token unit: unit row r belongs to slot slot_of_row[r];
